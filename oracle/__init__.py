@@ -1,0 +1,109 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package.  It shares no code with the GPU library and never
+calls it.  The arithmetic lives in ``oracle.c`` (plain C, fp64); this module
+only marshals arrays across ctypes.
+
+What is computed, per row (b, h, i):  the three-pass safe softmax of the scaled
+scores ("The Details of Flash Attention", section "Safe Softmax and the Three
+Passes") applied to softmax(Q K^T * scale) V ("FlashAttention Engine", the
+attention equation), with causal masking keeping key j iff j <= i, and the
+per-row log-sum-exp lse = m + ln(l) in natural-log, scaled-score units (the
+m and l statistics of "FlashAttention" (ai360xpert), section "Recomputation in
+the backward pass").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import time
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# element-type codes of oracle.h
+_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3}
+
+
+def lib():
+    """Load liboracle.so (built by oracle/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: run `python oracle/build.py` "
+                "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_attn_rows.restype = ctypes.c_int
+        L.oracle_attn_rows.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+            ctypes.c_double, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_thread_count.restype = ctypes.c_int
+        L.oracle_thread_count.argtypes = [ctypes.c_int]
+        L.oracle_load.restype = ctypes.c_double
+        L.oracle_load.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong]
+        _lib = L
+    return _lib
+
+
+def thread_count(threads: int = 0) -> int:
+    return lib().oracle_thread_count(int(threads))
+
+
+def _as_cpu(t):
+    if isinstance(t, np.ndarray):
+        t = torch.from_numpy(t)
+    if t.device.type != "cpu":
+        raise ValueError("the oracle takes host tensors")
+    return t.contiguous()
+
+
+def attn_rows(q, k, v, scale: float, causal: bool, rows=None, threads: int = 0):
+    """Oracle attention for selected rows.
+
+    q, k, v: host tensors [B, H, N, d] (float32 / float16 / bfloat16 / float64),
+    all of one dtype.  rows: flat row ids (b*H + h)*N + i; None means all rows.
+    Returns (o [n_rows, d] float64, lse [n_rows] float64) as numpy arrays.
+    """
+    q, k, v = _as_cpu(q), _as_cpu(k), _as_cpu(v)
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _CODES:
+        raise ValueError(f"unsupported dtype combination {q.dtype}/{k.dtype}/{v.dtype}")
+    B, H, N, d = q.shape
+    if rows is None:
+        rows = np.arange(B * H * N, dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib().oracle_attn_rows(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _CODES[q.dtype],
+        B, H, N, d, float(scale), int(bool(causal)),
+        rows.ctypes.data, n, o.ctypes.data, lse.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_rows failed with code {rc}")
+    return o, lse
+
+
+def attention(q, k, v, scale: float, causal: bool, threads: int = 0):
+    """All rows; returns (o [B,H,N,d], lse [B,H,N]) float64 numpy arrays."""
+    B, H, N, d = q.shape
+    o, lse = attn_rows(q, k, v, scale, causal, None, threads)
+    return o.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+def timed_attn_rows(q, k, v, scale, causal, rows, threads: int = 0):
+    """attn_rows plus the wall time of the C call and the thread count used."""
+    nt = min(thread_count(threads), max(1, len(rows)))
+    t0 = time.perf_counter()
+    o, lse = attn_rows(q, k, v, scale, causal, rows, threads)
+    return o, lse, time.perf_counter() - t0, nt

@@ -1,0 +1,168 @@
+/*
+ * oracle.c -- fp64 CPU oracle for exact attention (TEST INFRASTRUCTURE ONLY).
+ *
+ * The definition and its sources are stated in oracle.h.  This file is
+ * deliberately plain: one row at a time, three passes over the keys, fp64
+ * throughout, no blocking, no fused recurrence.  Threads only split the list
+ * of independent rows.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* bf16 is the upper half of an IEEE binary32: widen by placing its 16 bits
+ * above 16 zero bits. */
+static double bf16_to_f64(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int exp_bits = (h >> 10) & 0x1f;
+  int frac = h & 0x3ff;
+  double mag;
+  if (exp_bits == 0)
+    mag = ldexp((double)frac, -24); /* subnormal: frac * 2^-10 * 2^-14 */
+  else if (exp_bits == 31)
+    mag = frac ? NAN : INFINITY;
+  else
+    mag = ldexp((double)(frac | 0x400), exp_bits - 25); /* 1.frac * 2^(e-15) */
+  return sign ? -mag : mag;
+}
+
+double oracle_load(const void* base, int dtype, long long idx) {
+  switch (dtype) {
+    case ORACLE_F32: return (double)((const float*)base)[idx];
+    case ORACLE_F16: return f16_to_f64(((const uint16_t*)base)[idx]);
+    case ORACLE_BF16: return bf16_to_f64(((const uint16_t*)base)[idx]);
+    case ORACLE_F64: return ((const double*)base)[idx];
+    default: return NAN;
+  }
+}
+
+int oracle_thread_count(int threads) {
+  if (threads > 0) return threads;
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+typedef struct {
+  const void *q, *k, *v;
+  int dtype;
+  long long N, d;
+  double scale;
+  int causal;
+  const long long* rows;
+  long long n_rows;
+  double *o_out, *lse_out;
+  long long next; /* shared work counter, advanced atomically */
+} job_t;
+
+/* One query row r = (b*H + h)*N + i, three passes.  `qrow` (d doubles) and
+ * `s` (N doubles) are this thread's scratch: s holds the row's scaled scores,
+ * so passes 2 and 3 reuse the dot products of the score step. */
+static void one_row(const job_t* jb, long long r, double* qrow, double* s,
+                    double* o, double* lse) {
+  const long long N = jb->N, d = jb->d;
+  const long long head = r / N;                  /* b*H + h */
+  const long long i = r % N;                     /* query position */
+  const long long base = head * N * d;           /* start of this head */
+  const long long nkeys = jb->causal ? i + 1 : N; /* |J_i| */
+
+  for (long long c = 0; c < d; ++c)
+    qrow[c] = oracle_load(jb->q, jb->dtype, base + i * d + c);
+
+  /* scores s_j = scale * <q_i, k_j> for j in J_i */
+  for (long long j = 0; j < nkeys; ++j) {
+    double dot = 0.0;
+    for (long long c = 0; c < d; ++c)
+      dot += qrow[c] * oracle_load(jb->k, jb->dtype, base + j * d + c);
+    s[j] = jb->scale * dot;
+  }
+
+  /* pass 1: the row maximum m */
+  double m = -INFINITY;
+  for (long long j = 0; j < nkeys; ++j)
+    if (s[j] > m) m = s[j];
+
+  /* pass 2: the denominator l = sum exp(s_j - m) */
+  double l = 0.0;
+  for (long long j = 0; j < nkeys; ++j) l += exp(s[j] - m);
+
+  /* pass 3: o = sum (exp(s_j - m) / l) v_j */
+  for (long long c = 0; c < d; ++c) o[c] = 0.0;
+  for (long long j = 0; j < nkeys; ++j) {
+    const double w = exp(s[j] - m) / l;
+    for (long long c = 0; c < d; ++c)
+      o[c] += w * oracle_load(jb->v, jb->dtype, base + j * d + c);
+  }
+  *lse = m + log(l);
+}
+
+static void* worker(void* arg) {
+  job_t* jb = (job_t*)arg;
+  double* qrow = (double*)malloc((size_t)jb->d * sizeof(double));
+  double* s = (double*)malloc((size_t)jb->N * sizeof(double));
+  if (!qrow || !s) {
+    free(qrow);
+    free(s);
+    return (void*)1;
+  }
+  for (;;) {
+    long long t = __atomic_fetch_add(&jb->next, 1, __ATOMIC_RELAXED);
+    if (t >= jb->n_rows) break;
+    one_row(jb, jb->rows[t], qrow, s, jb->o_out + t * jb->d, jb->lse_out + t);
+  }
+  free(qrow);
+  free(s);
+  return NULL;
+}
+
+int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype,
+                     long long B, long long H, long long N, long long d,
+                     double scale, int causal,
+                     const long long* rows, long long n_rows,
+                     double* o_out, double* lse_out, int threads) {
+  if (!q || !k || !v || !o_out || !lse_out || (n_rows > 0 && !rows)) return -1;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || n_rows < 0) return -1;
+  if (causal != 0 && causal != 1) return -1;
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return -1;
+  const long long total = B * H * N;
+  for (long long t = 0; t < n_rows; ++t)
+    if (rows[t] < 0 || rows[t] >= total) return -1;
+  if (n_rows == 0) return 0;
+
+  job_t jb = {q, k, v, dtype, N, d, scale, causal, rows, n_rows,
+              o_out, lse_out, 0};
+  int nt = oracle_thread_count(threads);
+  if (nt > n_rows) nt = (int)n_rows;
+  pthread_t* tid = (pthread_t*)calloc((size_t)nt, sizeof(pthread_t));
+  if (!tid) return -2;
+  int started = 0, failed = 0;
+  for (int t = 0; t < nt; ++t) {
+    if (pthread_create(&tid[t], NULL, worker, &jb) != 0) break;
+    ++started;
+  }
+  if (started == 0) { /* no thread could start: do the work here */
+    if (worker(&jb) != NULL) failed = 1;
+  }
+  for (int t = 0; t < started; ++t) {
+    void* ret = NULL;
+    pthread_join(tid[t], &ret);
+    if (ret != NULL) failed = 1;
+  }
+  free(tid);
+  /* A worker that could not get its scratch leaves its rows to the others;
+   * only when every row was taken is the result complete. */
+  if (failed && jb.next < n_rows) return -2;
+  return 0;
+}

@@ -1,0 +1,78 @@
+/*
+ * oracle.h -- fp64 CPU oracle for exact scaled dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the checker, not the product:
+ * only the test suite, the package smoke check and the CPU-baseline leg of
+ * the benchmark may load it.  It shares no source, header or build step with
+ * the GPU library, and it never calls into it.
+ *
+ * What it computes (for each requested row r = (b, h, i) of a [B,H,N,d]
+ * problem) is the definition of attention written out, in the order of the
+ * three-pass safe softmax:
+ *
+ *   J_i  = {0..N-1}              (non-causal)
+ *        = {0..i}                (causal: key j kept iff j <= i)
+ *   s_j  = scale * sum_k q[b,h,i,k] * k[b,h,j,k]        for j in J_i
+ *   m    = max_{j in J_i} s_j                            (pass 1)
+ *   l    = sum_{j in J_i} exp(s_j - m)                   (pass 2)
+ *   o    = sum_{j in J_i} (exp(s_j - m) / l) * v[b,h,j,:] (pass 3)
+ *   lse  = m + ln(l)
+ *
+ * Sources: softmax(Q K^T / sqrt(d_k)) V -- "FlashAttention Engine" (the
+ * attention equation) and "The Details of Flash Attention" (section "The
+ * Attention Computation", eqs. 1-4); the three passes -- "The Details of
+ * Flash Attention", section "Safe Softmax and the Three Passes"; the causal
+ * mask as -inf fill of excluded scores -- "Transformer Attention: A
+ * Mathematical Deep Dive" (the PyTorch ScaledDotProductAttention listing);
+ * the per-row statistics kept for the backward pass (m and l) --
+ * "FlashAttention" (ai360xpert), section "Recomputation in the backward pass".
+ *
+ * All arithmetic is IEEE fp64 with plain left-to-right summation.  Inputs of
+ * lower precision are widened exactly (bf16 and fp16 by their bit-level
+ * definitions, fp32 by a C cast).
+ */
+#ifndef ORACLE_ATTN_H
+#define ORACLE_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type codes of the input arrays (this library's own numbering). */
+enum {
+  ORACLE_F32 = 0,
+  ORACLE_F16 = 1,
+  ORACLE_BF16 = 2,
+  ORACLE_F64 = 3
+};
+
+/*
+ * oracle_attn_rows
+ *   q, k, v : host pointers to contiguous row-major [B][H][N][d] arrays, all of
+ *             element type `dtype`.
+ *   rows    : host array of n_rows flat row ids r = (b*H + h)*N + i, each in
+ *             [0, B*H*N).  Rows are independent, so any subset is exact for the
+ *             rows it names.
+ *   o_out   : host [n_rows][d] fp64, written.
+ *   lse_out : host [n_rows] fp64 (natural log, scaled-score units), written.
+ *   threads : worker threads (<= 0 means one per online CPU).
+ * Returns 0 on success, -1 on an invalid argument (nothing written), -2 when
+ * memory for the per-thread scratch rows cannot be obtained.
+ * The call is synchronous; the caller owns every buffer.
+ */
+int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype,
+                     long long B, long long H, long long N, long long d,
+                     double scale, int causal,
+                     const long long* rows, long long n_rows,
+                     double* o_out, double* lse_out, int threads);
+
+/* Number of threads a call with `threads` would use. */
+int oracle_thread_count(int threads);
+
+/* Widen one element of type `dtype` at index `idx` of `base` to fp64. */
+double oracle_load(const void* base, int dtype, long long idx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ORACLE_ATTN_H */
