@@ -1,1 +1,19 @@
-"""MI355X-native FlashAttention forward (placeholder; the binding lands with the kernel)."""
+"""MI355X-native FlashAttention forward.
+
+    from exact_attention_29_amd import attention
+    o, lse = attention(q, k, v, causal=False, scale=None)
+
+q, k, v are contiguous device tensors [B, H, N, d] (bf16, fp16 or fp32).  All
+arithmetic runs in the HIP kernels of libfa.so behind the C ABI of
+include/fa.h; this package only marshals arguments.  There is no CPU path:
+without the built library every call raises.
+"""
+from ._native import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FA_ERR_HIP,
+                      FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_OK, FaError,
+                      attention, fa_fwd, fa_fwd_supported, fa_status_string,
+                      fa_version, library, library_path)
+
+__all__ = ["attention", "fa_fwd", "fa_fwd_supported", "fa_status_string", "fa_version",
+           "library", "library_path", "FaError", "FA_OK", "FA_ERR_INVALID_ARG",
+           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_FP32", "FA_DTYPE_FP16",
+           "FA_DTYPE_BF16"]

@@ -1,0 +1,118 @@
+"""ctypes binding of libfa.so (include/fa.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: FA_DTYPE_FP32, torch.float16: FA_DTYPE_FP16,
+               torch.bfloat16: FA_DTYPE_BF16}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero status from libfa.so."""
+
+    def __init__(self, status: int, where: str = "fa_fwd"):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def library():
+    """Load libfa.so.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError(
+                f"{_LIB} is not built; run `python -m exact_attention_29_amd.build` "
+                "(or __graft_entry__.build()).  There is no CPU fallback.")
+        L = ctypes.CDLL(_LIB)
+        L.fa_fwd.restype = ctypes.c_int
+        L.fa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.fa_fwd_supported.restype = ctypes.c_int
+        L.fa_fwd_supported.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_status_string.argtypes = [ctypes.c_int]
+        L.fa_version.restype = ctypes.c_int
+        L.fa_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def fa_status_string(status: int) -> str:
+    return library().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return library().fa_version()
+
+
+def fa_fwd_supported(d: int, dtype: int, causal: int) -> bool:
+    return bool(library().fa_fwd_supported(int(d), int(dtype), int(causal)))
+
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+           scale: float, causal: int, dtype: int, stream: int) -> int:
+    """The raw C entry point: integer device addresses in, status code out."""
+    return library().fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale),
+                            int(causal), int(dtype), stream)
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+              scale: float | None = None, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """O = softmax(scale * Q K^T) V and the per-row log-sum-exp, on the GPU.
+
+    q, k, v: contiguous device tensors [B, H, N, d] of one dtype.  scale
+    defaults to 1/sqrt(d).  Returns (o [B,H,N,d] in q's dtype, lse [B,H,N]
+    fp32).  The launch is asynchronous on `stream` (default: torch's current
+    stream).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, N]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
+                    stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st) if st == FA_ERR_HIP else ValueError(
+            f"fa_fwd: {fa_status_string(st)} (status {st})")
+    return out, lse

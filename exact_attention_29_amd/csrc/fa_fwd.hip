@@ -1,0 +1,538 @@
+// fa_fwd.hip -- FlashAttention forward for MI355X (gfx950, CDNA4), C ABI in include/fa.h.
+//
+// What is computed: O = softmax(scale * Q K^T) V per (batch, head), plus the
+// per-row log-sum-exp, one key/value tile at a time with the online-softmax
+// recurrence -- running row max m, running denominator l, and an unnormalized
+// accumulator rescaled by exp(m_old - m_new) when a tile raises the max, then
+// one divide by l at the end ("Deep Learning - Flash Attention", section "An
+// Example", steps 4-6; "The Details of Flash Attention", sections "Online
+// Softmax" and "Tiling the Loop").  One workgroup owns a block of query rows
+// and streams every key/value tile through it (the query-block worker of "An
+// Example", step 7).  The N x N score matrix never leaves registers.
+//
+// Two kernels:
+//  * attn_fwd_mfma16<T>: bf16 / fp16 inputs, head dim 64 or 128.  4 waves x 32
+//    query rows; K and V tiles of 64 keys double-buffered in LDS; both products
+//    on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulators.  The score tile
+//    is computed transposed (S^T = K Q^T) so that each lane owns one query
+//    column: the row max and row sum are in-lane plus one swap between the two
+//    32-lane halves, and the probabilities are already in the B-operand layout
+//    of the P V product (O^T = V^T P^T).  V is read out of its row-major LDS
+//    tile with ds_read_b64_tr_b16, which hands each lane four keys of one
+//    head-dim column.
+//  * attn_fwd_f32: fp32 inputs, head dim 64..1024, on v_mfma_f32_32x32x2_f32.
+//    Head dims above 128 are split across the waves of a workgroup (128
+//    columns each); the partial scores are summed through LDS in a fixed wave
+//    order, so every wave sees bitwise the same scores and the same softmax.
+//
+// Exponentials are exp2 of scores pre-multiplied by scale*log2(e) (v_exp_f32);
+// the log-sum-exp is converted back to natural-log units at the end.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// element-type traits for the 16-bit kernels
+struct Bf16 {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two fp32 -> one dword of two round-to-nearest-even bf16 (x in the low half)
+  static __device__ __forceinline__ unsigned pack(float x, float y) {
+    bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(unsigned, v);
+  }
+};
+struct F16 {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack(float x, float y) {
+    f16x2 v = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(unsigned, v);
+  }
+};
+
+// {x[lane], x[lane ^ 32]} with the lower-half lane's value first in both
+// halves, so a max or sum of the pair is bitwise identical across halves.
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Map the hardware workgroup id to a work item.  Workgroups are handed to the
+// 8 XCDs round-robin (id % 8); giving XCD x the contiguous range
+// [x*W/8, (x+1)*W/8) of work items keeps the query tiles of one head -- which
+// all stream the same K and V -- inside one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  const int per = total / 8;
+  if (wg >= per * 8) return wg;
+  return (wg % 8) * per + wg / 8;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel
+//
+// Layouts (D = head dim, BC = 64 keys per tile, 4 waves x 32 queries):
+//   Q fragment (registers, whole kernel): lane (q = lane%32, h = lane/32) holds
+//     Q[q][16c + 8h .. 16c + 8h + 7] for c = 0..D/16-1 (the MFMA B operand).
+//   K tile (LDS, row-major [BC][KSTR]): A operand of S^T = K Q^T, lane
+//     (key = lane%32, h) reads K[key][16c + 8h .. +7].
+//   S^T block (accumulator): lane (q, h), register r holds key
+//     8*(r/4) + 4h + r%4 of the 32-key block, for query q.
+//   P^T B operand of O^T += V^T P^T, 16-key chunk c: registers 8(c%2)..+7 of
+//     block c/2, i.e. lane (q, h) element t is key 16c + 8(t/4) + 4h + t%4.
+//   V tile (LDS, row-major [BC][VSTR]): two ds_read_b64_tr_b16 per A operand
+//     give lane (d = lane%32, h) the same eight keys for its column d.
+//   O^T (accumulator): block b, register r of lane (q, h) holds
+//     O[q][32b + 8*(r/4) + 4h + r%4].
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_mfma16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int N, int n_qtiles, int total_wg, float scale) {
+  constexpr int NW = 4, NT = NW * 64, BR = NW * 32, BC = 64;
+  constexpr int KSTR = D + 8;            // K row: 16-byte reads spread over banks
+  constexpr int VSTR = D + 32;           // V row stride = 64 mod 256 bytes for tr reads
+  constexpr int KT = BC * KSTR, VT = BC * VSTR, BUF = KT + VT;
+  constexpr int CH = BC * D / 8;         // 16-byte chunks per K (or V) tile
+  constexpr int CPT = CH / NT;           // chunks per thread
+  static_assert(CH % NT == 0, "tile must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int work = xcd_remap(blockIdx.x, total_wg);
+  const int bh = work / n_qtiles;
+  int qt = work % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+  const size_t head = (size_t)bh * N * D;
+  const int q_first = qt * BR + wave * 32;
+  const int my_q = q_first + lq;
+
+  // Q fragment
+  u32x4 qf[D / 16];
+  {
+    const uint16_t* qrow = Q + head + (size_t)my_q * D + 8 * hf;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qf[c] = (my_q < N) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
+  }
+
+  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;  // keys [0, kv_end)
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  // global -> registers for one K and V tile (rows past N read as zero)
+  u32x4 kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT, row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int key = j * BC + row;
+      const size_t off = head + (size_t)key * D + col;
+      kreg[i] = key < N ? *(const u32x4*)(K + off) : u32x4{0, 0, 0, 0};
+      vreg[i] = key < N ? *(const u32x4*)(V + off) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* kt = smem + buf * BUF;
+    uint16_t* vt = kt + KT;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT, row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *(u32x4*)(kt + row * KSTR + col) = kreg[i];
+      *(u32x4*)(vt + row * VSTR + col) = vreg[i];
+    }
+  };
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
+  // Running state per query (both lane halves agree on m_run and mc_run):
+  //   m_run  -- max of the raw scores q.k seen so far;
+  //   mc_run -- the exponent reference fl(m_run * c2) every exp2 so far was
+  //             taken against, so l and O hold sum 2^(s*c2 - mc_run) terms;
+  //   l_run  -- this half's share of that sum.
+  // Rescaling goes from one stored reference to the next, alpha =
+  // exp2(mc_old - mc_new), which is exactly 1 when the max is unchanged; a
+  // rescale recomputed from m (m*c2 - fl(m*c2)) would multiply the state by a
+  // rounding residual on every tile and drift over long rows.
+  float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
+  const float c2 = scale * kLog2e;
+
+  // lane constants of the transposed V read (see layout notes above)
+  const int tr_i = lane & 15, tr_grp = lane >> 4;
+  const int tr_h = tr_grp >> 1, tr_dsub = tr_grp & 1;
+  const int tr_row = 4 * tr_h + (tr_i >> 2);            // + 16c (+ 8 for the upper four)
+  const int tr_col = 16 * tr_dsub + 4 * (tr_i & 3);     // + 32b
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);  // in flight during this tile's math
+    const int k0 = j * BC;
+    const bool skip = CAUSAL && (k0 > q_first + 31);  // every key above this wave's rows
+    if (!skip) {
+      const uint16_t* kt = smem + buf * BUF;
+      const uint16_t* vt = kt + KT;
+      // S^T = K Q^T
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b) {
+        s[b] = f32x16{};
+        const uint16_t* kr = kt + (32 * b + lq) * KSTR + 8 * hf;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) s[b] = TT::mma(*(const u32x4*)(kr + 16 * c), qf[c], s[b]);
+      }
+      // mask keys past the diagonal (causal) or past the sequence
+      const bool need_mask = (CAUSAL && k0 + BC - 1 > q_first) || (k0 + BC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool keep = key < N && (!CAUSAL || key <= my_q);
+            if (!keep) s[b][r] = -INFINITY;
+          }
+      }
+      // online softmax update
+      float mt = s[0][0];
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[b][r]);
+      mt = half_max(mt);
+      const float m_new = fmaxf(m_run, mt);
+      // A row with every key so far masked keeps m = -inf; its offset is 0 so
+      // that exp2(-inf - 0) = 0 and no -inf - (-inf) arises.
+      const float mc_new = (m_new == -INFINITY) ? -INFINITY : m_new * c2;
+      const float off = (m_new == -INFINITY) ? 0.f : mc_new;
+      const float alpha = fast_exp2(mc_run - off);
+      float lsum = 0.f;
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[b][r], c2, -off));
+          s[b][r] = p;
+          lsum += p;
+        }
+      l_run = fmaf(l_run, alpha, lsum);
+      m_run = m_new;
+      mc_run = mc_new;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int c = 0; c < BC / 16; ++c) {
+        const int r0 = 8 * (c & 1);
+        const f32x16& sb = s[c >> 1];
+        const u32x4 pf = {TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
+                          TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
+        const uint16_t* vrow = vt + (16 * c + tr_row) * VSTR + tr_col;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vrow + 32 * b));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vrow + 8 * VSTR + 32 * b));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 va = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          o[b] = TT::mma(va, pf, o[b]);
+        }
+      }
+    }
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: O = O^T / l, lse = scale * m + ln(l)
+  const float l_tot = half_sum(l_run);
+  if (my_q < N) {
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = O + head + (size_t)my_q * D + 4 * hf;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {TT::pack(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv),
+                         TT::pack(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
+        *(u32x2*)(orow + 32 * b + 8 * g) = w;
+      }
+    if (hf == 0) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel
+//
+// A workgroup owns 32 query rows and DS waves; wave w owns head-dim columns
+// [w*DSL, (w+1)*DSL).  Keys go 32 per tile.  With the 32x32x2 fp32 MFMA each
+// lane supplies one element per operand, so K and V are read from global
+// memory (L2) straight into registers in operand order:
+//   S^T = K Q^T : step (u, v) contracts column  w*DSL + 8u + 4h + v,
+//                 lane (key, h) gives K[key][..], lane (q, h) gives Q[q][..].
+//   O^T += V^T P^T : step r contracts key 8(r/4) + 4h + r%4 (register r of
+//                 the score block); output block bb row i is column
+//                 w*DSL + NB*i + bb (NB = DSL/32 blocks), so one lane's NB
+//                 values of a V row are contiguous.
+template <int DSL, int DS, bool CAUSAL>
+__global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
+    float scale) {
+  constexpr int D = DSL * DS, NB = DSL / 32, BC = 32;
+  __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int work = xcd_remap(blockIdx.x, total_wg);
+  const int bh = work / n_qtiles;
+  int qt = work % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const size_t head = (size_t)bh * N * D;
+  const int q_first = qt * 32;
+  const int my_q = q_first + lq;
+  const int col0 = wave * DSL;
+
+  f32x4 qf[DSL / 8];
+  {
+    const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
+#pragma unroll
+    for (int u = 0; u < DSL / 8; ++u)
+      qf[u] = (my_q < N) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+  }
+  f32x16 o[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) o[b] = f32x16{};
+  // running state as in the 16-bit kernel: raw max, exponent reference, sum
+  float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
+  const float c2 = scale * kLog2e;
+  const int kv_end = CAUSAL ? min(N, q_first + 32) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * BC;
+    // partial S^T over this wave's columns
+    f32x16 s = f32x16{};
+    {
+      const int key = k0 + lq;
+      const float* krow = K + head + (size_t)key * D + col0 + 4 * hf;
+#pragma unroll
+      for (int u = 0; u < DSL / 8; ++u) {
+        const f32x4 kv = key < N ? *(const f32x4*)(krow + 8 * u) : f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[v], qf[u][v], s, 0, 0, 0);
+      }
+    }
+    if (DS > 1) {  // full scores = sum of the DS partials, in wave order
+      red[wave * 64 + lane] = s;
+      __syncthreads();
+      s = red[lane];
+#pragma unroll
+      for (int w = 1; w < DS; ++w) s += red[w * 64 + lane];
+      __syncthreads();
+    }
+    const bool need_mask = (CAUSAL && k0 + BC - 1 > q_first) || (k0 + BC > N);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (!(key < N && (!CAUSAL || key <= my_q))) s[r] = -INFINITY;
+      }
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = half_max(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float mc_new = (m_new == -INFINITY) ? -INFINITY : m_new * c2;
+    const float off = (m_new == -INFINITY) ? 0.f : mc_new;
+    const float alpha = fast_exp2(mc_run - off);
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(fmaf(s[r], c2, -off));
+      s[r] = p;
+      lsum += p;
+    }
+    l_run = fmaf(l_run, alpha, lsum);
+    m_run = m_new;
+    mc_run = mc_new;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b] *= alpha;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const float* vrow = V + head + (size_t)key * D + col0 + NB * lq;
+      float vv[NB];
+      if (key < N) {
+        if constexpr (NB == 4) {
+          const f32x4 t = *(const f32x4*)vrow;
+          vv[0] = t[0]; vv[1] = t[1]; vv[2] = t[2]; vv[3] = t[3];
+        } else if constexpr (NB == 2) {
+          const f32x2 t = *(const f32x2*)vrow;
+          vv[0] = t[0]; vv[1] = t[1];
+        } else {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) vv[b] = vrow[b];
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) vv[b] = 0.f;
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[b], s[r], o[b], 0, 0, 0);
+    }
+  }
+
+  const float l_tot = half_sum(l_run);
+  if (my_q < N) {
+    const float inv = 1.f / l_tot;
+    float* orow = O + head + (size_t)my_q * D + col0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * hf + (r & 3);
+      if constexpr (NB == 4) {
+        *(f32x4*)(orow + 4 * i) = f32x4{o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv};
+      } else if constexpr (NB == 2) {
+        *(f32x2*)(orow + 2 * i) = f32x2{o[0][r] * inv, o[1][r] * inv};
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) orow[NB * i + b] = o[b][r] * inv;
+      }
+    }
+    if (hf == 0 && wave == 0)
+      LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+template <class TT, int D>
+hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                    int N, float scale, bool causal, hipStream_t st) {
+  const int nq = (N + 127) / 128;
+  const int total = nq * BH;
+  const dim3 grid(total), block(256);
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_mfma16<TT, D, true>), grid, block, 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total,
+                       scale);
+  else
+    hipLaunchKernelGGL((attn_fwd_mfma16<TT, D, false>), grid, block, 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total,
+                       scale);
+  return hipGetLastError();
+}
+
+template <int DSL, int DS>
+hipError_t launch32(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                    int N, float scale, bool causal, hipStream_t st) {
+  const int nq = (N + 31) / 32;
+  const int total = nq * BH;
+  const dim3 grid(total), block(DS * 64);
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true>), grid, block, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale);
+  else
+    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false>), grid, block, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale);
+  return hipGetLastError();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_supported(int d, int dtype, int causal) {
+  if (causal != 0 && causal != 1) return 0;
+  if (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16) return d == 64 || d == 128;
+  if (dtype == FA_DTYPE_FP32) return d == 64 || d == 128 || d == 256 || d == 512 || d == 1024;
+  return 0;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 24)) return FA_ERR_INVALID_ARG;
+  const long long nq_max = (N + 31) / 32;  // most query tiles any kernel uses
+  if (nq_max * BH > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
+    return FA_ERR_UNSUPPORTED;
+  if (!fa_fwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
+
+  hipStream_t st = (hipStream_t)stream;
+  const bool c = causal != 0;
+  const int bh = (int)BH;
+  hipError_t e = hipSuccess;
+  if (dtype == FA_DTYPE_BF16) {
+    e = d == 64 ? launch16<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                : launch16<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+  } else if (dtype == FA_DTYPE_FP16) {
+    e = d == 64 ? launch16<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                : launch16<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+  } else {
+    switch (d) {
+      case 64: e = launch32<64, 1>(q, k, v, o, lse, bh, N, scale, c, st); break;
+      case 128: e = launch32<128, 1>(q, k, v, o, lse, bh, N, scale, c, st); break;
+      case 256: e = launch32<128, 2>(q, k, v, o, lse, bh, N, scale, c, st); break;
+      case 512: e = launch32<128, 4>(q, k, v, o, lse, bh, N, scale, c, st); break;
+      default: e = launch32<128, 8>(q, k, v, o, lse, bh, N, scale, c, st); break;
+    }
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype or alignment";
+    case FA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

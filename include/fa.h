@@ -1,0 +1,96 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention forward library, libfa.so.
+ *
+ * The one operation is exact scaled dot-product attention,
+ *     O = softmax(scale * Q K^T) V          (softmax over each query row),
+ * as defined in "FlashAttention Engine" (the attention equation) and "The
+ * Details of Flash Attention" (section "The Attention Computation", eqs. 1-4),
+ * computed tile by tile with the online-softmax recurrence ("The Details of
+ * Flash Attention", sections "Online Softmax" and "Tiling the Loop"; "Deep
+ * Learning - Flash Attention", section "An Example", steps 4-6) so that the
+ * N x N score matrix never exists in device memory.  Alongside O the library
+ * writes the per-row log-sum-exp, the statistic a recomputing backward pass
+ * needs ("FlashAttention" (ai360xpert), section "Recomputation in the backward
+ * pass").
+ *
+ * No function here allocates or frees device memory, synchronizes, or keeps
+ * state between calls.  No C++ exception crosses this boundary.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+typedef enum {
+  FA_DTYPE_FP32 = 0,
+  FA_DTYPE_FP16 = 1,
+  FA_DTYPE_BF16 = 2
+} fa_dtype_t;
+
+/* Return codes. */
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, causal not 0/1,
+                             non-finite or non-positive scale, size overflow */
+  FA_ERR_UNSUPPORTED = 2, /* head dim or dtype without a kernel, pointer not
+                             16-byte aligned */
+  FA_ERR_HIP = 3          /* the kernel launch reported an error */
+} fa_status_t;
+
+/*
+ * fa_fwd -- attention forward pass on one GPU.
+ *
+ *   q, k, v : device pointers, contiguous row-major [B][H][N][d] arrays of
+ *             element type `dtype` (the (batch, head, sequence, head-dim) order
+ *             of "The Details of Flash Attention", section "The Attention
+ *             Computation").  Batches and heads are independent problems.
+ *   o       : device pointer, [B][H][N][d] of the same type, written: row i of
+ *             head (b, h) is sum_j softmax_j(scale * q_i . k_j) v_j, rounded
+ *             from fp32 to the element type (round to nearest even).
+ *   lse     : device pointer, [B][H][N] fp32, written:
+ *             lse_i = ln sum_{j kept} exp(scale * q_i . k_j)  (natural log,
+ *             scaled-score units, masked keys excluded).
+ *   B, H, N, d : batch, heads, sequence length (queries = keys = N), head dim.
+ *   scale   : multiplies q_i . k_j before the softmax (callers normally pass
+ *             1/sqrt(d)).  Applied to the fp32 scores, never folded into q.
+ *   causal  : 0 = every key is kept; 1 = key j is kept for query i iff j <= i
+ *             (lower-triangular mask with the diagonal; excluded scores behave
+ *             as -inf, i.e. contribute exactly zero weight).
+ *   dtype   : fa_dtype_t.  Supported head dims: bf16 and fp16 -- 64, 128;
+ *             fp32 -- 64, 128, 256, 512, 1024.
+ *   stream  : a hipStream_t passed as void*; NULL means the null stream.
+ *
+ * Ownership: the caller allocates and owns every buffer; q, k, v are only
+ * read; o and lse must not overlap q, k, v or each other.  The call is
+ * asynchronous on `stream` and returns once the kernel is enqueued; results
+ * are valid after the stream is synchronized.
+ *
+ * Errors: every argument is checked before any HIP call.  On any error code
+ * nothing is launched and o, lse are not written.  FA_ERR_HIP is returned when
+ * hipGetLastError reports a failure right after the launch.
+ *
+ * Arithmetic: scores and all softmax statistics are fp32; bf16/fp16 products
+ * accumulate in fp32 on the matrix cores; probabilities are rounded to the
+ * input type before the product with V.  Results are bitwise reproducible run
+ * to run (no atomics, fixed reduction order).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/* 1 when fa_fwd has a kernel for (d, dtype, causal), else 0. */
+int fa_fwd_supported(int d, int dtype, int causal);
+
+/* Static description of a status code ("ok", "invalid argument", ...). */
+const char* fa_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H */
