@@ -1,0 +1,208 @@
+"""Benchmark: attention forward TFLOPS and fraction of the MI355X bf16 MFMA peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+A step is one fa_fwd call (the whole forward pass) over one batch of the
+workload, inputs already resident in device memory.  W untimed steps, then K
+timed steps between two synchronizations; one JSON line on stdout.
+
+Extra objects on the line:
+  roofline     -- the kernel's achieved TFLOP/s (algorithmic FLOPs per launch
+                  over the mean launch duration from HIP events recorded on
+                  the stream the kernel runs on) against the bf16 dense MFMA
+                  peak; `traffic` is the HBM bytes per launch measured with
+                  rocprofv3 counters, read from the profile summary of the
+                  same kernel source (null if the source changed since).
+  cpu_baseline -- the fp64 oracle timed on the host cores on a bounded,
+                  seeded sample of rows of the same workload, in the same
+                  unit; the GPU output on those rows is compared too.
+
+Other modes (used to take the profiles):
+  --no-cpu-baseline        skip the oracle leg
+  --copy-calibration MiB   run only a plain device copy of that size
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (1 GPU)"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_FP32_TFLOPS = 157.3    # 256 CU x 256 FLOP/clk x 2.4 GHz, dense MFMA
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_29_amd", "csrc", "fa_fwd.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kernel_tag(w) -> str:
+    """Name of the kernel instance a workload runs, as used by profiles/."""
+    kern = "attn_fwd_f32" if w.dtype == "fp32" else "attn_fwd_mfma16"
+    mask = "causal" if w.causal else "noncausal"
+    return f"{kern}_{w.dtype}_{mask}_B{w.B}_H{w.H}_N{w.N}_d{w.d}"
+
+
+def read_traffic(w):
+    """HBM bytes per launch from profiles/<kernel tag>.traffic.md, if that
+    summary was taken from the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag(w)}.traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    b = re.search(r"HBM bytes per launch:\s*`?([0-9.eE+]+)", text)
+    if not h or not b or h.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
+
+
+def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s: float, seed: int = 0):
+    """Time the oracle on a seeded uniform sample of rows sized to ~target_s."""
+    import oracle
+
+    rng = np.random.default_rng(seed)
+    total_rows = w.B * w.H * w.N
+
+    def flops(rows):
+        pos = rows % w.N
+        keys = (pos + 1) if w.causal else np.full_like(pos, w.N)
+        return float((4.0 * keys * w.d).sum())
+
+    perm = rng.permutation(total_rows)
+    first = np.sort(perm[:min(512, total_rows)])
+    o1, l1, t1, nt = oracle.timed_attn_rows(q, k, v, w.scale, w.causal, first)
+    rate = flops(first) / max(t1, 1e-9)
+    # enough further rows to bring the total to about target_s
+    avg = flops(first) / len(first)
+    more = int(max(0.0, target_s - t1) * rate / avg)
+    more = min(more, total_rows - len(first))
+    rows, o_ref, l_ref, secs = first, o1, l1, t1
+    if more > 0:
+        second = np.sort(perm[len(first):len(first) + more])
+        o2, l2, t2, _ = oracle.timed_attn_rows(q, k, v, w.scale, w.causal, second)
+        rows = np.concatenate([first, second])
+        o_ref, l_ref, secs = np.concatenate([o1, o2]), np.concatenate([l1, l2]), t1 + t2
+    fl = flops(rows)
+    og = o_gpu.double().cpu().reshape(total_rows, w.d).numpy()[rows]
+    lg = lse_gpu.double().cpu().reshape(total_rows).numpy()[rows]
+    parity = {"rows": int(len(rows)), "max_abs_o": float(np.abs(og - o_ref).max()),
+              "mean_abs_o": float(np.abs(og - o_ref).mean()),
+              "max_abs_lse": float(np.abs(lg - l_ref).max())}
+    return {
+        "value": fl / secs / 1e12, "unit": "TFLOPS", "cores": int(nt), "kind": "oracle",
+        "sample": (f"{len(rows)} of {total_rows} query rows of the workload, seeded uniform "
+                   f"over batch, head and position; FLOPs counted 4*|keys kept|*d per row; "
+                   f"{secs:.1f} s of oracle time"),
+        "seconds": secs, "gflop": fl / 1e9,
+    }, parity
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the forward pass on a single "
+              "MI355X (no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
+        return 1
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
+
+    import exact_attention_29_amd as fa
+    from exact_attention_29_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    q_h, k_h, v_h = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # timed region: K steps; a HIP event pair around every launch on its stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype in ("bf16", "fp16") else PEAK_FP32_TFLOPS
+    traffic = read_traffic(w)
+    algo_bytes = (4 * w.B * w.H * w.N * w.d * (2 if w.dtype != "fp32" else 4)
+                  + 4 * w.B * w.H * w.N)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) per the workload recipe)",
+        "config": {**w.as_dict(), "flops_per_step": w.flops,
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel_ms": round(kernel_ms, 4),
+                     "algorithmic_bytes": algo_bytes,
+                     "kernel_source_sha256_16": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        cb, par = cpu_baseline(w, q_h, k_h, v_h, o, lse, args.cpu_seconds)
+        line["cpu_baseline"] = cb
+        line["parity_on_cpu_sample"] = par
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
