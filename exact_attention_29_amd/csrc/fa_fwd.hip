@@ -49,6 +49,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// The exponent reference of a row moves only when its max has grown past it
+// by more than this many powers of two (probabilities stay <= 256).
+constexpr float kLazyRescale = 8.0f;
+// Word 3 of a raw buffer descriptor on gfx9-class GPUs: 32-bit data format,
+// no swizzle, no stride; reads past num_records return zero.
+constexpr int kBufferFlags = 0x00020000;
 
 // ---------------------------------------------------------------------------
 // element-type traits for the 16-bit kernels
@@ -62,6 +68,11 @@ struct Bf16 {
     bf16x2 v = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(unsigned, v);
   }
+  // acc + both halves of a packed pair (v_dot2c_f32_bf16 against (1, 1))
+  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+  }
 };
 struct F16 {
   static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
@@ -71,6 +82,10 @@ struct F16 {
   static __device__ __forceinline__ unsigned pack(float x, float y) {
     f16x2 v = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(unsigned, v);
+  }
+  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
   }
 };
 
@@ -149,16 +164,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;  // keys [0, kv_end)
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  // global -> registers for one K and V tile (rows past N read as zero)
+  // global -> registers for one K and V tile.  Raw buffer loads over this
+  // head's N*D elements: a 16-byte chunk of a row past N lies wholly outside
+  // the descriptor's range and reads as zero, so the tail needs no branch.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, N * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head), (short)0, N * D * 2, kBufferFlags);
   u32x4 kreg[CPT], vreg[CPT];
   auto load_tile = [&](int j) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = j * BC + row;
-      const size_t off = head + (size_t)key * D + col;
-      kreg[i] = key < N ? *(const u32x4*)(K + off) : u32x4{0, 0, 0, 0};
-      vreg[i] = key < N ? *(const u32x4*)(V + off) : u32x4{0, 0, 0, 0};
+      const int off = ((j * BC + row) * D + col) * 2;
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
@@ -177,14 +197,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
   // Running state per query (both lane halves agree on m_run and mc_run):
   //   m_run  -- max of the raw scores q.k seen so far;
-  //   mc_run -- the exponent reference fl(m_run * c2) every exp2 so far was
-  //             taken against, so l and O hold sum 2^(s*c2 - mc_run) terms;
-  //   l_run  -- this half's share of that sum.
-  // Rescaling goes from one stored reference to the next, alpha =
-  // exp2(mc_old - mc_new), which is exactly 1 when the max is unchanged; a
-  // rescale recomputed from m (m*c2 - fl(m*c2)) would multiply the state by a
+  //   mc_run -- the exponent reference every exp2 so far was taken against,
+  //             so l and O hold sums of 2^(s*c2 - mc_run);
+  //   l_run  -- this half's share of that sum (fp32 terms; gives the lse);
+  //   lw_run -- the same sum over the terms as rounded to the input type,
+  //             i.e. the weights the P V product really used.  O is divided
+  //             by it, so O is an exact convex combination of V rows with
+  //             those weights: a dominant key's rounding cancels instead of
+  //             scaling the output.
+  // The reference is moved only when some row of the wave has outgrown it by
+  // more than kLazyRescale (so every p stays <= 2^kLazyRescale, far inside
+  // fp32 and bf16 range); then each row moves to fl(m_run * c2) and the state
+  // is rescaled from one stored reference to the next, alpha =
+  // exp2(mc_old - mc_new).  Any reference gives the same softmax, and the
+  // log-sum-exp is taken against the one in use.  Rescaling by a factor
+  // recomputed from m (m*c2 - fl(m*c2)) would instead multiply the state by a
   // rounding residual on every tile and drift over long rows.
-  float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
   const float c2 = scale * kLog2e;
 
   // lane constants of the transposed V read (see layout notes above)
@@ -233,12 +262,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[b][r]);
       mt = half_max(mt);
-      const float m_new = fmaxf(m_run, mt);
-      // A row with every key so far masked keeps m = -inf; its offset is 0 so
-      // that exp2(-inf - 0) = 0 and no -inf - (-inf) arises.
-      const float mc_new = (m_new == -INFINITY) ? -INFINITY : m_new * c2;
-      const float off = (m_new == -INFINITY) ? 0.f : mc_new;
-      const float alpha = fast_exp2(mc_run - off);
+      m_run = fmaxf(m_run, mt);
+      // A row with every key so far masked keeps m = -inf and reference -inf.
+      const float mc_cand = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
+      if (__builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0) {
+        // 0 for a row's first finite tile; a row still fully masked has a zero
+        // state and keeps it (alpha = 1 avoids exp2(-inf - (-inf)))
+        const float alpha = (mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
+        mc_run = mc_cand;
+        l_run *= alpha;
+        lw_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+      }
+      // offset 0 for a still fully masked row: exp2(-inf - 0) = 0, never -inf - (-inf)
+      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
       float lsum = 0.f;
 #pragma unroll
       for (int b = 0; b < BC / 32; ++b)
@@ -248,11 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           s[b][r] = p;
           lsum += p;
         }
-      l_run = fmaf(l_run, alpha, lsum);
-      m_run = m_new;
-      mc_run = mc_new;
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+      l_run += lsum;
       // O^T += V^T P^T
 #pragma unroll
       for (int c = 0; c < BC / 16; ++c) {
@@ -260,6 +294,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const f32x16& sb = s[c >> 1];
         const u32x4 pf = {TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
                           TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
+        lw_run = TT::sum2(pf[3], TT::sum2(pf[2], TT::sum2(pf[1], TT::sum2(pf[0], lw_run))));
         const uint16_t* vrow = vt + (16 * c + tr_row) * VSTR + tr_col;
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
@@ -277,10 +312,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
 
-  // epilogue: O = O^T / l, lse = scale * m + ln(l)
+  // epilogue: O = O^T / (sum of the rounded weights), lse = ln2 * (mc + log2 l)
   const float l_tot = half_sum(l_run);
+  const float lw_tot = half_sum(lw_run);
   if (my_q < N) {
-    const float inv = 1.f / l_tot;
+    const float inv = __builtin_amdgcn_rcpf(lw_tot);
     uint16_t* orow = O + head + (size_t)my_q * D + 4 * hf;
 #pragma unroll
     for (int b = 0; b < D / 32; ++b)
@@ -499,6 +535,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
     return FA_ERR_UNSUPPORTED;
   if (!fa_fwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
+  // per-head byte offsets (plus one tile of slack) must fit the 32-bit
+  // offsets of the buffer loads
+  const long long elem = dtype == FA_DTYPE_FP32 ? 4 : 2;
+  if (((long long)N + 128) * d * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
 
   hipStream_t st = (hipStream_t)stream;
