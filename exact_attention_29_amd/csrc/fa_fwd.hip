@@ -31,6 +31,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fa.h"
 
@@ -55,6 +56,8 @@ constexpr float kLazyRescale = 8.0f;
 // Word 3 of a raw buffer descriptor on gfx9-class GPUs: 32-bit data format,
 // no swizzle, no stride; reads past num_records return zero.
 constexpr int kBufferFlags = 0x00020000;
+// s_waitcnt operand that waits for vmcnt = 0 only (expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // ---------------------------------------------------------------------------
 // element-type traits for the 16-bit kernels
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(CH % NT == 0, "tile must split evenly over the workgroup");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const int work = xcd_remap(blockIdx.x, total_wg);
   const int bh = work / n_qtiles;
@@ -331,6 +334,388 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
+// LDS tile layout shared by the ping-pong kernel
+//
+// A K or V tile is 64 keys x D elements (2D bytes per key row), stored as
+// 1 KB blocks of 16 rows x 4 sixteen-byte chunks: block (rg, cg) holds rows
+// 16rg..16rg+15 and chunks 4cg..4cg+3, at byte (rg * D/32 + cg) * 1024.
+//   K blocks are chunk-major inside (chunk ci, row ri at (ci*16 + ri)*16), so
+//     the 16 rows one 16-lane group reads for an A operand are 16 consecutive
+//     16-byte slots: no bank conflicts.
+//   V blocks are row-major inside (row ri, chunk ci at (ri*4 + ci)*16), so a
+//     16-lane group's ds_read_b64_tr_b16 (4 rows x 32 bytes) spans 256
+//     distinct bytes.
+// Each block is filled by one wave-wide buffer load that writes straight to
+// LDS (lane L's 16 bytes land at block + 16L; rows past N read as zero), and
+// every operand read is a lane constant plus a compile-time offset.
+template <int D>
+struct TileLayout {
+  static constexpr int CG = D / 32;               // chunk groups per row
+  static constexpr int BLOCKS = 4 * CG;           // 1 KB blocks per tile
+  static constexpr int BYTES = BLOCKS * 1024;     // = 64 * D * 2
+  // source element offset (within the tile's first row) of lane L in block `blk`
+  static __device__ __forceinline__ int k_src(int blk, int L) {
+    const int rg = blk / CG, cg = blk % CG;
+    return (16 * rg + (L & 15)) * D + 8 * (4 * cg + (L >> 4));
+  }
+  static __device__ __forceinline__ int v_src(int blk, int L) {
+    const int rg = blk / CG, cg = blk % CG;
+    return (16 * rg + (L >> 2)) * D + 8 * (4 * cg + (L & 3));
+  }
+};
+
+// A raw buffer descriptor as four SGPRs: 48-bit base, no stride,
+// num_records bytes, reads past the end return zero.
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, unsigned bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(unsigned)__builtin_amdgcn_readfirstlane((unsigned)a),
+               (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu),
+               (unsigned)__builtin_amdgcn_readfirstlane(bytes), (unsigned)kBufferFlags};
+}
+
+// One wave-wide 16-byte-per-lane buffer load straight into LDS: lane L's
+// bytes land at LDS byte address lds_addr + 16 L.  Written as inline asm so
+// that the compiler does not wait for it at every LDS read and barrier: the
+// caller waits (vmcnt) before the barrier that precedes the first read of
+// the data.
+__device__ __forceinline__ void dma16(u32x4 desc, unsigned lds_addr, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voffset), "s"(desc)
+               : "memory", "m0");
+}
+
+// This wave's share of one K (or V) tile: blocks first_blk, first_blk +
+// stride, ... of the tile whose first key row is key0.
+template <int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0, int first_blk,
+                                         int stride, int lane) {
+  using L = TileLayout<D>;
+#pragma unroll
+  for (int blk = first_blk; blk < L::BLOCKS; blk += stride) {
+    const int el = key0 * D + (IS_V ? L::v_src(blk, lane) : L::k_src(blk, lane));
+    dma16(desc, lds_tile + blk * 1024, el * 2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel, software-pipelined
+//
+// A wave issues in order, so its matrix-core work overlaps its vector work
+// only when the two are interleaved in its instruction stream (an MFMA runs
+// for 32 cycles while the wave keeps issuing independent VALU).  Each
+// iteration j therefore pairs independent work:
+//   step A: S_{j+1} = K_{j+1} Q^T (MFMA)  with  exponentials, sums and packing
+//           of tile j's probabilities P_j (VALU);
+//   step B: O += P_j V_j (MFMA)           with  mask, max and reference update
+//           of tile j+1 (VALU); a rare rescale of O follows the product.
+// LDS stage j holds (K_{j+1}, V_j) in buffer j % 2 (block layout above),
+// loaded by all waves during iteration j-1; one barrier per iteration.
+// Tiles that need a mask (diagonal, sequence tail) and each wave's last tile
+// take a general path without the interleaving constraints.
+// Operand layouts are those of attn_fwd_mfma16.
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_sp(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int N, int n_qtiles, int total_wg, float scale) {
+  constexpr int NW = 4, BR = 32 * NW, BC = 64;
+  using LY = TileLayout<D>;
+  constexpr int TB = LY::BYTES, CG = LY::CG;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TB];  // [buffer][K, V]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const int work = xcd_remap(blockIdx.x, total_wg);
+  const int bh = work / n_qtiles;
+  int qt = work % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+  const size_t head = (size_t)bh * N * D;
+  const int q_first = qt * BR + 32 * wave;
+  const int my_q = q_first + lq;
+
+  u32x4 qf[D / 16];
+  {
+    const uint16_t* qrow = Q + head + (size_t)my_q * D + 8 * hf;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qf[c] = (my_q < N) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
+  }
+
+  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
+  const int T = (kv_end + BC - 1) / BC;
+  const int my_T = CAUSAL ? min(T, (q_first + 31) / BC + 1) : T;
+
+  const u32x4 kdesc = buffer_desc(K + head, (unsigned)N * D * 2);
+  const u32x4 vdesc = buffer_desc(V + head, (unsigned)N * D * 2);
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer st & 1
+  auto load_stage = [&](int st) {
+    const unsigned base = lds0 + (st & 1) * 2 * TB;
+    if (st + 1 < T) dma_tile<D, false>(kdesc, base, (st + 1) * BC, wave, NW, lane);
+    if (st >= 0) dma_tile<D, true>(vdesc, base + TB, st * BC, wave, NW, lane);
+  };
+
+  const int k_lane = (lq >> 4) * CG * 1024 + (hf * 16 + (lq & 15)) * 16;
+  const int tr_i = lane & 15, tr_grp = lane >> 4;
+  const int v_lane = (4 * (tr_grp >> 1) + (tr_i >> 2)) * 64 + (2 * (tr_grp & 1) + ((tr_i & 3) >> 1)) * 16 +
+                     8 * (tr_i & 1);
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
+  // running state, as in attn_fwd_mfma16
+  float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
+  const float c2 = scale * kLog2e;
+  u32x4 pf[BC / 16];  // P_j packed, B operand of the P V product
+
+  auto qk = [&](const uint8_t* kt, f32x16 (&acc)[BC / 32]) {
+#pragma unroll
+    for (int b = 0; b < BC / 32; ++b) {
+      acc[b] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const u32x4 a = *(const u32x4*)(kt + k_lane + (2 * b * CG + (c >> 1)) * 1024 + (c & 1) * 512);
+        acc[b] = TT::mma(a, qf[c], acc[b]);
+      }
+    }
+  };
+  auto pv = [&](const uint8_t* vt) {
+#pragma unroll
+    for (int cc = 0; cc < BC / 16; ++cc)
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        const uint8_t* va = vt + v_lane + (cc * CG + b) * 1024;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        o[b] = TT::mma(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pf[cc], o[b]);
+      }
+  };
+  // Tile t's mask (if any), row max and reference move.  Returns the factor
+  // for O, which the caller applies after O has received the previous tile;
+  // l and lw are rescaled here.  `resc` tells whether any row moved.
+  auto part1 = [&](f32x16 (&sv)[BC / 32], int t, bool masked, bool& resc) -> float {
+    if (masked) {
+      const int k0 = t * BC;
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool keep = key < N && (!CAUSAL || key <= my_q);
+          if (!keep) sv[b][r] = -INFINITY;
+        }
+    }
+    float mt = sv[0][0];
+#pragma unroll
+    for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[b][r]);
+    mt = half_max(mt);
+    m_run = fmaxf(m_run, mt);
+    const float mc_cand = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
+    resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
+    // 0 for a row's first finite tile; a still fully masked row keeps alpha 1
+    const float alpha = (!resc || mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
+    mc_run = resc ? mc_cand : mc_run;
+    l_run *= alpha;
+    lw_run *= alpha;
+    return alpha;
+  };
+  // Exponentials against the current reference, the two sums, and P packed.
+  auto part2 = [&](f32x16 (&sv)[BC / 32]) {
+    const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
+    float ls[2] = {0.f, 0.f}, lws[2] = {0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sv[b][r], c2, -off));
+        sv[b][r] = p;
+        ls[r & 1] += p;
+      }
+#pragma unroll
+    for (int c = 0; c < BC / 16; ++c) {
+      const int r0 = 8 * (c & 1);
+      const f32x16& sb = sv[c >> 1];
+      pf[c] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
+                    TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
+      lws[c & 1] = TT::sum2(pf[c][3], TT::sum2(pf[c][2], TT::sum2(pf[c][1], TT::sum2(pf[c][0], lws[c & 1]))));
+    }
+    l_run += ls[0] + ls[1];
+    lw_run += lws[0] + lws[1];
+  };
+  auto tile_masked = [&](int t) { return (CAUSAL && t * BC + BC - 1 > q_first) || (t * BC + BC > N); };
+
+  // One steady-state step (tile j's softmax and product, tile j+1's scores
+  // and statistics), written in issue order and fenced so that every MFMA is
+  // followed by the independent vector work that hides it.
+  auto steady = [&](f32x16 (&cur)[BC / 32], f32x16 (&nxt)[BC / 32], const uint8_t* kt,
+                    const uint8_t* vt, int t_next) {
+    constexpr int NQK = BC / 32 * D / 16, NPV = BC / 16 * D / 32;
+    constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
+    const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
+    float ls0 = 0.f, ls1 = 0.f, lw0 = 0.f, lw1 = 0.f;
+    // ---- step A: S_{j+1} (MFMA) with exp / sums / packing of tile j (VALU)
+    auto kaddr = [&](int i) {
+      const int bb = i / (D / 16), c = i % (D / 16);
+      return (const u32x4*)(kt + k_lane + (2 * bb * CG + (c >> 1)) * 1024 + (c & 1) * 512);
+    };
+    u32x4 kop[3];
+    kop[0] = *kaddr(0);
+    kop[1] = *kaddr(1);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int EPM = ELEM / NQK;  // elements of tile j per MFMA (2 at d = 128, 4 at d = 64)
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      if (i + 2 < NQK) kop[(i + 2) % 3] = *kaddr(i + 2);
+      const int bb = i / (D / 16), c = i % (D / 16);
+      nxt[bb] = TT::mma(kop[i % 3], qf[c], c == 0 ? f32x16{} : nxt[bb]);
+#pragma unroll
+      for (int e = EPM * i; e < EPM * (i + 1); ++e) {
+        const float pe = fast_exp2(fmaf(cur[e >> 4][e & 15], c2, -off));
+        cur[e >> 4][e & 15] = pe;
+        if (e & 1) ls1 += pe; else ls0 += pe;
+        if ((e & 7) == 7) {  // a 16-key chunk's probabilities are complete: pack them
+          const int cc = e >> 3, r0 = 8 * (cc & 1);
+          const f32x16& sb = cur[cc >> 1];
+          pf[cc] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
+                         TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
+          if (cc & 1) lw1 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw1))));
+          else lw0 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw0))));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += ls0 + ls1;
+    lw_run += lw0 + lw1;
+    // ---- step B: O += P_j V_j (MFMA) with tile j+1's row max (VALU)
+    auto vaddr = [&](int i) {
+      const int cc = i / (D / 32), bb = i % (D / 32);
+      return vt + v_lane + (cc * CG + bb) * 1024;
+    };
+    u32x4 vop[3];
+    auto vload = [&](int i) {
+      const uint8_t* va = vaddr(i);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    };
+    vop[0] = vload(0);
+    vop[1] = vload(1);
+    __builtin_amdgcn_sched_barrier(0);
+    float mt0 = -INFINITY, mt1 = -INFINITY;
+    constexpr int MPM = (ELEM / 2 + NPV - 3) / (NPV - 2);  // score pairs per MFMA from the third on
+    int e = 0;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      if (i + 2 < NPV) vop[(i + 2) % 3] = vload(i + 2);
+      const int cc = i / (D / 32), bb = i % (D / 32);
+      o[bb] = TT::mma(vop[i % 3], pf[cc], o[bb]);
+      if (i >= 2) {
+#pragma unroll
+        for (int k = 0; k < MPM; ++k) {
+          if (e < ELEM / 2) {  // two scores of tile j+1 per max3
+            const int e0 = 2 * e, e1 = 2 * e + 1;
+            if (e & 1) mt1 = fmaxf(mt1, fmaxf(nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]));
+            else mt0 = fmaxf(mt0, fmaxf(nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]));
+            ++e;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // tile j+1's statistics (no mask on this path)
+    const float mt = half_max(fmaxf(mt0, mt1));
+    m_run = fmaxf(m_run, mt);
+    const float mc_cand = m_run * c2;
+    const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
+    if (resc) {
+      const float alpha = fast_exp2(mc_run - mc_cand);
+      mc_run = mc_cand;
+      l_run *= alpha;
+      lw_run *= alpha;
+#pragma unroll
+      for (int bb = 0; bb < D / 32; ++bb) o[bb] *= alpha;
+    }
+    (void)t_next;
+  };
+
+  // Tiles j + 1 <= J_steady are unmasked for every wave of the workgroup, so
+  // iterations 0 .. J_steady-1 run the steady step; the rest run the general
+  // path.  (Causal: the lowest row of the workgroup bounds the unmasked keys.)
+  int J_steady = CAUSAL ? (qt * BR) / BC : N / BC;  // tiles wholly unmasked for all rows
+  J_steady = max(0, min(J_steady, T) - 1);
+
+  // prologue: stage -1 (K_0) and stage 0 (K_1, V_0); S_0 and its statistics
+  f32x16 sA[BC / 32], sB[BC / 32];
+  load_stage(-1);
+  load_stage(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (0 < my_T) {
+    bool resc;
+    qk(smem + 1 * 2 * TB, sA);
+    part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
+  }
+  __syncthreads();  // every wave is done with buffer 1 before it is refilled
+
+  int j = 0;
+  // steady loop, two tiles per trip so the score registers swap roles
+  for (; j + 1 < J_steady; j += 2) {
+    load_stage(j + 1);
+    steady(sA, sB, smem + (j & 1) * 2 * TB, smem + (j & 1) * 2 * TB + TB, j + 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    load_stage(j + 2);
+    steady(sB, sA, smem + ((j + 1) & 1) * 2 * TB, smem + ((j + 1) & 1) * 2 * TB + TB, j + 2);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+  // remaining tiles: general path (masks, each wave's last tile)
+  for (; j < T; ++j) {
+    if (j + 1 < T) load_stage(j + 1);  // (K_{j+2}, V_{j+1}) into buffer (j+1) & 1
+    const uint8_t* kt = smem + (j & 1) * 2 * TB;  // K_{j+1}
+    const uint8_t* vt = kt + TB;                  // V_j
+    if (j < my_T) {
+      part2(sA);
+      pv(vt);
+      if (j + 1 < my_T) {
+        bool resc;
+        qk(kt, sB);
+        const float alpha = part1(sB, j + 1, tile_masked(j + 1), resc);
+        if (resc) {
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+        }
+#pragma unroll
+        for (int b = 0; b < BC / 32; ++b) sA[b] = sB[b];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // stage j+1 has landed
+    __syncthreads();
+  }
+
+  const float l_tot = half_sum(l_run);
+  const float lw_tot = half_sum(lw_run);
+  if (my_q < N) {
+    const float inv = __builtin_amdgcn_rcpf(lw_tot);
+    uint16_t* orow = O + head + (size_t)my_q * D + 4 * hf;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {TT::pack(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv),
+                         TT::pack(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
+        *(u32x2*)(orow + 32 * b + 8 * g) = w;
+      }
+    if (hf == 0) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel
 //
 // A workgroup owns 32 query rows and DS waves; wave w owns head-dim columns
@@ -351,7 +736,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   constexpr int D = DSL * DS, NB = DSL / 32, BC = 32;
   __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const int work = xcd_remap(blockIdx.x, total_wg);
   const int bh = work / n_qtiles;
@@ -478,6 +863,21 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 // ---------------------------------------------------------------------------
 // host side
 template <class TT, int D>
+hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                     int N, float scale, bool causal, hipStream_t st) {
+  const int nq = (N + 127) / 128;
+  const int total = nq * BH;
+  const dim3 grid(total), block(256);
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_sp<TT, D, true>), grid, block, 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total, scale);
+  else
+    hipLaunchKernelGGL((attn_fwd_sp<TT, D, false>), grid, block, 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total, scale);
+  return hipGetLastError();
+}
+
+template <class TT, int D>
 hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                     int N, float scale, bool causal, hipStream_t st) {
   const int nq = (N + 127) / 128;
@@ -545,12 +945,21 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   const bool c = causal != 0;
   const int bh = (int)BH;
   hipError_t e = hipSuccess;
+  static const bool four_wave = getenv("FA_KERNEL") && getenv("FA_KERNEL")[0] == '4';
   if (dtype == FA_DTYPE_BF16) {
-    e = d == 64 ? launch16<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                : launch16<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    if (four_wave)
+      e = d == 64 ? launch16<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                  : launch16<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    else
+      e = d == 64 ? launch_sp<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                  : launch_sp<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
   } else if (dtype == FA_DTYPE_FP16) {
-    e = d == 64 ? launch16<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                : launch16<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    if (four_wave)
+      e = d == 64 ? launch16<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                  : launch16<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    else
+      e = d == 64 ? launch_sp<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                  : launch_sp<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
   } else {
     switch (d) {
       case 64: e = launch32<64, 1>(q, k, v, o, lse, bh, N, scale, c, st); break;
