@@ -58,6 +58,8 @@ constexpr float kLazyRescale = 8.0f;
 constexpr int kBufferFlags = 0x00020000;
 // s_waitcnt operand that waits for vmcnt = 0 only (expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmcnt0 = 0x0F70;
+// ... and for vmcnt <= n (n < 64: low 4 bits in 3:0, high 2 bits in 15:14)
+constexpr int wait_vmcnt(int n) { return kWaitVmcnt0 | (n & 15) | ((n >> 4) << 14); }
 
 // ---------------------------------------------------------------------------
 // element-type traits for the 16-bit kernels
@@ -414,15 +416,18 @@ __device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0
 // Tiles that need a mask (diagonal, sequence tail) and each wave's last tile
 // take a general path without the interleaving constraints.
 // Operand layouts are those of attn_fwd_mfma16.
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_sp(
+template <class TT, int D, bool CAUSAL, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int N, int n_qtiles, int total_wg, float scale) {
-  constexpr int NW = 4, BR = 32 * NW, BC = 64;
+  constexpr int BR = 32 * NW, BC = 64;
   using LY = TileLayout<D>;
   constexpr int TB = LY::BYTES, CG = LY::CG;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TB];  // [buffer][K, V]
+  // DMA instructions one wave issues for one full stage (K and V tiles)
+  constexpr int NDMA = 2 * LY::BLOCKS / NW;
+  static_assert(2 * LY::BLOCKS % NW == 0 && NS >= 2, "stages split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * 2 * TB];  // [stage buffer][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
@@ -449,13 +454,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const u32x4 kdesc = buffer_desc(K + head, (unsigned)N * D * 2);
   const u32x4 vdesc = buffer_desc(V + head, (unsigned)N * D * 2);
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer st & 1
+  // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer (st+1) % NS
+  auto stage_buf = [&](int st) { return (st + 1) % NS; };
   auto load_stage = [&](int st) {
-    const unsigned base = lds0 + (st & 1) * 2 * TB;
+    const unsigned base = lds0 + stage_buf(st) * 2 * TB;
     if (st + 1 < T) dma_tile<D, false>(kdesc, base, (st + 1) * BC, wave, NW, lane);
     if (st >= 0) dma_tile<D, true>(vdesc, base + TB, st * BC, wave, NW, lane);
   };
-
   const int k_lane = (lq >> 4) * CG * 1024 + (hf * 16 + (lq & 15)) * 16;
   const int tr_i = lane & 15, tr_grp = lane >> 4;
   const int v_lane = (4 * (tr_grp >> 1) + (tr_i >> 2)) * 64 + (2 * (tr_grp & 1) + ((tr_i & 3) >> 1)) * 16 +
@@ -649,36 +654,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int J_steady = CAUSAL ? (qt * BR) / BC : N / BC;  // tiles wholly unmasked for all rows
   J_steady = max(0, min(J_steady, T) - 1);
 
-  // prologue: stage -1 (K_0) and stage 0 (K_1, V_0); S_0 and its statistics
+  // Stages are issued AHEAD = NS-1 iterations early: iteration j issues stage
+  // j + AHEAD into the buffer of stage j - 1, which iteration j - 1 finished
+  // reading before its closing barrier.  Before that barrier, iteration j
+  // waits until stage j + 1 (read next) has landed while stages j + 2 ..
+  // j + AHEAD stay in flight.  vmcnt retires in issue order, so "at most n
+  // outstanding" (n = this wave's loads of those younger stages) means every
+  // older load is done.
+  constexpr int AHEAD = NS - 1;
+  static_assert((NS & (NS - 1)) == 0 && NS <= 4, "power-of-two stage count, at most 4");
+  auto issue_for = [&](int j) { if (j + AHEAD < T) load_stage(j + AHEAD); };
+  // loads one wave issues for stage st: K tile (if st+1 < T) and V tile (if st >= 0)
+  auto stage_loads = [&](int st) {
+    return st >= T ? 0 : (st + 1 < T ? NDMA / 2 : 0) + (st >= 0 ? NDMA / 2 : 0);
+  };
+  // s_waitcnt takes an immediate, so each reachable count (a multiple of half
+  // a stage, at most NS-2 full stages) gets its own instruction
+  auto wait_keep = [&](int keep) {
+    constexpr int H = NDMA / 2;
+    static_assert((NS - 2) * NDMA <= 63, "vmcnt is a 6-bit count");
+    if constexpr (NS >= 4) {
+      if (keep >= 4 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * H)); return; }
+      if (keep == 3 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * H)); return; }
+    }
+    if constexpr (NS >= 3) {
+      if (keep >= 2 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * H)); return; }
+      if (keep == H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(H)); return; }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  };
+  auto end_iter = [&](int j) {
+    int keep = 0;
+#pragma unroll
+    for (int st = 2; st <= AHEAD; ++st) keep += stage_loads(j + st);
+    wait_keep(keep);
+    __syncthreads();
+  };
+
+  // prologue: stages -1 (K_0), 0 (K_1, V_0), ..., NS-2; S_0 and its statistics
   f32x16 sA[BC / 32], sB[BC / 32];
   load_stage(-1);
-  load_stage(0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+  for (int st = 0; st <= NS - 2; ++st)
+    if (st < T) load_stage(st);
+  // stages -1 and 0 must be in; stages 1 .. NS-2 may stay in flight
+  {
+    int keep = 0;
+#pragma unroll
+    for (int st = 1; st <= NS - 2; ++st) keep += stage_loads(st);
+    wait_keep(keep);
+  }
   __syncthreads();
   if (0 < my_T) {
     bool resc;
-    qk(smem + 1 * 2 * TB, sA);
+    qk(smem + stage_buf(-1) * 2 * TB, sA);
     part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
   }
-  __syncthreads();  // every wave is done with buffer 1 before it is refilled
+  __syncthreads();  // every wave is done with stage -1's buffer before it is refilled
 
   int j = 0;
   // steady loop, two tiles per trip so the score registers swap roles
   for (; j + 1 < J_steady; j += 2) {
-    load_stage(j + 1);
-    steady(sA, sB, smem + (j & 1) * 2 * TB, smem + (j & 1) * 2 * TB + TB, j + 1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    load_stage(j + 2);
-    steady(sB, sA, smem + ((j + 1) & 1) * 2 * TB, smem + ((j + 1) & 1) * 2 * TB + TB, j + 2);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+    issue_for(j);
+    {
+      const uint8_t* kt = smem + stage_buf(j) * 2 * TB;
+      steady(sA, sB, kt, kt + TB, j + 1);
+    }
+    end_iter(j);
+    issue_for(j + 1);
+    {
+      const uint8_t* kt = smem + stage_buf(j + 1) * 2 * TB;
+      steady(sB, sA, kt, kt + TB, j + 2);
+    }
+    end_iter(j + 1);
   }
   // remaining tiles: general path (masks, each wave's last tile)
   for (; j < T; ++j) {
-    if (j + 1 < T) load_stage(j + 1);  // (K_{j+2}, V_{j+1}) into buffer (j+1) & 1
-    const uint8_t* kt = smem + (j & 1) * 2 * TB;  // K_{j+1}
-    const uint8_t* vt = kt + TB;                  // V_j
+    issue_for(j);
+    const uint8_t* kt = smem + stage_buf(j) * 2 * TB;  // K_{j+1}
+    const uint8_t* vt = kt + TB;                        // V_j
     if (j < my_T) {
       part2(sA);
       pv(vt);
@@ -694,8 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int b = 0; b < BC / 32; ++b) sA[b] = sB[b];
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // stage j+1 has landed
-    __syncthreads();
+    end_iter(j);
   }
 
   const float l_tot = half_sum(l_run);
@@ -865,14 +918,15 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 template <class TT, int D>
 hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                      int N, float scale, bool causal, hipStream_t st) {
-  const int nq = (N + 127) / 128;
+  constexpr int NW = 4, NS = 2;
+  const int nq = (N + 32 * NW - 1) / (32 * NW);
   const int total = nq * BH;
-  const dim3 grid(total), block(256);
+  const dim3 grid(total), block(64 * NW);
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_sp<TT, D, true>), grid, block, 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, D, true, NW, NS>), grid, block, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total, scale);
   else
-    hipLaunchKernelGGL((attn_fwd_sp<TT, D, false>), grid, block, 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, D, false, NW, NS>), grid, block, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total, scale);
   return hipGetLastError();
 }
