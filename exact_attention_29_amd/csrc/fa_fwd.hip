@@ -107,6 +107,15 @@ __device__ __forceinline__ float half_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b, c) in one v_max3_f32.  fmaxf would first canonicalise each input
+// (one extra instruction per score); the scores fed here are finite MFMA
+// results, for which canonicalising changes nothing.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Map the hardware workgroup id to a work item.  Workgroups are handed to the
 // 8 XCDs round-robin (id % 8); giving XCD x the contiguous range
 // [x*W/8, (x+1)*W/8) of work items keeps the query tiles of one head -- which
@@ -451,16 +460,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int T = (kv_end + BC - 1) / BC;
   const int my_T = CAUSAL ? min(T, (q_first + 31) / BC + 1) : T;
 
-  const u32x4 kdesc = buffer_desc(K + head, (unsigned)N * D * 2);
-  const u32x4 vdesc = buffer_desc(V + head, (unsigned)N * D * 2);
+  const uint16_t* const kbase = K + head;
+  const uint16_t* const vbase = V + head;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer (st+1) % NS
-  auto stage_buf = [&](int st) { return (st + 1) % NS; };
+  // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer (st+1) % NS.
+  // Each tile gets a descriptor starting at its first key row (scalar
+  // arithmetic), so the per-lane offsets are the same for every tile; the
+  // record count ends at row N, so rows past N read as zero.
   auto load_stage = [&](int st) {
-    const unsigned base = lds0 + stage_buf(st) * 2 * TB;
-    if (st + 1 < T) dma_tile<D, false>(kdesc, base, (st + 1) * BC, wave, NW, lane);
-    if (st >= 0) dma_tile<D, true>(vdesc, base + TB, st * BC, wave, NW, lane);
+    const unsigned base = lds0 + ((st + 1) % NS) * 2 * TB;
+    if (st + 1 < T) {
+      const int k0 = (st + 1) * BC;
+      dma_tile<D, false>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base, 0, wave, NW, lane);
+    }
+    if (st >= 0) {
+      const int k0 = st * BC;
+      dma_tile<D, true>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base + TB, 0, wave, NW, lane);
+    }
   };
+  auto stage_buf = [&](int st) { return (st + 1) % NS; };
   const int k_lane = (lq >> 4) * CG * 1024 + (hf * 16 + (lq & 15)) * 16;
   const int tr_i = lane & 15, tr_grp = lane >> 4;
   const int v_lane = (4 * (tr_grp >> 1) + (tr_i >> 2)) * 64 + (2 * (tr_grp & 1) + ((tr_i & 3) >> 1)) * 16 +
@@ -600,7 +618,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int cc = i / (D / 32), bb = i % (D / 32);
       return vt + v_lane + (cc * CG + bb) * 1024;
     };
-    u32x4 vop[3];
+    constexpr int VP = 4;  // V operands in flight ahead of the matrix core
+    u32x4 vop[VP + 1];
     auto vload = [&](int i) {
       const uint8_t* va = vaddr(i);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
@@ -608,24 +627,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
       return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
     };
-    vop[0] = vload(0);
-    vop[1] = vload(1);
+#pragma unroll
+    for (int i = 0; i < VP && i < NPV; ++i) vop[i] = vload(i);
     __builtin_amdgcn_sched_barrier(0);
     float mt0 = -INFINITY, mt1 = -INFINITY;
     constexpr int MPM = (ELEM / 2 + NPV - 3) / (NPV - 2);  // score pairs per MFMA from the third on
     int e = 0;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      if (i + 2 < NPV) vop[(i + 2) % 3] = vload(i + 2);
+      if (i + VP < NPV) vop[(i + VP) % (VP + 1)] = vload(i + VP);
       const int cc = i / (D / 32), bb = i % (D / 32);
-      o[bb] = TT::mma(vop[i % 3], pf[cc], o[bb]);
+      o[bb] = TT::mma(vop[i % (VP + 1)], pf[cc], o[bb]);
       if (i >= 2) {
 #pragma unroll
         for (int k = 0; k < MPM; ++k) {
           if (e < ELEM / 2) {  // two scores of tile j+1 per max3
             const int e0 = 2 * e, e1 = 2 * e + 1;
-            if (e & 1) mt1 = fmaxf(mt1, fmaxf(nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]));
-            else mt0 = fmaxf(mt0, fmaxf(nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]));
+            if (e & 1) mt1 = max3(mt1, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
+            else mt0 = max3(mt0, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
             ++e;
           }
         }
@@ -633,7 +652,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_barrier(0);
     }
     // tile j+1's statistics (no mask on this path)
-    const float mt = half_max(fmaxf(mt0, mt1));
+    const float mt = half_max(max3(mt0, mt1, mt1));
     m_run = fmaxf(m_run, mt);
     const float mc_cand = m_run * c2;
     const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
