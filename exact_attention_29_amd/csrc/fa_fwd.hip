@@ -585,16 +585,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int bb = i / (D / 16), c = i % (D / 16);
       return (const u32x4*)(kt + k_lane + (2 * bb * CG + (c >> 1)) * 1024 + (c & 1) * 512);
     };
-    u32x4 kop[3];
-    kop[0] = *kaddr(0);
-    kop[1] = *kaddr(1);
+    constexpr int KP = 4;  // K operands in flight ahead of the matrix core
+    u32x4 kop[KP + 1];
+#pragma unroll
+    for (int i = 0; i < KP && i < NQK; ++i) kop[i] = *kaddr(i);
     __builtin_amdgcn_sched_barrier(0);
     constexpr int EPM = ELEM / NQK;  // elements of tile j per MFMA (2 at d = 128, 4 at d = 64)
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      if (i + 2 < NQK) kop[(i + 2) % 3] = *kaddr(i + 2);
+      if (i + KP < NQK) kop[(i + KP) % (KP + 1)] = *kaddr(i + KP);
       const int bb = i / (D / 16), c = i % (D / 16);
-      nxt[bb] = TT::mma(kop[i % 3], qf[c], c == 0 ? f32x16{} : nxt[bb]);
+      nxt[bb] = TT::mma(kop[i % (KP + 1)], qf[c], c == 0 ? f32x16{} : nxt[bb]);
 #pragma unroll
       for (int e = EPM * i; e < EPM * (i + 1); ++e) {
         const float pe = fast_exp2(fmaf(cur[e >> 4][e & 15], c2, -off));
@@ -629,6 +630,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
 #pragma unroll
     for (int i = 0; i < VP && i < NPV; ++i) vop[i] = vload(i);
+    // Raised wave priority while this wave feeds the matrix core: when the
+    // other wave on the SIMD is in its exponential-heavy step, the arbiter
+    // issues this wave's MFMAs first instead of letting them queue behind
+    // vector instructions.
+    __builtin_amdgcn_s_setprio(2);
     __builtin_amdgcn_sched_barrier(0);
     float mt0 = -INFINITY, mt1 = -INFINITY;
     constexpr int MPM = (ELEM / 2 + NPV - 3) / (NPV - 2);  // score pairs per MFMA from the third on
@@ -651,6 +657,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // tile j+1's statistics (no mask on this path)
     const float mt = half_max(max3(mt0, mt1, mt1));
     m_run = fmaxf(m_run, mt);
