@@ -50,7 +50,7 @@ def kernel_source_hash() -> str:
 
 def kernel_tag(w) -> str:
     """Name of the kernel instance a workload runs, as used by profiles/."""
-    kern = "attn_fwd_f32" if w.dtype == "fp32" else "attn_fwd_mfma16"
+    kern = "attn_fwd_f32" if w.dtype == "fp32" else "attn_fwd_sp"
     mask = "causal" if w.causal else "noncausal"
     return f"{kern}_{w.dtype}_{mask}_B{w.B}_H{w.H}_N{w.N}_d{w.d}"
 

@@ -11,15 +11,17 @@
 // Example", step 7).  The N x N score matrix never leaves registers.
 //
 // Two kernels:
-//  * attn_fwd_mfma16<T>: bf16 / fp16 inputs, head dim 64 or 128.  4 waves x 32
-//    query rows; K and V tiles of 64 keys double-buffered in LDS; both products
-//    on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulators.  The score tile
-//    is computed transposed (S^T = K Q^T) so that each lane owns one query
+//  * attn_fwd_sp<T>: bf16 / fp16 inputs, head dim 64 or 128.  4 waves x 32
+//    query rows per work item; K and V tiles of 64 keys double-buffered in LDS
+//    and filled by buffer loads that write straight to LDS; both products on
+//    v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulators.  The score tile is
+//    computed transposed (S^T = K Q^T) so that each lane owns one query
 //    column: the row max and row sum are in-lane plus one swap between the two
 //    32-lane halves, and the probabilities are already in the B-operand layout
 //    of the P V product (O^T = V^T P^T).  V is read out of its row-major LDS
-//    tile with ds_read_b64_tr_b16, which hands each lane four keys of one
-//    head-dim column.
+//    blocks with ds_read_b64_tr_b16, which hands each lane four keys of one
+//    head-dim column.  Each wave software-pipelines the score product of the
+//    next tile against the softmax of the current one.
 //  * attn_fwd_f32: fp32 inputs, head dim 64..1024, on v_mfma_f32_32x32x2_f32.
 //    Head dims above 128 are split across the waves of a workgroup (128
 //    columns each); the partial scores are summed through LDS in a fixed wave
@@ -127,225 +129,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 / fp16 kernel
-//
-// Layouts (D = head dim, BC = 64 keys per tile, 4 waves x 32 queries):
-//   Q fragment (registers, whole kernel): lane (q = lane%32, h = lane/32) holds
-//     Q[q][16c + 8h .. 16c + 8h + 7] for c = 0..D/16-1 (the MFMA B operand).
-//   K tile (LDS, row-major [BC][KSTR]): A operand of S^T = K Q^T, lane
-//     (key = lane%32, h) reads K[key][16c + 8h .. +7].
-//   S^T block (accumulator): lane (q, h), register r holds key
-//     8*(r/4) + 4h + r%4 of the 32-key block, for query q.
-//   P^T B operand of O^T += V^T P^T, 16-key chunk c: registers 8(c%2)..+7 of
-//     block c/2, i.e. lane (q, h) element t is key 16c + 8(t/4) + 4h + t%4.
-//   V tile (LDS, row-major [BC][VSTR]): two ds_read_b64_tr_b16 per A operand
-//     give lane (d = lane%32, h) the same eight keys for its column d.
-//   O^T (accumulator): block b, register r of lane (q, h) holds
-//     O[q][32b + 8*(r/4) + 4h + r%4].
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_mfma16(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int N, int n_qtiles, int total_wg, float scale) {
-  constexpr int NW = 4, NT = NW * 64, BR = NW * 32, BC = 64;
-  constexpr int KSTR = D + 8;            // K row: 16-byte reads spread over banks
-  constexpr int VSTR = D + 32;           // V row stride = 64 mod 256 bytes for tr reads
-  constexpr int KT = BC * KSTR, VT = BC * VSTR, BUF = KT + VT;
-  constexpr int CH = BC * D / 8;         // 16-byte chunks per K (or V) tile
-  constexpr int CPT = CH / NT;           // chunks per thread
-  static_assert(CH % NT == 0, "tile must split evenly over the workgroup");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lq = lane & 31, hf = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, total_wg);
-  const int bh = work / n_qtiles;
-  int qt = work % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
-  const size_t head = (size_t)bh * N * D;
-  const int q_first = qt * BR + wave * 32;
-  const int my_q = q_first + lq;
-
-  // Q fragment
-  u32x4 qf[D / 16];
-  {
-    const uint16_t* qrow = Q + head + (size_t)my_q * D + 8 * hf;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      qf[c] = (my_q < N) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
-  }
-
-  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;  // keys [0, kv_end)
-  const int ntiles = (kv_end + BC - 1) / BC;
-
-  // global -> registers for one K and V tile.  Raw buffer loads over this
-  // head's N*D elements: a 16-byte chunk of a row past N lies wholly outside
-  // the descriptor's range and reads as zero, so the tail needs no branch.
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, N * D * 2, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head), (short)0, N * D * 2, kBufferFlags);
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int off = ((j * BC + row) * D + col) * 2;
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* kt = smem + buf * BUF;
-    uint16_t* vt = kt + KT;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4*)(kt + row * KSTR + col) = kreg[i];
-      *(u32x4*)(vt + row * VSTR + col) = vreg[i];
-    }
-  };
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
-  // Running state per query (both lane halves agree on m_run and mc_run):
-  //   m_run  -- max of the raw scores q.k seen so far;
-  //   mc_run -- the exponent reference every exp2 so far was taken against,
-  //             so l and O hold sums of 2^(s*c2 - mc_run);
-  //   l_run  -- this half's share of that sum (fp32 terms; gives the lse);
-  //   lw_run -- the same sum over the terms as rounded to the input type,
-  //             i.e. the weights the P V product really used.  O is divided
-  //             by it, so O is an exact convex combination of V rows with
-  //             those weights: a dominant key's rounding cancels instead of
-  //             scaling the output.
-  // The reference is moved only when some row of the wave has outgrown it by
-  // more than kLazyRescale (so every p stays <= 2^kLazyRescale, far inside
-  // fp32 and bf16 range); then each row moves to fl(m_run * c2) and the state
-  // is rescaled from one stored reference to the next, alpha =
-  // exp2(mc_old - mc_new).  Any reference gives the same softmax, and the
-  // log-sum-exp is taken against the one in use.  Rescaling by a factor
-  // recomputed from m (m*c2 - fl(m*c2)) would instead multiply the state by a
-  // rounding residual on every tile and drift over long rows.
-  float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
-  const float c2 = scale * kLog2e;
-
-  // lane constants of the transposed V read (see layout notes above)
-  const int tr_i = lane & 15, tr_grp = lane >> 4;
-  const int tr_h = tr_grp >> 1, tr_dsub = tr_grp & 1;
-  const int tr_row = 4 * tr_h + (tr_i >> 2);            // + 16c (+ 8 for the upper four)
-  const int tr_col = 16 * tr_dsub + 4 * (tr_i & 3);     // + 32b
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);  // in flight during this tile's math
-    const int k0 = j * BC;
-    const bool skip = CAUSAL && (k0 > q_first + 31);  // every key above this wave's rows
-    if (!skip) {
-      const uint16_t* kt = smem + buf * BUF;
-      const uint16_t* vt = kt + KT;
-      // S^T = K Q^T
-      f32x16 s[BC / 32];
-#pragma unroll
-      for (int b = 0; b < BC / 32; ++b) {
-        s[b] = f32x16{};
-        const uint16_t* kr = kt + (32 * b + lq) * KSTR + 8 * hf;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) s[b] = TT::mma(*(const u32x4*)(kr + 16 * c), qf[c], s[b]);
-      }
-      // mask keys past the diagonal (causal) or past the sequence
-      const bool need_mask = (CAUSAL && k0 + BC - 1 > q_first) || (k0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool keep = key < N && (!CAUSAL || key <= my_q);
-            if (!keep) s[b][r] = -INFINITY;
-          }
-      }
-      // online softmax update
-      float mt = s[0][0];
-#pragma unroll
-      for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[b][r]);
-      mt = half_max(mt);
-      m_run = fmaxf(m_run, mt);
-      // A row with every key so far masked keeps m = -inf and reference -inf.
-      const float mc_cand = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
-      if (__builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0) {
-        // 0 for a row's first finite tile; a row still fully masked has a zero
-        // state and keeps it (alpha = 1 avoids exp2(-inf - (-inf)))
-        const float alpha = (mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
-        mc_run = mc_cand;
-        l_run *= alpha;
-        lw_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
-      }
-      // offset 0 for a still fully masked row: exp2(-inf - 0) = 0, never -inf - (-inf)
-      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
-      float lsum = 0.f;
-#pragma unroll
-      for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[b][r], c2, -off));
-          s[b][r] = p;
-          lsum += p;
-        }
-      l_run += lsum;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int c = 0; c < BC / 16; ++c) {
-        const int r0 = 8 * (c & 1);
-        const f32x16& sb = s[c >> 1];
-        const u32x4 pf = {TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
-                          TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
-        lw_run = TT::sum2(pf[3], TT::sum2(pf[2], TT::sum2(pf[1], TT::sum2(pf[0], lw_run))));
-        const uint16_t* vrow = vt + (16 * c + tr_row) * VSTR + tr_col;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vrow + 32 * b));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vrow + 8 * VSTR + 32 * b));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 va = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          o[b] = TT::mma(va, pf, o[b]);
-        }
-      }
-    }
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: O = O^T / (sum of the rounded weights), lse = ln2 * (mc + log2 l)
-  const float l_tot = half_sum(l_run);
-  const float lw_tot = half_sum(lw_run);
-  if (my_q < N) {
-    const float inv = __builtin_amdgcn_rcpf(lw_tot);
-    uint16_t* orow = O + head + (size_t)my_q * D + 4 * hf;
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {TT::pack(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv),
-                         TT::pack(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
-        *(u32x2*)(orow + 32 * b + 8 * g) = w;
-      }
-    if (hf == 0) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// LDS tile layout shared by the ping-pong kernel
+// LDS tile layout of the bf16 / fp16 kernel
 //
 // A K or V tile is 64 keys x D elements (2D bytes per key row), stored as
 // 1 KB blocks of 16 rows x 4 sixteen-byte chunks: block (rg, cg) holds rows
@@ -424,7 +208,20 @@ __device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0
 // loaded by all waves during iteration j-1; one barrier per iteration.
 // Tiles that need a mask (diagonal, sequence tail) and each wave's last tile
 // take a general path without the interleaving constraints.
-// Operand layouts are those of attn_fwd_mfma16.
+//
+// Register layouts (D = head dim, BC = 64 keys per tile, 32 queries per wave):
+//   Q fragment (registers, whole kernel): lane (q = lane%32, h = lane/32) holds
+//     Q[q][16c + 8h .. 16c + 8h + 7] for c = 0..D/16-1 (the MFMA B operand).
+//   K tile (LDS blocks, chunk-major): A operand of S^T = K Q^T, lane
+//     (key = lane%32, h) reads K[key][16c + 8h .. +7].
+//   S^T block (accumulator): lane (q, h), register r holds key
+//     8*(r/4) + 4h + r%4 of the 32-key block, for query q.
+//   P^T B operand of O^T += V^T P^T, 16-key chunk c: registers 8(c%2)..+7 of
+//     block c/2, i.e. lane (q, h) element t is key 16c + 8(t/4) + 4h + t%4.
+//   V tile (LDS blocks, row-major): two ds_read_b64_tr_b16 per A operand
+//     give lane (d = lane%32, h) the same eight keys for its column d.
+//   O^T (accumulator): block b, register r of lane (q, h) holds
+//     O[q][32b + 8*(r/4) + 4h + r%4].
 template <class TT, int D, bool CAUSAL, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -487,7 +284,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   f32x16 o[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
-  // running state, as in attn_fwd_mfma16
+  // running state: row max m, its scaled reference mc (exponents are taken
+  // against mc), fp32 sum l and the sum lw of the bf16-rounded weights
   float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
   const float c2 = scale * kLog2e;
   u32x4 pf[BC / 16];  // P_j packed, B operand of the P V product
@@ -957,23 +755,6 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   return hipGetLastError();
 }
 
-template <class TT, int D>
-hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                    int N, float scale, bool causal, hipStream_t st) {
-  const int nq = (N + 127) / 128;
-  const int total = nq * BH;
-  const dim3 grid(total), block(256);
-  if (causal)
-    hipLaunchKernelGGL((attn_fwd_mfma16<TT, D, true>), grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total,
-                       scale);
-  else
-    hipLaunchKernelGGL((attn_fwd_mfma16<TT, D, false>), grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total,
-                       scale);
-  return hipGetLastError();
-}
-
 template <int DSL, int DS>
 hipError_t launch32(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                     int N, float scale, bool causal, hipStream_t st) {
@@ -1025,21 +806,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   const bool c = causal != 0;
   const int bh = (int)BH;
   hipError_t e = hipSuccess;
-  static const bool four_wave = getenv("FA_KERNEL") && getenv("FA_KERNEL")[0] == '4';
   if (dtype == FA_DTYPE_BF16) {
-    if (four_wave)
-      e = d == 64 ? launch16<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                  : launch16<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
-    else
-      e = d == 64 ? launch_sp<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                  : launch_sp<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    e = d == 64 ? launch_sp<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                : launch_sp<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
   } else if (dtype == FA_DTYPE_FP16) {
-    if (four_wave)
-      e = d == 64 ? launch16<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                  : launch16<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
-    else
-      e = d == 64 ? launch_sp<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                  : launch_sp<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    e = d == 64 ? launch_sp<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
+                : launch_sp<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
   } else {
     switch (d) {
       case 64: e = launch32<64, 1>(q, k, v, o, lse, bh, N, scale, c, st); break;
