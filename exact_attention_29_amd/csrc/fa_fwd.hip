@@ -180,14 +180,16 @@ __device__ __forceinline__ void dma16(u32x4 desc, unsigned lds_addr, int voffset
                : "memory", "m0");
 }
 
-// This wave's share of one K (or V) tile: blocks first_blk, first_blk +
-// stride, ... of the tile whose first key row is key0.
-template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0, int first_blk,
-                                         int stride, int lane) {
+// This wave's share of one K (or V) tile: blocks wave, wave + NW, ... (the
+// same count for every wave) of the tile whose first key row is key0.
+template <int D, bool IS_V, int NW>
+__device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0, int wave,
+                                         int lane) {
   using L = TileLayout<D>;
+  static_assert(L::BLOCKS % NW == 0, "tile blocks split evenly over the waves");
 #pragma unroll
-  for (int blk = first_blk; blk < L::BLOCKS; blk += stride) {
+  for (int i = 0; i < L::BLOCKS / NW; ++i) {
+    const int blk = wave + i * NW;
     const int el = key0 * D + (IS_V ? L::v_src(blk, lane) : L::k_src(blk, lane));
     dma16(desc, lds_tile + blk * 1024, el * 2);
   }
@@ -268,11 +270,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const unsigned base = lds0 + ((st + 1) % NS) * 2 * TB;
     if (st + 1 < T) {
       const int k0 = (st + 1) * BC;
-      dma_tile<D, false>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base, 0, wave, NW, lane);
+      dma_tile<D, false, NW>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base, 0, wave, lane);
     }
     if (st >= 0) {
       const int k0 = st * BC;
-      dma_tile<D, true>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base + TB, 0, wave, NW, lane);
+      dma_tile<D, true, NW>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base + TB, 0, wave, lane);
     }
   };
   auto stage_buf = [&](int st) { return (st + 1) % NS; };
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // and statistics), written in issue order and fenced so that every MFMA is
   // followed by the independent vector work that hides it.
   auto steady = [&](f32x16 (&cur)[BC / 32], f32x16 (&nxt)[BC / 32], const uint8_t* kt,
-                    const uint8_t* vt, int t_next) {
+                    const uint8_t* vt, int t_next, bool mask_next) {
     constexpr int NQK = BC / 32 * D / 16, NPV = BC / 16 * D / 32;
     constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
     const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
@@ -428,6 +430,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
 #pragma unroll
     for (int i = 0; i < VP && i < NPV; ++i) vop[i] = vload(i);
+    if (mask_next) {
+      // keys past the row (causal) or past N score -inf: lane (q, h) keeps
+      // key offsets 32b + 8(r/4) + r%4 <= lim within tile t_next
+      const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - (t_next * BC + 4 * hf);
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * b + 8 * (r >> 2) + (r & 3) > lim) nxt[b][r] = -INFINITY;
+    }
     // Raised wave priority while this wave feeds the matrix core: when the
     // other wave on the SIMD is in its exponential-heavy step, the arbiter
     // issues this wave's MFMAs first instead of letting them queue behind
@@ -456,7 +468,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    // tile j+1's statistics (no mask on this path)
+    // tile j+1's statistics; a row whose keys in this tile are all masked
+    // keeps its max (tile 0 gave every row a finite one)
     const float mt = half_max(max3(mt0, mt1, mt1));
     m_run = fmaxf(m_run, mt);
     const float mc_cand = m_run * c2;
@@ -469,14 +482,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int bb = 0; bb < D / 32; ++bb) o[bb] *= alpha;
     }
-    (void)t_next;
   };
-
-  // Tiles j + 1 <= J_steady are unmasked for every wave of the workgroup, so
-  // iterations 0 .. J_steady-1 run the steady step; the rest run the general
-  // path.  (Causal: the lowest row of the workgroup bounds the unmasked keys.)
-  int J_steady = CAUSAL ? (qt * BR) / BC : N / BC;  // tiles wholly unmasked for all rows
-  J_steady = max(0, min(J_steady, T) - 1);
 
   // Stages are issued AHEAD = NS-1 iterations early: iteration j issues stage
   // j + AHEAD into the buffer of stage j - 1, which iteration j - 1 finished
@@ -536,23 +542,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   __syncthreads();  // every wave is done with stage -1's buffer before it is refilled
 
+  // Steady steps run in pairs while both tiles have a successor, masking the
+  // next tile's scores where it crosses the diagonal or the end of the
+  // sequence; the last one or two tiles take the general path.
   int j = 0;
-  // steady loop, two tiles per trip so the score registers swap roles
-  for (; j + 1 < J_steady; j += 2) {
+  // two tiles per trip so the score registers swap roles
+  for (; j + 2 < T; j += 2) {
     issue_for(j);
     {
       const uint8_t* kt = smem + stage_buf(j) * 2 * TB;
-      steady(sA, sB, kt, kt + TB, j + 1);
+      steady(sA, sB, kt, kt + TB, j + 1, tile_masked(j + 1));
     }
     end_iter(j);
     issue_for(j + 1);
     {
       const uint8_t* kt = smem + stage_buf(j + 1) * 2 * TB;
-      steady(sB, sA, kt, kt + TB, j + 2);
+      steady(sB, sA, kt, kt + TB, j + 2, tile_masked(j + 2));
     }
     end_iter(j + 1);
   }
-  // remaining tiles: general path (masks, each wave's last tile)
+  // remaining tiles: general path (a wave skips tiles past its last row)
   for (; j < T; ++j) {
     issue_for(j);
     const uint8_t* kt = smem + stage_buf(j) * 2 * TB;  // K_{j+1}
