@@ -11,17 +11,18 @@
 // Example", step 7).  The N x N score matrix never leaves registers.
 //
 // Two kernels:
-//  * attn_fwd_sp<T>: bf16 / fp16 inputs, head dim 64 or 128.  4 waves x 32
-//    query rows per work item; K and V tiles of 64 keys double-buffered in LDS
-//    and filled by buffer loads that write straight to LDS; both products on
-//    v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulators.  The score tile is
-//    computed transposed (S^T = K Q^T) so that each lane owns one query
-//    column: the row max and row sum are in-lane plus one swap between the two
-//    32-lane halves, and the probabilities are already in the B-operand layout
-//    of the P V product (O^T = V^T P^T).  V is read out of its row-major LDS
-//    blocks with ds_read_b64_tr_b16, which hands each lane four keys of one
-//    head-dim column.  Each wave software-pipelines the score product of the
-//    next tile against the softmax of the current one.
+//  * attn_fwd_sp<T>: bf16 / fp16 inputs, head dim 64 or 128.  4 (d = 64) or
+//    8 (d = 128) waves x 32 query rows per workgroup; K and V tiles of 64
+//    keys double-buffered in LDS and filled by buffer loads that write
+//    straight to LDS; both products on v_mfma_f32_32x32x16_{bf16,f16} with
+//    fp32 accumulators.  The score tile is computed transposed (S^T = K Q^T)
+//    so that each lane owns one query column: the row max and row sum are
+//    in-lane plus one swap between the two 32-lane halves, and the
+//    probabilities are already in the B-operand layout of the P V product
+//    (O^T = V^T P^T).  V is read out of its row-major LDS blocks with
+//    ds_read_b64_tr_b16, which hands each lane four keys of one head-dim
+//    column.  Each wave software-pipelines the score product of the next
+//    tile against the softmax of the current one.
 //  * attn_fwd_f32: fp32 inputs, head dim 64..1024, on v_mfma_f32_32x32x2_f32.
 //    Head dims above 128 are split across the waves of a workgroup (128
 //    columns each); the partial scores are summed through LDS in a fixed wave
@@ -751,7 +752,9 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 template <class TT, int D>
 hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                      int N, float scale, bool causal, hipStream_t st) {
-  constexpr int NW = 4, NS = 2;
+  // d = 128: 8 waves (256 query rows) per workgroup halve the K/V tile
+  // loads per FLOP; d = 64 keeps 4 waves so that two workgroups share a CU.
+  constexpr int NW = D == 128 ? 8 : 4, NS = 2;
   const int nq = (N + 32 * NW - 1) / (32 * NW);
   const int total = nq * BH;
   const dim3 grid(total), block(64 * NW);
