@@ -36,6 +36,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "fa.h"
 
 namespace {
@@ -127,6 +130,51 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   const int per = total / 8;
   if (wg >= per * 8) return wg;
   return (wg % 8) * per + wg / 8;
+}
+
+// Dynamic work distribution for the persistent bf16 / fp16 kernel.  The
+// items of a launch (a head and a block of query rows each) are split into 8
+// contiguous ranges, one per XCD, in the order xcd_remap gives: the query
+// blocks of one head go to one XCD's L2, longest first.  A workgroup takes
+// the next unclaimed item of its own XCD's range with an atomic counter, and
+// once that range is exhausted takes items from the other ranges, so no XCD
+// idles while another still has work.  Each launch uses one of kWorkSlots
+// counter sets (round-robin on the host), so launches that run concurrently
+// on different streams do not share counters; the last workgroup of a launch
+// clears its set for the launch that next uses it.  (More than kWorkSlots
+// launches in flight at once, or one captured launch replayed concurrently
+// with itself, would share a set.)
+constexpr int kWorkSlots = 64;
+__device__ unsigned g_next_rank[kWorkSlots][8];  // per XCD: next item rank to hand out
+__device__ unsigned g_done_wg[kWorkSlots];       // workgroups that have left the launch
+
+__device__ __forceinline__ int xcd_id() {
+  // hardware register XCC_ID (id 20), bits [3:0]
+  return (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7u);
+}
+
+__device__ __forceinline__ int take_item(int slot, int xcd, int total) {
+  for (int i = 0; i < 8; ++i) {
+    const int y = (xcd + i) & 7;
+    const unsigned lo = (unsigned)((long long)y * total / 8);
+    const unsigned n = (unsigned)((long long)(y + 1) * total / 8) - lo;
+    unsigned* ctr = &g_next_rank[slot][y];
+    if (n == 0 || __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+    const unsigned t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t < n) return (int)(lo + t);
+  }
+  return -1;
+}
+
+// Called once per workgroup by one thread, after its last claim.
+__device__ __forceinline__ void leave_launch(int slot) {
+  __threadfence();
+  const unsigned prev = __hip_atomic_fetch_add(&g_done_wg[slot], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev == gridDim.x - 1) {
+    for (int y = 0; y < 8; ++y)
+      __hip_atomic_store(&g_next_rank[slot][y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&g_done_wg[slot], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -225,11 +273,11 @@ __device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0
 //     give lane (d = lane%32, h) the same eight keys for its column d.
 //   O^T (accumulator): block b, register r of lane (q, h) holds
 //     O[q][32b + 8*(r/4) + 4h + r%4].
-template <class TT, int D, bool CAUSAL, int NW, int NS>
+template <class TT, int D, bool CAUSAL, int NW, int NS, bool PERSIST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int N, int n_qtiles, int total_wg, float scale) {
+    int N, int n_qtiles, int total_items, int slot, float scale) {
   constexpr int BR = 32 * NW, BC = 64;
   using LY = TileLayout<D>;
   constexpr int TB = LY::BYTES, CG = LY::CG;
@@ -240,366 +288,385 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, total_wg);
-  const int bh = work / n_qtiles;
-  int qt = work % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
-  const size_t head = (size_t)bh * N * D;
-  const int q_first = qt * BR + 32 * wave;
-  const int my_q = q_first + lq;
+  // Work loop.  Persistent: the workgroup claims items until none is left;
+  // thread 0 claims the next item during the current one's last tile.
+  // Otherwise the workgroup runs the one item its id maps to.  Every item
+  // ends with a barrier after its last LDS read, so the next item's first
+  // tile loads may overwrite the stage buffers.
+  __shared__ int s_item;
+  const int xcd = xcd_id();
+  if (tid == 0) s_item = PERSIST ? take_item(slot, xcd, total_items) : xcd_remap(blockIdx.x, total_items);
+  __syncthreads();
+  int work = __builtin_amdgcn_readfirstlane(s_item);
+  while (work >= 0) {
+    int next = -1;
+    const int bh = work / n_qtiles;
+    int qt = work % n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+    const size_t head = (size_t)bh * N * D;
+    const int q_first = qt * BR + 32 * wave;
+    const int my_q = q_first + lq;
 
-  u32x4 qf[D / 16];
-  {
-    const uint16_t* qrow = Q + head + (size_t)my_q * D + 8 * hf;
+    u32x4 qf[D / 16];
+    {
+      const uint16_t* qrow = Q + head + (size_t)my_q * D + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      qf[c] = (my_q < N) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
-  }
-
-  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
-  const int T = (kv_end + BC - 1) / BC;
-  const int my_T = CAUSAL ? min(T, (q_first + 31) / BC + 1) : T;
-
-  const uint16_t* const kbase = K + head;
-  const uint16_t* const vbase = V + head;
-  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer (st+1) % NS.
-  // Each tile gets a descriptor starting at its first key row (scalar
-  // arithmetic), so the per-lane offsets are the same for every tile; the
-  // record count ends at row N, so rows past N read as zero.
-  auto load_stage = [&](int st) {
-    const unsigned base = lds0 + ((st + 1) % NS) * 2 * TB;
-    if (st + 1 < T) {
-      const int k0 = (st + 1) * BC;
-      dma_tile<D, false, NW>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base, 0, wave, lane);
+      for (int c = 0; c < D / 16; ++c)
+        qf[c] = (my_q < N) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
     }
-    if (st >= 0) {
-      const int k0 = st * BC;
-      dma_tile<D, true, NW>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base + TB, 0, wave, lane);
-    }
-  };
-  auto stage_buf = [&](int st) { return (st + 1) % NS; };
-  const int k_lane = (lq >> 4) * CG * 1024 + (hf * 16 + (lq & 15)) * 16;
-  const int tr_i = lane & 15, tr_grp = lane >> 4;
-  const int v_lane = (4 * (tr_grp >> 1) + (tr_i >> 2)) * 64 + (2 * (tr_grp & 1) + ((tr_i & 3) >> 1)) * 16 +
-                     8 * (tr_i & 1);
 
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
-  // running state: row max m, its scaled reference mc (exponents are taken
-  // against mc), fp32 sum l and the sum lw of the bf16-rounded weights
-  float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
-  const float c2 = scale * kLog2e;
-  u32x4 pf[BC / 16];  // P_j packed, B operand of the P V product
+    const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
+    const int T = (kv_end + BC - 1) / BC;
+    const int my_T = CAUSAL ? min(T, (q_first + 31) / BC + 1) : T;
 
-  auto qk = [&](const uint8_t* kt, f32x16 (&acc)[BC / 32]) {
-#pragma unroll
-    for (int b = 0; b < BC / 32; ++b) {
-      acc[b] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const u32x4 a = *(const u32x4*)(kt + k_lane + (2 * b * CG + (c >> 1)) * 1024 + (c & 1) * 512);
-        acc[b] = TT::mma(a, qf[c], acc[b]);
+    const uint16_t* const kbase = K + head;
+    const uint16_t* const vbase = V + head;
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer (st+1) % NS.
+    // Each tile gets a descriptor starting at its first key row (scalar
+    // arithmetic), so the per-lane offsets are the same for every tile; the
+    // record count ends at row N, so rows past N read as zero.
+    auto load_stage = [&](int st) {
+      const unsigned base = lds0 + ((st + 1) % NS) * 2 * TB;
+      if (st + 1 < T) {
+        const int k0 = (st + 1) * BC;
+        dma_tile<D, false, NW>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base, 0, wave, lane);
       }
-    }
-  };
-  auto pv = [&](const uint8_t* vt) {
-#pragma unroll
-    for (int cc = 0; cc < BC / 16; ++cc)
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
-        const uint8_t* va = vt + v_lane + (cc * CG + b) * 1024;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        o[b] = TT::mma(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pf[cc], o[b]);
+      if (st >= 0) {
+        const int k0 = st * BC;
+        dma_tile<D, true, NW>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base + TB, 0, wave, lane);
       }
-  };
-  // Tile t's mask (if any), row max and reference move.  Returns the factor
-  // for O, which the caller applies after O has received the previous tile;
-  // l and lw are rescaled here.  `resc` tells whether any row moved.
-  auto part1 = [&](f32x16 (&sv)[BC / 32], int t, bool masked, bool& resc) -> float {
-    if (masked) {
-      const int k0 = t * BC;
+    };
+    auto stage_buf = [&](int st) { return (st + 1) % NS; };
+    const int k_lane = (lq >> 4) * CG * 1024 + (hf * 16 + (lq & 15)) * 16;
+    const int tr_i = lane & 15, tr_grp = lane >> 4;
+    const int v_lane = (4 * (tr_grp >> 1) + (tr_i >> 2)) * 64 + (2 * (tr_grp & 1) + ((tr_i & 3) >> 1)) * 16 +
+                       8 * (tr_i & 1);
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
+    // running state: row max m, its scaled reference mc (exponents are taken
+    // against mc), fp32 sum l and the sum lw of the bf16-rounded weights
+    float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
+    const float c2 = scale * kLog2e;
+    u32x4 pf[BC / 16];  // P_j packed, B operand of the P V product
+
+    auto qk = [&](const uint8_t* kt, f32x16 (&acc)[BC / 32]) {
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b) {
+        acc[b] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          const u32x4 a = *(const u32x4*)(kt + k_lane + (2 * b * CG + (c >> 1)) * 1024 + (c & 1) * 512);
+          acc[b] = TT::mma(a, qf[c], acc[b]);
+        }
+      }
+    };
+    auto pv = [&](const uint8_t* vt) {
+#pragma unroll
+      for (int cc = 0; cc < BC / 16; ++cc)
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          const uint8_t* va = vt + v_lane + (cc * CG + b) * 1024;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          o[b] = TT::mma(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pf[cc], o[b]);
+        }
+    };
+    // Tile t's mask (if any), row max and reference move.  Returns the factor
+    // for O, which the caller applies after O has received the previous tile;
+    // l and lw are rescaled here.  `resc` tells whether any row moved.
+    auto part1 = [&](f32x16 (&sv)[BC / 32], int t, bool masked, bool& resc) -> float {
+      if (masked) {
+        const int k0 = t * BC;
+#pragma unroll
+        for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool keep = key < N && (!CAUSAL || key <= my_q);
+            if (!keep) sv[b][r] = -INFINITY;
+          }
+      }
+      float mt = sv[0][0];
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[b][r]);
+      mt = half_max(mt);
+      m_run = fmaxf(m_run, mt);
+      const float mc_cand = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
+      resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
+      // 0 for a row's first finite tile; a still fully masked row keeps alpha 1
+      const float alpha = (!resc || mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
+      mc_run = resc ? mc_cand : mc_run;
+      l_run *= alpha;
+      lw_run *= alpha;
+      return alpha;
+    };
+    // Exponentials against the current reference, the two sums, and P packed.
+    auto part2 = [&](f32x16 (&sv)[BC / 32]) {
+      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
+      float ls[2] = {0.f, 0.f}, lws[2] = {0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < BC / 32; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool keep = key < N && (!CAUSAL || key <= my_q);
-          if (!keep) sv[b][r] = -INFINITY;
+          const float p = fast_exp2(fmaf(sv[b][r], c2, -off));
+          sv[b][r] = p;
+          ls[r & 1] += p;
         }
-    }
-    float mt = sv[0][0];
 #pragma unroll
-    for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[b][r]);
-    mt = half_max(mt);
-    m_run = fmaxf(m_run, mt);
-    const float mc_cand = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
-    resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
-    // 0 for a row's first finite tile; a still fully masked row keeps alpha 1
-    const float alpha = (!resc || mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
-    mc_run = resc ? mc_cand : mc_run;
-    l_run *= alpha;
-    lw_run *= alpha;
-    return alpha;
-  };
-  // Exponentials against the current reference, the two sums, and P packed.
-  auto part2 = [&](f32x16 (&sv)[BC / 32]) {
-    const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
-    float ls[2] = {0.f, 0.f}, lws[2] = {0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sv[b][r], c2, -off));
-        sv[b][r] = p;
-        ls[r & 1] += p;
+      for (int c = 0; c < BC / 16; ++c) {
+        const int r0 = 8 * (c & 1);
+        const f32x16& sb = sv[c >> 1];
+        pf[c] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
+                      TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
+        lws[c & 1] = TT::sum2(pf[c][3], TT::sum2(pf[c][2], TT::sum2(pf[c][1], TT::sum2(pf[c][0], lws[c & 1]))));
       }
-#pragma unroll
-    for (int c = 0; c < BC / 16; ++c) {
-      const int r0 = 8 * (c & 1);
-      const f32x16& sb = sv[c >> 1];
-      pf[c] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
-                    TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
-      lws[c & 1] = TT::sum2(pf[c][3], TT::sum2(pf[c][2], TT::sum2(pf[c][1], TT::sum2(pf[c][0], lws[c & 1]))));
-    }
-    l_run += ls[0] + ls[1];
-    lw_run += lws[0] + lws[1];
-  };
-  auto tile_masked = [&](int t) { return (CAUSAL && t * BC + BC - 1 > q_first) || (t * BC + BC > N); };
+      l_run += ls[0] + ls[1];
+      lw_run += lws[0] + lws[1];
+    };
+    auto tile_masked = [&](int t) { return (CAUSAL && t * BC + BC - 1 > q_first) || (t * BC + BC > N); };
 
-  // One steady-state step (tile j's softmax and product, tile j+1's scores
-  // and statistics), written in issue order and fenced so that every MFMA is
-  // followed by the independent vector work that hides it.
-  auto steady = [&](f32x16 (&cur)[BC / 32], f32x16 (&nxt)[BC / 32], const uint8_t* kt,
-                    const uint8_t* vt, int t_next, bool mask_next) {
-    constexpr int NQK = BC / 32 * D / 16, NPV = BC / 16 * D / 32;
-    constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
-    const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
-    float ls0 = 0.f, ls1 = 0.f, lw0 = 0.f, lw1 = 0.f;
-    // ---- step A: S_{j+1} (MFMA) with exp / sums / packing of tile j (VALU)
-    auto kaddr = [&](int i) {
-      const int bb = i / (D / 16), c = i % (D / 16);
-      return (const u32x4*)(kt + k_lane + (2 * bb * CG + (c >> 1)) * 1024 + (c & 1) * 512);
-    };
-    constexpr int KP = 4;  // K operands in flight ahead of the matrix core
-    u32x4 kop[KP + 1];
+    // One steady-state step (tile j's softmax and product, tile j+1's scores
+    // and statistics), written in issue order and fenced so that every MFMA is
+    // followed by the independent vector work that hides it.
+    auto steady = [&](f32x16 (&cur)[BC / 32], f32x16 (&nxt)[BC / 32], const uint8_t* kt,
+                      const uint8_t* vt, int t_next, bool mask_next) {
+      constexpr int NQK = BC / 32 * D / 16, NPV = BC / 16 * D / 32;
+      constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
+      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
+      float ls0 = 0.f, ls1 = 0.f, lw0 = 0.f, lw1 = 0.f;
+      // ---- step A: S_{j+1} (MFMA) with exp / sums / packing of tile j (VALU)
+      auto kaddr = [&](int i) {
+        const int bb = i / (D / 16), c = i % (D / 16);
+        return (const u32x4*)(kt + k_lane + (2 * bb * CG + (c >> 1)) * 1024 + (c & 1) * 512);
+      };
+      constexpr int KP = 4;  // K operands in flight ahead of the matrix core
+      u32x4 kop[KP + 1];
 #pragma unroll
-    for (int i = 0; i < KP && i < NQK; ++i) kop[i] = *kaddr(i);
-    __builtin_amdgcn_sched_barrier(0);
-    constexpr int EPM = ELEM / NQK;  // elements of tile j per MFMA (2 at d = 128, 4 at d = 64)
-#pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      if (i + KP < NQK) kop[(i + KP) % (KP + 1)] = *kaddr(i + KP);
-      const int bb = i / (D / 16), c = i % (D / 16);
-      nxt[bb] = TT::mma(kop[i % (KP + 1)], qf[c], c == 0 ? f32x16{} : nxt[bb]);
-#pragma unroll
-      for (int e = EPM * i; e < EPM * (i + 1); ++e) {
-        const float pe = fast_exp2(fmaf(cur[e >> 4][e & 15], c2, -off));
-        cur[e >> 4][e & 15] = pe;
-        if (e & 1) ls1 += pe; else ls0 += pe;
-        if ((e & 7) == 7) {  // a 16-key chunk's probabilities are complete: pack them
-          const int cc = e >> 3, r0 = 8 * (cc & 1);
-          const f32x16& sb = cur[cc >> 1];
-          pf[cc] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
-                         TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
-          if (cc & 1) lw1 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw1))));
-          else lw0 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw0))));
-        }
-      }
+      for (int i = 0; i < KP && i < NQK; ++i) kop[i] = *kaddr(i);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    l_run += ls0 + ls1;
-    lw_run += lw0 + lw1;
-    // ---- step B: O += P_j V_j (MFMA) with tile j+1's row max (VALU)
-    auto vaddr = [&](int i) {
-      const int cc = i / (D / 32), bb = i % (D / 32);
-      return vt + v_lane + (cc * CG + bb) * 1024;
-    };
-    constexpr int VP = 4;  // V operands in flight ahead of the matrix core
-    u32x4 vop[VP + 1];
-    auto vload = [&](int i) {
-      const uint8_t* va = vaddr(i);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-      return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-    };
+      constexpr int EPM = ELEM / NQK;  // elements of tile j per MFMA (2 at d = 128, 4 at d = 64)
 #pragma unroll
-    for (int i = 0; i < VP && i < NPV; ++i) vop[i] = vload(i);
-    if (mask_next) {
-      // keys past the row (causal) or past N score -inf: lane (q, h) keeps
-      // key offsets 32b + 8(r/4) + r%4 <= lim within tile t_next
-      const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - (t_next * BC + 4 * hf);
+      for (int i = 0; i < NQK; ++i) {
+        if (i + KP < NQK) kop[(i + KP) % (KP + 1)] = *kaddr(i + KP);
+        const int bb = i / (D / 16), c = i % (D / 16);
+        nxt[bb] = TT::mma(kop[i % (KP + 1)], qf[c], c == 0 ? f32x16{} : nxt[bb]);
 #pragma unroll
-      for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * b + 8 * (r >> 2) + (r & 3) > lim) nxt[b][r] = -INFINITY;
-    }
-    // Raised wave priority while this wave feeds the matrix core: when the
-    // other wave on the SIMD is in its exponential-heavy step, the arbiter
-    // issues this wave's MFMAs first instead of letting them queue behind
-    // vector instructions.
-    __builtin_amdgcn_s_setprio(2);
-    __builtin_amdgcn_sched_barrier(0);
-    float mt0 = -INFINITY, mt1 = -INFINITY;
-    constexpr int MPM = (ELEM / 2 + NPV - 3) / (NPV - 2);  // score pairs per MFMA from the third on
-    int e = 0;
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      if (i + VP < NPV) vop[(i + VP) % (VP + 1)] = vload(i + VP);
-      const int cc = i / (D / 32), bb = i % (D / 32);
-      o[bb] = TT::mma(vop[i % (VP + 1)], pf[cc], o[bb]);
-      if (i >= 2) {
-#pragma unroll
-        for (int k = 0; k < MPM; ++k) {
-          if (e < ELEM / 2) {  // two scores of tile j+1 per max3
-            const int e0 = 2 * e, e1 = 2 * e + 1;
-            if (e & 1) mt1 = max3(mt1, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
-            else mt0 = max3(mt0, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
-            ++e;
+        for (int e = EPM * i; e < EPM * (i + 1); ++e) {
+          const float pe = fast_exp2(fmaf(cur[e >> 4][e & 15], c2, -off));
+          cur[e >> 4][e & 15] = pe;
+          if (e & 1) ls1 += pe; else ls0 += pe;
+          if ((e & 7) == 7) {  // a 16-key chunk's probabilities are complete: pack them
+            const int cc = e >> 3, r0 = 8 * (cc & 1);
+            const f32x16& sb = cur[cc >> 1];
+            pf[cc] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
+                           TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
+            if (cc & 1) lw1 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw1))));
+            else lw0 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw0))));
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      l_run += ls0 + ls1;
+      lw_run += lw0 + lw1;
+      // ---- step B: O += P_j V_j (MFMA) with tile j+1's row max (VALU)
+      auto vaddr = [&](int i) {
+        const int cc = i / (D / 32), bb = i % (D / 32);
+        return vt + v_lane + (cc * CG + bb) * 1024;
+      };
+      constexpr int VP = 4;  // V operands in flight ahead of the matrix core
+      u32x4 vop[VP + 1];
+      auto vload = [&](int i) {
+        const uint8_t* va = vaddr(i);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      };
+#pragma unroll
+      for (int i = 0; i < VP && i < NPV; ++i) vop[i] = vload(i);
+      if (mask_next) {
+        // keys past the row (causal) or past N score -inf: lane (q, h) keeps
+        // key offsets 32b + 8(r/4) + r%4 <= lim within tile t_next
+        const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - (t_next * BC + 4 * hf);
+#pragma unroll
+        for (int b = 0; b < BC / 32; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * b + 8 * (r >> 2) + (r & 3) > lim) nxt[b][r] = -INFINITY;
+      }
+      // Raised wave priority while this wave feeds the matrix core: when the
+      // other wave on the SIMD is in its exponential-heavy step, the arbiter
+      // issues this wave's MFMAs first instead of letting them queue behind
+      // vector instructions.
+      __builtin_amdgcn_s_setprio(2);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // tile j+1's statistics; a row whose keys in this tile are all masked
-    // keeps its max (tile 0 gave every row a finite one)
-    const float mt = half_max(max3(mt0, mt1, mt1));
-    m_run = fmaxf(m_run, mt);
-    const float mc_cand = m_run * c2;
-    const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
-    if (resc) {
-      const float alpha = fast_exp2(mc_run - mc_cand);
-      mc_run = mc_cand;
-      l_run *= alpha;
-      lw_run *= alpha;
+      float mt0 = -INFINITY, mt1 = -INFINITY;
+      constexpr int MPM = (ELEM / 2 + NPV - 3) / (NPV - 2);  // score pairs per MFMA from the third on
+      int e = 0;
 #pragma unroll
-      for (int bb = 0; bb < D / 32; ++bb) o[bb] *= alpha;
-    }
-  };
-
-  // Stages are issued AHEAD = NS-1 iterations early: iteration j issues stage
-  // j + AHEAD into the buffer of stage j - 1, which iteration j - 1 finished
-  // reading before its closing barrier.  Before that barrier, iteration j
-  // waits until stage j + 1 (read next) has landed while stages j + 2 ..
-  // j + AHEAD stay in flight.  vmcnt retires in issue order, so "at most n
-  // outstanding" (n = this wave's loads of those younger stages) means every
-  // older load is done.
-  constexpr int AHEAD = NS - 1;
-  static_assert((NS & (NS - 1)) == 0 && NS <= 4, "power-of-two stage count, at most 4");
-  auto issue_for = [&](int j) { if (j + AHEAD < T) load_stage(j + AHEAD); };
-  // loads one wave issues for stage st: K tile (if st+1 < T) and V tile (if st >= 0)
-  auto stage_loads = [&](int st) {
-    return st >= T ? 0 : (st + 1 < T ? NDMA / 2 : 0) + (st >= 0 ? NDMA / 2 : 0);
-  };
-  // s_waitcnt takes an immediate, so each reachable count (a multiple of half
-  // a stage, at most NS-2 full stages) gets its own instruction
-  auto wait_keep = [&](int keep) {
-    constexpr int H = NDMA / 2;
-    static_assert((NS - 2) * NDMA <= 63, "vmcnt is a 6-bit count");
-    if constexpr (NS >= 4) {
-      if (keep >= 4 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * H)); return; }
-      if (keep == 3 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * H)); return; }
-    }
-    if constexpr (NS >= 3) {
-      if (keep >= 2 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * H)); return; }
-      if (keep == H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(H)); return; }
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  };
-  auto end_iter = [&](int j) {
-    int keep = 0;
+      for (int i = 0; i < NPV; ++i) {
+        if (i + VP < NPV) vop[(i + VP) % (VP + 1)] = vload(i + VP);
+        const int cc = i / (D / 32), bb = i % (D / 32);
+        o[bb] = TT::mma(vop[i % (VP + 1)], pf[cc], o[bb]);
+        if (i >= 2) {
 #pragma unroll
-    for (int st = 2; st <= AHEAD; ++st) keep += stage_loads(j + st);
-    wait_keep(keep);
-    __syncthreads();
-  };
-
-  // prologue: stages -1 (K_0), 0 (K_1, V_0), ..., NS-2; S_0 and its statistics
-  f32x16 sA[BC / 32], sB[BC / 32];
-  load_stage(-1);
-#pragma unroll
-  for (int st = 0; st <= NS - 2; ++st)
-    if (st < T) load_stage(st);
-  // stages -1 and 0 must be in; stages 1 .. NS-2 may stay in flight
-  {
-    int keep = 0;
-#pragma unroll
-    for (int st = 1; st <= NS - 2; ++st) keep += stage_loads(st);
-    wait_keep(keep);
-  }
-  __syncthreads();
-  if (0 < my_T) {
-    bool resc;
-    qk(smem + stage_buf(-1) * 2 * TB, sA);
-    part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
-  }
-  __syncthreads();  // every wave is done with stage -1's buffer before it is refilled
-
-  // Steady steps run in pairs while both tiles have a successor, masking the
-  // next tile's scores where it crosses the diagonal or the end of the
-  // sequence; the last one or two tiles take the general path.
-  int j = 0;
-  // two tiles per trip so the score registers swap roles
-  for (; j + 2 < T; j += 2) {
-    issue_for(j);
-    {
-      const uint8_t* kt = smem + stage_buf(j) * 2 * TB;
-      steady(sA, sB, kt, kt + TB, j + 1, tile_masked(j + 1));
-    }
-    end_iter(j);
-    issue_for(j + 1);
-    {
-      const uint8_t* kt = smem + stage_buf(j + 1) * 2 * TB;
-      steady(sB, sA, kt, kt + TB, j + 2, tile_masked(j + 2));
-    }
-    end_iter(j + 1);
-  }
-  // remaining tiles: general path (a wave skips tiles past its last row)
-  for (; j < T; ++j) {
-    issue_for(j);
-    const uint8_t* kt = smem + stage_buf(j) * 2 * TB;  // K_{j+1}
-    const uint8_t* vt = kt + TB;                        // V_j
-    if (j < my_T) {
-      part2(sA);
-      pv(vt);
-      if (j + 1 < my_T) {
-        bool resc;
-        qk(kt, sB);
-        const float alpha = part1(sB, j + 1, tile_masked(j + 1), resc);
-        if (resc) {
-#pragma unroll
-          for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+          for (int k = 0; k < MPM; ++k) {
+            if (e < ELEM / 2) {  // two scores of tile j+1 per max3
+              const int e0 = 2 * e, e1 = 2 * e + 1;
+              if (e & 1) mt1 = max3(mt1, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
+              else mt0 = max3(mt0, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
+              ++e;
+            }
+          }
         }
-#pragma unroll
-        for (int b = 0; b < BC / 32; ++b) sA[b] = sB[b];
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    end_iter(j);
-  }
+      __builtin_amdgcn_s_setprio(0);
+      // tile j+1's statistics; a row whose keys in this tile are all masked
+      // keeps its max (tile 0 gave every row a finite one)
+      const float mt = half_max(max3(mt0, mt1, mt1));
+      m_run = fmaxf(m_run, mt);
+      const float mc_cand = m_run * c2;
+      const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
+      if (resc) {
+        const float alpha = fast_exp2(mc_run - mc_cand);
+        mc_run = mc_cand;
+        l_run *= alpha;
+        lw_run *= alpha;
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb) o[bb] *= alpha;
+      }
+    };
 
-  const float l_tot = half_sum(l_run);
-  const float lw_tot = half_sum(lw_run);
-  if (my_q < N) {
-    const float inv = __builtin_amdgcn_rcpf(lw_tot);
-    uint16_t* orow = O + head + (size_t)my_q * D + 4 * hf;
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {TT::pack(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv),
-                         TT::pack(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
-        *(u32x2*)(orow + 32 * b + 8 * g) = w;
+    // Stages are issued AHEAD = NS-1 iterations early: iteration j issues stage
+    // j + AHEAD into the buffer of stage j - 1, which iteration j - 1 finished
+    // reading before its closing barrier.  Before that barrier, iteration j
+    // waits until stage j + 1 (read next) has landed while stages j + 2 ..
+    // j + AHEAD stay in flight.  vmcnt retires in issue order, so "at most n
+    // outstanding" (n = this wave's loads of those younger stages) means every
+    // older load is done.
+    constexpr int AHEAD = NS - 1;
+    static_assert((NS & (NS - 1)) == 0 && NS <= 4, "power-of-two stage count, at most 4");
+    auto issue_for = [&](int j) { if (j + AHEAD < T) load_stage(j + AHEAD); };
+    // loads one wave issues for stage st: K tile (if st+1 < T) and V tile (if st >= 0)
+    auto stage_loads = [&](int st) {
+      return st >= T ? 0 : (st + 1 < T ? NDMA / 2 : 0) + (st >= 0 ? NDMA / 2 : 0);
+    };
+    // s_waitcnt takes an immediate, so each reachable count (a multiple of half
+    // a stage, at most NS-2 full stages) gets its own instruction
+    auto wait_keep = [&](int keep) {
+      constexpr int H = NDMA / 2;
+      static_assert((NS - 2) * NDMA <= 63, "vmcnt is a 6-bit count");
+      if constexpr (NS >= 4) {
+        if (keep >= 4 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * H)); return; }
+        if (keep == 3 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * H)); return; }
       }
-    if (hf == 0) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      if constexpr (NS >= 3) {
+        if (keep >= 2 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * H)); return; }
+        if (keep == H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(H)); return; }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    };
+    auto end_iter = [&](int j) {
+      int keep = 0;
+#pragma unroll
+      for (int st = 2; st <= AHEAD; ++st) keep += stage_loads(j + st);
+      wait_keep(keep);
+      __syncthreads();
+    };
+
+    // prologue: stages -1 (K_0), 0 (K_1, V_0), ..., NS-2; S_0 and its statistics
+    f32x16 sA[BC / 32], sB[BC / 32];
+    load_stage(-1);
+#pragma unroll
+    for (int st = 0; st <= NS - 2; ++st)
+      if (st < T) load_stage(st);
+    // stages -1 and 0 must be in; stages 1 .. NS-2 may stay in flight
+    {
+      int keep = 0;
+#pragma unroll
+      for (int st = 1; st <= NS - 2; ++st) keep += stage_loads(st);
+      wait_keep(keep);
+    }
+    __syncthreads();
+    if (0 < my_T) {
+      bool resc;
+      qk(smem + stage_buf(-1) * 2 * TB, sA);
+      part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
+    }
+    __syncthreads();  // every wave is done with stage -1's buffer before it is refilled
+
+    // Steady steps run in pairs while both tiles have a successor, masking the
+    // next tile's scores where it crosses the diagonal or the end of the
+    // sequence; the last one or two tiles take the general path.
+    int j = 0;
+    // two tiles per trip so the score registers swap roles
+    for (; j + 2 < T; j += 2) {
+      issue_for(j);
+      {
+        const uint8_t* kt = smem + stage_buf(j) * 2 * TB;
+        steady(sA, sB, kt, kt + TB, j + 1, tile_masked(j + 1));
+      }
+      end_iter(j);
+      issue_for(j + 1);
+      {
+        const uint8_t* kt = smem + stage_buf(j + 1) * 2 * TB;
+        steady(sB, sA, kt, kt + TB, j + 2, tile_masked(j + 2));
+      }
+      end_iter(j + 1);
+    }
+    // remaining tiles: general path (a wave skips tiles past its last row)
+    for (; j < T; ++j) {
+      issue_for(j);
+      // claim the next item during the last tile: claiming earlier would
+      // reserve work that an idle workgroup could have started sooner
+      if (PERSIST && tid == 0 && j == T - 1) next = take_item(slot, xcd, total_items);
+      const uint8_t* kt = smem + stage_buf(j) * 2 * TB;  // K_{j+1}
+      const uint8_t* vt = kt + TB;                        // V_j
+      if (j < my_T) {
+        part2(sA);
+        pv(vt);
+        if (j + 1 < my_T) {
+          bool resc;
+          qk(kt, sB);
+          const float alpha = part1(sB, j + 1, tile_masked(j + 1), resc);
+          if (resc) {
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+          }
+#pragma unroll
+          for (int b = 0; b < BC / 32; ++b) sA[b] = sB[b];
+        }
+      }
+      end_iter(j);
+    }
+
+    const float l_tot = half_sum(l_run);
+    const float lw_tot = half_sum(lw_run);
+    if (my_q < N) {
+      const float inv = __builtin_amdgcn_rcpf(lw_tot);
+      uint16_t* orow = O + head + (size_t)my_q * D + 4 * hf;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = {TT::pack(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv),
+                           TT::pack(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
+          *(u32x2*)(orow + 32 * b + 8 * g) = w;
+        }
+      if (hf == 0) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    if (tid == 0) s_item = next;
+    __syncthreads();
+    work = __builtin_amdgcn_readfirstlane(s_item);
   }
+  if (PERSIST && tid == 0) leave_launch(slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -749,21 +816,50 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 
 // ---------------------------------------------------------------------------
 // host side
+// Compute units of the current device, queried once per device.
+hipError_t compute_units(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && (*cus = cache[dev].load(std::memory_order_relaxed)) > 0)
+    return hipSuccess;
+  if (hipError_t e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+      e != hipSuccess)
+    return e;
+  if (*cus <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
 template <class TT, int D>
 hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                      int N, float scale, bool causal, hipStream_t st) {
   // d = 128: 8 waves (256 query rows) per workgroup halve the K/V tile
-  // loads per FLOP; d = 64 keeps 4 waves so that two workgroups share a CU.
+  // loads per FLOP, and one persistent workgroup per CU claims work items
+  // (no gap between items, no idle XCD at the end).  d = 64: 4 waves, two
+  // workgroups per CU, one workgroup per item.
   constexpr int NW = D == 128 ? 8 : 4, NS = 2;
+  constexpr bool PERSIST = D == 128;
+  static std::atomic<unsigned> launches{0};
   const int nq = (N + 32 * NW - 1) / (32 * NW);
   const int total = nq * BH;
-  const dim3 grid(total), block(64 * NW);
+  int grid_wg = total, slot = 0;
+  if (PERSIST) {
+    int cus = 0;
+    if (hipError_t e = compute_units(&cus); e != hipSuccess) return e;
+    grid_wg = std::min(total, cus);
+    slot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kWorkSlots);
+  }
+  const dim3 grid(grid_wg), block(64 * NW);
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_sp<TT, D, true, NW, NS>), grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total, scale);
+    hipLaunchKernelGGL((attn_fwd_sp<TT, D, true, NW, NS, PERSIST>), grid, block, 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N,
+                       nq, total, slot, scale);
   else
-    hipLaunchKernelGGL((attn_fwd_sp<TT, D, false, NW, NS>), grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, nq, total, scale);
+    hipLaunchKernelGGL((attn_fwd_sp<TT, D, false, NW, NS, PERSIST>), grid, block, 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N,
+                       nq, total, slot, scale);
   return hipGetLastError();
 }
 

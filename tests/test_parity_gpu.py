@@ -185,6 +185,33 @@ def test_side_stream_and_preallocated_outputs():
     assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
 
 
+def test_many_launches_and_two_streams_agree():
+    """Head dim 128 runs one persistent workgroup per CU that claims work
+    items from per-launch counters, reused every 64 launches and cleared by
+    each launch's last workgroup.  150 launches (more items than CUs, so each
+    workgroup claims several), alternating between two streams that run
+    concurrently, must all give bitwise the first launch's result."""
+    q, k, v = make_qkv(1, 64, 2048, 128, "bf16", 82)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    ref_o, ref_l = fa.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [(torch.empty_like(q), torch.empty((1, 64, 2048), device="cuda")) for _ in streams]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    bad = 0
+    for i in range(75):
+        for s_, (o_, l_) in zip(streams, outs):
+            with torch.cuda.stream(s_):
+                o_.fill_(7.0)
+                l_.fill_(7.0)
+                fa.attention(q, k, v, causal=True, out=o_, lse=l_)
+        for s_, (o_, l_) in zip(streams, outs):
+            s_.synchronize()
+            bad += int(not (torch.equal(o_, ref_o) and torch.equal(l_, ref_l)))
+    assert bad == 0, f"{bad} of 150 launches differ from the first"
+
+
 def test_rejected_call_writes_nothing():
     q = torch.randn(1, 1, 64, 96, device="cuda", dtype=torch.bfloat16)
     out = torch.full_like(q, 3.0)
