@@ -159,7 +159,7 @@ __device__ __forceinline__ int take_item(int slot, int xcd, int total) {
     const unsigned lo = (unsigned)((long long)y * total / 8);
     const unsigned n = (unsigned)((long long)(y + 1) * total / 8) - lo;
     unsigned* ctr = &g_next_rank[slot][y];
-    if (n == 0 || __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+    if (n == 0) continue;
     const unsigned t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (t < n) return (int)(lo + t);
   }
@@ -285,6 +285,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int NDMA = 2 * LY::BLOCKS / NW;
   static_assert(2 * LY::BLOCKS % NW == 0 && NS >= 2, "stages split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * 2 * TB];  // [stage buffer][K, V]
+  // O staging in the epilogue: per wave 32 rows x 64 columns (bf16) at a
+  // 144-byte row stride (16-byte aligned rows, writes spread over the banks)
+  constexpr int kOStageRow = 144, kOStageBytes = 32 * kOStageRow;
+  static_assert(NW * kOStageBytes <= NS * 2 * TB && D % 64 == 0, "O staging fits the stage buffers");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
@@ -647,20 +651,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       end_iter(j);
     }
 
+    // Epilogue.  A lane holds 8-byte pieces of its row at 16-byte strides, so
+    // storing straight from registers would make every store instruction
+    // touch 32 rows; instead each wave passes its normalised, rounded rows
+    // through its own LDS area (the stage buffers are free after the last
+    // barrier) and stores whole 128-byte row segments, 8 lanes per segment.
     const float l_tot = half_sum(l_run);
     const float lw_tot = half_sum(lw_run);
-    if (my_q < N) {
-      const float inv = __builtin_amdgcn_rcpf(lw_tot);
-      uint16_t* orow = O + head + (size_t)my_q * D + 4 * hf;
+    {
+      const float inv = __builtin_amdgcn_rcpf(lw_tot);  // rows past N: finite, not stored
+      uint8_t* stg = smem + wave * kOStageBytes;
 #pragma unroll
-      for (int b = 0; b < D / 32; ++b)
+      for (int r = 0; r < D / 64; ++r) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 w = {TT::pack(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv),
-                           TT::pack(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
-          *(u32x2*)(orow + 32 * b + 8 * g) = w;
+        for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& ob = o[2 * r + bl];
+            const u32x2 w = {TT::pack(ob[4 * g + 0] * inv, ob[4 * g + 1] * inv),
+                             TT::pack(ob[4 * g + 2] * inv, ob[4 * g + 3] * inv)};
+            *(u32x2*)(stg + lq * kOStageRow + 2 * (32 * bl + 8 * g + 4 * hf)) = w;
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * i + (lane >> 3);
+          const u32x4 v = *(const u32x4*)(stg + row * kOStageRow + 16 * (lane & 7));
+          if (q_first + row < N)
+            *(u32x4*)(O + head + (size_t)(q_first + row) * D + 64 * r + 8 * (lane & 7)) = v;
         }
-      if (hf == 0) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      }
+      if (hf == 0 && my_q < N) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
     if (tid == 0) s_item = next;
     __syncthreads();
