@@ -10,10 +10,11 @@ without the built library every call raises.
 """
 from ._native import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FA_ERR_HIP,
                       FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_OK, FaError,
-                      attention, fa_fwd, fa_fwd_supported, fa_status_string,
-                      fa_version, library, library_path)
+                      attention, fa_fwd, fa_fwd_supported, fa_fwd_workspace_size,
+                      fa_fwd_ws, fa_status_string, fa_version, library, library_path)
 
-__all__ = ["attention", "fa_fwd", "fa_fwd_supported", "fa_status_string", "fa_version",
+__all__ = ["attention", "fa_fwd", "fa_fwd_ws", "fa_fwd_workspace_size", "fa_fwd_supported",
+           "fa_status_string", "fa_version",
            "library", "library_path", "FaError", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_FP32", "FA_DTYPE_FP16",
            "FA_DTYPE_BF16"]

@@ -42,6 +42,12 @@ def library():
         L.fa_fwd.restype = ctypes.c_int
         L.fa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.fa_fwd_ws.restype = ctypes.c_int
+        L.fa_fwd_ws.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.c_void_p]
+        L.fa_fwd_workspace_size.restype = ctypes.c_size_t
+        L.fa_fwd_workspace_size.argtypes = [ctypes.c_int] * 6
         L.fa_fwd_supported.restype = ctypes.c_int
         L.fa_fwd_supported.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.fa_status_string.restype = ctypes.c_char_p
@@ -71,15 +77,32 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: 
                             int(causal), int(dtype), stream)
 
 
+def fa_fwd_ws(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+              scale: float, causal: int, dtype: int, workspace: int, workspace_bytes: int,
+              stream: int) -> int:
+    """The raw C entry point with a caller workspace."""
+    return library().fa_fwd_ws(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), int(causal),
+                               int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_workspace_size(B: int, H: int, N: int, d: int, causal: int, dtype: int) -> int:
+    """Workspace bytes fa_fwd_ws can use on the current device (0: none)."""
+    return int(library().fa_fwd_workspace_size(int(B), int(H), int(N), int(d), int(causal),
+                                               int(dtype)))
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               scale: float | None = None, out: torch.Tensor | None = None,
-              lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+              lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
+              split_keys: bool = True):
     """O = softmax(scale * Q K^T) V and the per-row log-sum-exp, on the GPU.
 
     q, k, v: contiguous device tensors [B, H, N, d] of one dtype.  scale
     defaults to 1/sqrt(d).  Returns (o [B,H,N,d] in q's dtype, lse [B,H,N]
     fp32).  The launch is asynchronous on `stream` (default: torch's current
-    stream).
+    stream).  With split_keys, problems the library would split over key
+    ranges (fp32 grids smaller than the GPU) get a workspace from torch's
+    allocator on `stream` and run through fa_fwd_ws; otherwise fa_fwd.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
@@ -108,10 +131,19 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
         raise ValueError("lse must be a contiguous fp32 tensor [B, H, N]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    code = _DTYPE_CODE[q.dtype]
     with torch.cuda.device(q.device):
-        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
-                    stream.cuda_stream)
+        ws_bytes = fa_fwd_workspace_size(B, H, N, d, int(bool(causal)), code) if split_keys else 0
+        if ws_bytes:
+            with torch.cuda.stream(stream):
+                ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            st = fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code,
+                           ws.data_ptr(), ws_bytes, stream.cuda_stream)
+            ws.record_stream(stream)
+        else:
+            st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, N, d, float(scale), int(bool(causal)), code, stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st) if st == FA_ERR_HIP else ValueError(
             f"fa_fwd: {fa_status_string(st)} (status {st})")

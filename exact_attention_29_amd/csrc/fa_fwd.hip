@@ -702,17 +702,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 //                 the score block); output block bb row i is column
 //                 w*DSL + NB*i + bb (NB = DSL/32 blocks), so one lane's NB
 //                 values of a V row are contiguous.
-template <int DSL, int DS, bool CAUSAL>
+//
+// Key split (SPLIT): work item (query block, split s) covers key tiles
+// [s*tps, (s+1)*tps) only and writes its own normalised output and
+// log-sum-exp over those keys to Opart[s] / LSEpart[s] (rows*D and rows
+// floats per split); attn_combine_f32 merges the splits.  A split that holds
+// no kept key of a row writes 0 and -inf for it.
+template <int DSL, int DS, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
-    float scale) {
+    float scale, int n_split, int tps, float* __restrict__ Opart, float* __restrict__ LSEpart) {
   constexpr int D = DSL * DS, NB = DSL / 32, BC = 32;
   __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane & 31, hf = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, total_wg);
+  const int item = xcd_remap(blockIdx.x, total_wg);
+  const int split = SPLIT ? item % n_split : 0;  // the splits of a block are neighbours
+  const int work = SPLIT ? item / n_split : item;
   const int bh = work / n_qtiles;
   int qt = work % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;
@@ -736,8 +744,10 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const float c2 = scale * kLog2e;
   const int kv_end = CAUSAL ? min(N, q_first + 32) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
+  const int j_begin = SPLIT ? split * tps : 0;
+  const int j_end = SPLIT ? min(ntiles, j_begin + tps) : ntiles;
 
-  for (int j = 0; j < ntiles; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     const int k0 = j * BC;
     // partial S^T over this wave's columns
     f32x16 s = f32x16{};
@@ -815,8 +825,10 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 
   const float l_tot = half_sum(l_run);
   if (my_q < N) {
-    const float inv = 1.f / l_tot;
-    float* orow = O + head + (size_t)my_q * D + col0;
+    // a split may hold no kept key of this row: weight 0, lse -inf
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* orow = (SPLIT ? Opart + (size_t)split * ((size_t)N * D * (total_wg / (n_qtiles * n_split))) : O) +
+                  head + (size_t)my_q * D + col0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -829,9 +841,44 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
         for (int b = 0; b < NB; ++b) orow[NB * i + b] = o[b][r] * inv;
       }
     }
-    if (hf == 0 && wave == 0)
-      LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (hf == 0 && wave == 0) {
+      const float lse_row = l_tot > 0.f ? (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      if (SPLIT)
+        LSEpart[(size_t)split * N * (total_wg / (n_qtiles * n_split)) + (size_t)bh * N + my_q] = lse_row;
+      else
+        LSE[(size_t)bh * N + my_q] = lse_row;
+    }
   }
+}
+
+// Merge of the key splits: for each row, lse = ln sum_s exp(lse_s) and
+// O = sum_s exp(lse_s - lse) O_s -- the rule by which two partial softmax
+// results over disjoint key sets combine ("FlashAttention Engine", "Core
+// FlashAttention Mechanics", item 3).  D/4 threads per row, 4 columns each;
+// splits are summed in order, so the result is reproducible.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict__ Opart,
+                                                        const float* __restrict__ LSEpart,
+                                                        float* __restrict__ O,
+                                                        float* __restrict__ LSE, int rows,
+                                                        int n_split) {
+  constexpr int TPR = D / 4, RPB = TPR >= 256 ? 1 : 256 / TPR;  // threads per row, rows per block
+  const int t = threadIdx.x % TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (threadIdx.x / TPR >= RPB || row >= rows) return;
+  float m = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, LSEpart[(size_t)sp * rows + row]);
+  float sum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float w = __expf(LSEpart[(size_t)sp * rows + row] - m);  // 0 for an empty split
+    sum += w;
+    const f32x4 op = *(const f32x4*)(Opart + ((size_t)sp * rows + row) * D + 4 * t);
+    acc += w * op;
+  }
+  const float inv = 1.f / sum;
+  *(f32x4*)(O + (size_t)row * D + 4 * t) = acc * inv;
+  if (t == 0) LSE[row] = m + __logf(sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -883,18 +930,67 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   return hipGetLastError();
 }
 
+// Key-split plan of the fp32 path for grids too small to fill the GPU: about
+// one workgroup per CU, at least 4 key tiles per split.  n_split = 1: none.
+struct SplitPlan {
+  int n_split = 1, tps = 0;
+  size_t bytes = 0;  // workspace: n_split*rows*d floats of partial O, then n_split*rows of lse
+};
+
+SplitPlan plan_split(long long BH, int N, int d, int dtype) {
+  SplitPlan p;
+  if (dtype != FA_DTYPE_FP32) return p;
+  int cus = 0;
+  if (compute_units(&cus) != hipSuccess) return p;
+  const long long ntiles = (N + 31) / 32, items = ntiles * BH;
+  if (items >= cus) return p;
+  long long sp = std::min<long long>((cus + items - 1) / items, ntiles / 4);
+  if (sp < 2) return p;
+  p.tps = (int)((ntiles + sp - 1) / sp);
+  p.n_split = (int)((ntiles + p.tps - 1) / p.tps);
+  if (p.n_split < 2) return SplitPlan{};
+  const size_t rows = (size_t)BH * N;
+  p.bytes = (size_t)p.n_split * rows * (size_t)(d + 1) * sizeof(float);
+  return p;
+}
+
 template <int DSL, int DS>
 hipError_t launch32(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                    int N, float scale, bool causal, hipStream_t st) {
+                    int N, float scale, bool causal, hipStream_t st, const SplitPlan& plan,
+                    void* ws) {
+  constexpr int D = DSL * DS;
   const int nq = (N + 31) / 32;
+  if (plan.n_split > 1) {
+    const int total = nq * BH * plan.n_split;
+    float* opart = (float*)ws;
+    float* lpart = opart + (size_t)plan.n_split * BH * N * D;
+    const dim3 grid(total), block(DS * 64);
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true, true>), grid, block, 0, st, (const float*)q,
+                         (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale,
+                         plan.n_split, plan.tps, opart, lpart);
+    else
+      hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false, true>), grid, block, 0, st, (const float*)q,
+                         (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale,
+                         plan.n_split, plan.tps, opart, lpart);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    constexpr int RPB = D / 4 >= 256 ? 1 : 256 / (D / 4);
+    const int rows = BH * N;
+    hipLaunchKernelGGL((attn_combine_f32<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                       (const float*)opart, (const float*)lpart, (float*)o, lse, rows,
+                       plan.n_split);
+    return hipGetLastError();
+  }
   const int total = nq * BH;
   const dim3 grid(total), block(DS * 64);
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true>), grid, block, 0, st, (const float*)q,
-                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale);
+    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true, false>), grid, block, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale, 1, 0,
+                       nullptr, nullptr);
   else
-    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false>), grid, block, 0, st, (const float*)q,
-                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale);
+    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false, false>), grid, block, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale, 1, 0,
+                       nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -911,8 +1007,13 @@ int fa_fwd_supported(int d, int dtype, int causal) {
   return 0;
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-           int N, int d, float scale, int causal, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the entry points (no HIP call).
+int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               int B, int H, int N, int d, float scale, int causal, int dtype) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -921,6 +1022,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (BH > (1LL << 24)) return FA_ERR_INVALID_ARG;
   const long long nq_max = (N + 31) / 32;  // most query tiles any kernel uses
   if (nq_max * BH > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_INVALID_ARG;  // row index of lse
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
     return FA_ERR_UNSUPPORTED;
   if (!fa_fwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
@@ -929,10 +1031,15 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   const long long elem = dtype == FA_DTYPE_FP32 ? 4 : 2;
   if (((long long)N + 128) * d * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
 
+int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int N, int d, float scale, int causal, int dtype, const SplitPlan& plan, void* ws,
+             void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool c = causal != 0;
-  const int bh = (int)BH;
+  const int bh = B * H;
   hipError_t e = hipSuccess;
   if (dtype == FA_DTYPE_BF16) {
     e = d == 64 ? launch_sp<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
@@ -942,14 +1049,46 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                 : launch_sp<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
   } else {
     switch (d) {
-      case 64: e = launch32<64, 1>(q, k, v, o, lse, bh, N, scale, c, st); break;
-      case 128: e = launch32<128, 1>(q, k, v, o, lse, bh, N, scale, c, st); break;
-      case 256: e = launch32<128, 2>(q, k, v, o, lse, bh, N, scale, c, st); break;
-      case 512: e = launch32<128, 4>(q, k, v, o, lse, bh, N, scale, c, st); break;
-      default: e = launch32<128, 8>(q, k, v, o, lse, bh, N, scale, c, st); break;
+      case 64: e = launch32<64, 1>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
+      case 128: e = launch32<128, 1>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
+      case 256: e = launch32<128, 2>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
+      case 512: e = launch32<128, 4>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
+      default: e = launch32<128, 8>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
     }
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (int err = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype); err != FA_OK)
+    return err;
+  return dispatch(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, SplitPlan{}, nullptr, stream);
+}
+
+size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0 || (causal != 0 && causal != 1)) return 0;
+  if (!fa_fwd_supported(d, dtype, causal)) return 0;
+  if ((long long)B * H > (1LL << 24) || (long long)B * H * N > 0x7fffffffLL) return 0;
+  return plan_split((long long)B * H, N, d, dtype).bytes;
+}
+
+int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int N, int d, float scale, int causal, int dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (int err = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype); err != FA_OK)
+    return err;
+  if (workspace == nullptr || workspace_bytes == 0)
+    return dispatch(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, SplitPlan{}, nullptr,
+                    stream);
+  const SplitPlan plan = plan_split((long long)B * H, N, d, dtype);
+  if (workspace_bytes < plan.bytes) return FA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return FA_ERR_UNSUPPORTED;
+  return dispatch(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, plan, workspace, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -13,11 +13,15 @@
  * needs ("FlashAttention" (ai360xpert), section "Recomputation in the backward
  * pass").
  *
- * No function here allocates or frees device memory, synchronizes, or keeps
- * state between calls.  No C++ exception crosses this boundary.
+ * No function here allocates or frees device memory or synchronizes.  The
+ * only state kept between calls is a fixed array of work counters in the
+ * library's code object (see fa_fwd, "Scheduling").  No C++ exception
+ * crosses this boundary.
  */
 #ifndef FA_H
 #define FA_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -75,11 +79,53 @@ typedef enum {
  * Arithmetic: scores and all softmax statistics are fp32; bf16/fp16 products
  * accumulate in fp32 on the matrix cores; probabilities are rounded to the
  * input type before the product with V.  Results are bitwise reproducible run
- * to run (no atomics, fixed reduction order).
+ * to run (fixed reduction order).
+ *
+ * Scheduling: at head dim 128 (bf16/fp16) one workgroup per compute unit
+ * claims work items through atomic counters in the library's code object:
+ * 64 sets per device, taken round-robin per call and cleared by each call's
+ * last workgroup.  Which workgroup computes an item never changes the result.
+ * Calls that overlap in time use different sets unless more than 64 are in
+ * flight at once on one device, or one captured call is replayed
+ * concurrently with itself; such overlapping uses would share counters and
+ * must be avoided.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* stream);
+
+/*
+ * fa_fwd_workspace_size -- device workspace, in bytes, that fa_fwd_ws can use
+ * for this problem on the current device; 0 when it would run exactly as
+ * fa_fwd does.  Nonzero only for fp32 problems whose (query block, head,
+ * batch) items are fewer than the device's compute units: fa_fwd_ws then
+ * splits each query block's keys into ranges, computes the softmax-weighted
+ * output and log-sum-exp of every range in its own workgroup, and merges the
+ * ranges with lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s ("The
+ * Details of Flash Attention", section "Online Softmax": partial softmax
+ * results over disjoint key sets combine exactly; "FlashAttention Engine",
+ * "Core FlashAttention Mechanics", item 3, the same merge of two blocks).
+ * Returns 0 for invalid or unsupported arguments.
+ */
+size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
+
+/*
+ * fa_fwd_ws -- fa_fwd with a caller-owned device workspace.  Same arguments,
+ * outputs, errors and asynchrony as fa_fwd, plus:
+ *   workspace       : device pointer, 16-byte aligned, used as scratch by the
+ *                     call (contents on entry ignored, on return undefined);
+ *                     it must stay allocated until the stream has run the
+ *                     call, and must not overlap q, k, v, o or lse.
+ *   workspace_bytes : its size.  NULL or 0 runs exactly as fa_fwd.  Otherwise
+ *                     it must be >= fa_fwd_workspace_size(...) for the same
+ *                     problem on the same device, else FA_ERR_INVALID_ARG
+ *                     (a misaligned workspace gives FA_ERR_UNSUPPORTED).
+ * The key-split result equals fa_fwd's up to fp32 rounding (the merge adds
+ * one rounding per range); it is bitwise reproducible run to run.
+ */
+int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /* 1 when fa_fwd has a kernel for (d, dtype, causal), else 0. */
 int fa_fwd_supported(int d, int dtype, int causal);

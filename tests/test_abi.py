@@ -76,6 +76,22 @@ def test_unsupported_configurations(kw):
     assert call(**kw) == fa.FA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("kw", [dict(q=None), dict(B=0), dict(causal=2), dict(scale=0.0)])
+def test_workspace_entry_point_checks_arguments_first(kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, scale=0.125,
+             causal=0, dtype=fa.FA_DTYPE_FP32)
+    a.update(kw)
+    st = fa.fa_fwd_ws(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                      a["scale"], a["causal"], a["dtype"], FAKE, 1 << 20, None)
+    assert st == fa.FA_ERR_INVALID_ARG
+
+
+def test_workspace_size_is_zero_for_invalid_problems():
+    assert fa.fa_fwd_workspace_size(0, 1, 16, 64, 0, fa.FA_DTYPE_FP32) == 0
+    assert fa.fa_fwd_workspace_size(1, 1, 16, 96, 0, fa.FA_DTYPE_FP32) == 0
+    assert fa.fa_fwd_workspace_size(1, 1, 16, 64, 3, fa.FA_DTYPE_FP32) == 0
+
+
 def test_python_wrapper_rejects_host_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)

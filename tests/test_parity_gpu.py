@@ -60,6 +60,48 @@ def test_fp32_wide_heads():
             parity.check(parity.compare(o, lse, q, k, v, 1 / math.sqrt(d), causal), torch.float32)
 
 
+# ------------------------------------------------------------------ key split (fp32, small grids)
+@pytest.mark.parametrize("d", [64, 128, 256, 1024])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_split_matches_oracle_and_unsplit_path(d, causal):
+    """fp32 grids smaller than the GPU split each query block's keys into
+    ranges merged by their log-sum-exps; both that path and the unsplit one
+    must match the oracle, and each other to fp32 rounding."""
+    N = 391 if d < 1024 else 300
+    q, k, v = make_qkv(1, 2, N, d, "fp32", 90 + d + int(causal))
+    assert fa.fa_fwd_workspace_size(1, 2, N, d, int(causal), fa.FA_DTYPE_FP32) > 0
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    o_s, l_s = fa.attention(qc, kc, vc, causal=causal)
+    o_u, l_u = fa.attention(qc, kc, vc, causal=causal, split_keys=False)
+    o_s2, l_s2 = fa.attention(qc, kc, vc, causal=causal)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    parity.check(parity.compare(o_s, l_s, q, k, v, scale, causal), torch.float32)
+    parity.check(parity.compare(o_u, l_u, q, k, v, scale, causal), torch.float32)
+    assert (o_s - o_u).abs().max().item() <= 2e-6
+    assert (l_s - l_u).abs().max().item() <= 2e-6
+    assert torch.equal(o_s, o_s2) and torch.equal(l_s, l_s2)
+
+
+def test_workspace_size_and_rejection():
+    """No workspace for 16-bit inputs or grids that fill the GPU; a workspace
+    smaller than the reported size is rejected before anything is written."""
+    assert fa.fa_fwd_workspace_size(1, 1, 4096, 128, 0, fa.FA_DTYPE_BF16) == 0
+    assert fa.fa_fwd_workspace_size(4, 64, 1024, 64, 0, fa.FA_DTYPE_FP32) == 0
+    need = fa.fa_fwd_workspace_size(1, 1, 1024, 1024, 0, fa.FA_DTYPE_FP32)
+    assert need > 0
+    q = torch.randn(1, 1, 1024, 1024, device="cuda")
+    out = torch.full_like(q, 3.0)
+    lse = torch.full((1, 1, 1024), 3.0, device="cuda")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = fa.fa_fwd_ws(q.data_ptr(), q.data_ptr(), q.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      1, 1, 1024, 1024, 1 / 32, 0, fa.FA_DTYPE_FP32, ws.data_ptr(), need - 16,
+                      torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (out == 3.0).all() and (lse == 3.0).all()
+
+
 # ------------------------------------------------------------------ the five workloads, full size
 def _workload_rows(w):
     if w.B * w.H * w.N <= 1 << 16:  # workloads 1 and 2: every row
