@@ -46,6 +46,13 @@ def lib():
             ctypes.c_double, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_longlong,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_attn_bwd.restype = ctypes.c_int
+        L.oracle_attn_bwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+            ctypes.c_double, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.oracle_thread_count.restype = ctypes.c_int
         L.oracle_thread_count.argtypes = [ctypes.c_int]
         L.oracle_load.restype = ctypes.c_double
@@ -99,6 +106,44 @@ def attention(q, k, v, scale: float, causal: bool, threads: int = 0):
     B, H, N, d = q.shape
     o, lse = attn_rows(q, k, v, scale, causal, None, threads)
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+def attn_bwd(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=None,
+             threads: int = 0):
+    """Oracle gradients for selected rows (oracle_bwd.c).
+
+    q, k, v, dout: host tensors [B, H, N, d] of one dtype; dout = dL/dO.
+    q_rows / k_rows: flat row ids (b*H + h)*N + i; None means all rows.
+    Returns (dq [n_q, d], dk [n_k, d], dv [n_k, d]) float64 numpy arrays.
+    """
+    q, k, v, dout = _as_cpu(q), _as_cpu(k), _as_cpu(v), _as_cpu(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape) or q.dim() != 4:
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in _CODES:
+        raise ValueError("q, k, v, dout must share one supported dtype")
+    B, H, N, d = q.shape
+    qr = np.arange(B * H * N, dtype=np.int64) if q_rows is None else q_rows
+    kr = np.arange(B * H * N, dtype=np.int64) if k_rows is None else k_rows
+    qr = np.ascontiguousarray(np.asarray(qr, dtype=np.int64))
+    kr = np.ascontiguousarray(np.asarray(kr, dtype=np.int64))
+    dq = np.empty((qr.shape[0], d), dtype=np.float64)
+    dk = np.empty((kr.shape[0], d), dtype=np.float64)
+    dv = np.empty((kr.shape[0], d), dtype=np.float64)
+    rc = lib().oracle_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), _CODES[q.dtype],
+        B, H, N, d, float(scale), int(bool(causal)),
+        qr.ctypes.data, qr.shape[0], kr.ctypes.data, kr.shape[0],
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd failed with code {rc}")
+    return dq, dk, dv
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0):
+    """All rows; returns (dq, dk, dv) [B,H,N,d] float64 numpy arrays."""
+    B, H, N, d = q.shape
+    dq, dk, dv = attn_bwd(q, k, v, dout, scale, causal, None, None, threads)
+    return dq.reshape(B, H, N, d), dk.reshape(B, H, N, d), dv.reshape(B, H, N, d)
 
 
 def timed_attn_rows(q, k, v, scale, causal, rows, threads: int = 0):

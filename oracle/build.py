@@ -15,7 +15,7 @@ def build(verbose: bool = False) -> str:
     tmp = out + ".tmp"
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-pthread",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-           os.path.join(HERE, "oracle.c"), "-o", tmp, "-lm"]
+           os.path.join(HERE, "oracle.c"), os.path.join(HERE, "oracle_bwd.c"), "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -66,6 +66,22 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype,
                      const long long* rows, long long n_rows,
                      double* o_out, double* lse_out, int threads);
 
+/*
+ * oracle_attn_bwd -- gradients of the same attention (oracle_bwd.c):
+ * for an upstream gradient dout = dL/do ([B][H][N][d], type `dtype`), the
+ * gradients dL/dq of the query rows q_rows (flat ids (b*H + h)*N + i) and
+ * dL/dk, dL/dv of the key rows k_rows (flat ids (b*H + h)*N + j), fp64,
+ * written to dq_out [n_q][d], dk_out [n_k][d], dv_out [n_k][d].  Rows of one
+ * head need that head's per-row statistics, computed once per touched head.
+ * Returns 0, -1 (invalid argument, nothing written) or -2 (no memory).
+ */
+int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                    long long B, long long H, long long N, long long d,
+                    double scale, int causal,
+                    const long long* q_rows, long long n_q,
+                    const long long* k_rows, long long n_k,
+                    double* dq_out, double* dk_out, double* dv_out, int threads);
+
 /* Number of threads a call with `threads` would use. */
 int oracle_thread_count(int threads);
 
