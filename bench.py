@@ -40,12 +40,17 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (1 GPU)"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_FP32_TFLOPS = 157.3    # 256 CU x 256 FLOP/clk x 2.4 GHz, dense MFMA
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_29_amd", "csrc", "fa_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_29_amd", "csrc", n)
+               for n in ("fa_fwd.hip", "fa_device.h")]
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernels' sources (the file and the shared header)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_tag(w) -> str:
