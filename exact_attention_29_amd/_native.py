@@ -50,6 +50,14 @@ def library():
         L.fa_fwd_workspace_size.argtypes = [ctypes.c_int] * 6
         L.fa_fwd_supported.restype = ctypes.c_int
         L.fa_fwd_supported.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.c_void_p]
+        L.fa_bwd_workspace_size.restype = ctypes.c_size_t
+        L.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 6
+        L.fa_bwd_supported.restype = ctypes.c_int
+        L.fa_bwd_supported.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_status_string.argtypes = [ctypes.c_int]
         L.fa_version.restype = ctypes.c_int
@@ -148,3 +156,74 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
         raise FaError(st) if st == FA_ERR_HIP else ValueError(
             f"fa_fwd: {fa_status_string(st)} (status {st})")
     return out, lse
+
+
+def fa_bwd_supported(d: int, dtype: int, causal: int) -> bool:
+    return bool(library().fa_bwd_supported(int(d), int(dtype), int(causal)))
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int, causal: int, dtype: int) -> int:
+    """Workspace bytes fa_bwd needs (0: invalid or unsupported problem)."""
+    return int(library().fa_bwd_workspace_size(int(B), int(H), int(N), int(d), int(causal),
+                                               int(dtype)))
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+           B: int, H: int, N: int, d: int, scale: float, causal: int, dtype: int,
+           workspace: int, workspace_bytes: int, stream: int) -> int:
+    """The raw C entry point: integer device addresses in, status code out."""
+    return library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, ctypes.c_float(scale),
+                            int(causal), int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                  lse: torch.Tensor, dout: torch.Tensor, causal: bool = False,
+                  scale: float | None = None, dq: torch.Tensor | None = None,
+                  dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                  stream: torch.cuda.Stream | None = None):
+    """Gradients (dq, dk, dv) of the attention `attention()` computes.
+
+    q, k, v, o, dout: contiguous device tensors [B, H, N, d] of one 16-bit
+    dtype; o and lse as returned by attention() for the same arguments.  The
+    workspace comes from torch's allocator on `stream`.  Asynchronous on
+    `stream` (default: torch's current stream).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if q.dim() != 4 or q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"q must be [B, H, N, d] of a supported dtype, got {tuple(q.shape)} {q.dtype}")
+    B, H, N, d = q.shape
+    if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32 \
+            or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+        outs.append(t)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    code = _DTYPE_CODE[q.dtype]
+    with torch.cuda.device(q.device):
+        ws_bytes = fa_bwd_workspace_size(B, H, N, d, int(bool(causal)), code)
+        if ws_bytes == 0:
+            raise ValueError(f"fa_bwd: {fa_status_string(FA_ERR_UNSUPPORTED)} "
+                             f"(d={d}, dtype={q.dtype})")
+        with torch.cuda.stream(stream):
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                    B, H, N, d, float(scale), int(bool(causal)), code, ws.data_ptr(), ws_bytes,
+                    stream.cuda_stream)
+        ws.record_stream(stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd") if st == FA_ERR_HIP else ValueError(
+            f"fa_bwd: {fa_status_string(st)} (status {st})")
+    return tuple(outs)

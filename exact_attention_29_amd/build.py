@@ -13,7 +13,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("fa_fwd.hip", "fa_bwd.hip")]
 LIB = os.path.join(HERE, "libfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -1,0 +1,502 @@
+// fa_bwd.hip -- gradients of exact attention for MI355X (gfx950, CDNA4), C ABI in include/fa.h.
+//
+// For one head, with kept pairs (i, j) as in the forward pass (j <= i when
+// causal), s_ij = scale <q_i, k_j>, P_ij = exp(s_ij - lse_i) and an upstream
+// gradient dO:
+//   dV_j = sum_i P_ij dO_i,   dP_ij = <dO_i, v_j>,   delta_i = <dO_i, O_i>,
+//   dS_ij = P_ij (dP_ij - delta_i),
+//   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
+// P is never stored: every kernel recomputes it tile by tile from the row
+// log-sum-exp the forward pass wrote, the statistic a recomputing backward pass
+// keeps ("FlashAttention" (ai360xpert), section "Recomputation in the
+// backward pass"); delta_i = sum_j P_ij dP_ij reduces to <dO_i, O_i> because
+// O_i = sum_j P_ij v_j.
+//
+// Three kernels, no atomics, so the result is bitwise reproducible:
+//  * attn_bwd_prep: per row, nl = -lse/scale and nd = -delta (fp32) into the
+//    caller's workspace (rows padded to a multiple of 32 with zeros).  These
+//    are the initial accumulators of the score and dP products below, so
+//    S + nl and dP - delta come out of the matrix core directly.
+//  * attn_bwd_dkdv: a workgroup owns 128 keys (32 per wave) of one head, with
+//    its K and V rows held in registers, and streams 32-row tiles of Q and dO
+//    through double-buffered LDS.  S = Q K^T and dP = dO V^T are computed in
+//    (query x key) orientation, so each lane owns one key column and its P and
+//    dS values are already the B operand of dV^T += dO^T P and
+//    dK^T += Q^T dS; dO^T and Q^T are read out of the row-major LDS tiles with
+//    ds_read_b64_tr_b16 (the V^T reads of the forward kernel).
+//  * attn_bwd_dq: a workgroup owns 128 query rows (32 per wave) with Q and dO
+//    in registers and streams 64-key tiles of K and V, like the forward pass:
+//    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read by the
+//    transpose instruction.
+// All products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulators;
+// P and dS are rounded to the input type before their products.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "fa.h"
+#include "fa_device.h"
+
+namespace {
+
+using namespace fa_dev;
+
+// widen one 16-bit element to fp32
+template <class TT>
+__device__ __forceinline__ float widen(uint16_t x);
+template <>
+__device__ __forceinline__ float widen<Bf16>(uint16_t x) {
+  return __uint_as_float((unsigned)x << 16);
+}
+template <>
+__device__ __forceinline__ float widen<F16>(uint16_t x) {
+  return (float)__builtin_bit_cast(_Float16, x);
+}
+
+constexpr int kRowPad = 32;  // statistic rows are padded to this multiple
+
+// Byte offset, inside a row-major LDS tile (1 KB blocks of 16 rows x 4
+// sixteen-byte chunks; block (rg, cg) at (rg * D/32 + cg) KB, row ri chunk ci
+// at (ri * 4 + ci) * 16), of the 16 bytes lane (row, hf) supplies as the A
+// operand of a 32x32x16 product over head-dim chunk c: elements
+// [16c + 8hf, 16c + 8hf + 8) of row `row`.
+template <int D>
+__device__ __forceinline__ int rowmajor_a(int row, int hf, int c) {
+  const int t = 2 * c + hf;  // 16-byte chunk of the row
+  return ((row >> 4) * (D / 32) + (t >> 2)) * 1024 + ((row & 15) * 4 + (t & 3)) * 16;
+}
+
+// Lane part of the transpose read (ds_read_b64_tr_b16) of a row-major block:
+// two reads, at this offset and 512 bytes on, give lane (x = lane % 32,
+// h = lane / 32) rows {4h .. 4h+3} and {8 + 4h .. 8 + 4h + 3} of column x of
+// the block's 32 columns -- the A-operand order that matches a B operand
+// packed from accumulator registers 0..7 (rows 8(r/4) + 4h + r%4).
+__device__ __forceinline__ int tr_lane(int lane) {
+  const int i = lane & 15, grp = lane >> 4;
+  return (4 * (grp >> 1) + (i >> 2)) * 64 + (2 * (grp & 1) + ((i & 3) >> 1)) * 16 + 8 * (i & 1);
+}
+
+__device__ __forceinline__ u32x4 tr_read(const uint8_t* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 512));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+}
+
+// Store a wave's 32 x D transposed accumulator (block b, register r of lane
+// (x, h) = element [row x][32b + 8(r/4) + 4h + r%4]) times `mul`, rounded to
+// the element type, to rows row0 .. row0+31 of `out` (rows >= n_valid are
+// skipped).  Passes through the wave's own LDS area `stg` (32 rows x 144
+// bytes) so that each store writes whole 128-byte row segments.
+template <class TT, int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mul, uint8_t* stg,
+                                           uint16_t* out, int row0, int n_valid, int lane) {
+  constexpr int kRow = 144;
+  const int x = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < D / 64; ++r) {
+#pragma unroll
+    for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc[2 * r + bl];
+        const u32x2 w = {TT::pack(a[4 * g + 0] * mul, a[4 * g + 1] * mul),
+                         TT::pack(a[4 * g + 2] * mul, a[4 * g + 3] * mul)};
+        *(u32x2*)(stg + x * kRow + 2 * (32 * bl + 8 * g + 4 * h)) = w;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const u32x4 v = *(const u32x4*)(stg + row * kRow + 16 * (lane & 7));
+      if (row0 + row < n_valid) *(u32x4*)(out + (size_t)(row0 + row) * D + 64 * r + 8 * (lane & 7)) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics.  TPR = D/8 threads per row, 8 elements each.
+template <class TT, int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep(const uint16_t* __restrict__ O,
+                                                     const uint16_t* __restrict__ dO,
+                                                     const float* __restrict__ LSE,
+                                                     float* __restrict__ NL, float* __restrict__ ND,
+                                                     int N, int n_pad, long long padded_rows,
+                                                     float inv_scale) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const int t = threadIdx.x % TPR;
+  const long long prow = (long long)blockIdx.x * RPB + threadIdx.x / TPR;  // padded row id
+  if (prow >= padded_rows) return;  // whole rows only: TPR divides the wave
+  const long long bh = prow / n_pad;
+  const int i = (int)(prow % n_pad);
+  float acc = 0.f, nl = 0.f;
+  if (i < N) {
+    const size_t row = (size_t)bh * N + i;
+    const u32x4 a = *(const u32x4*)(O + row * D + 8 * t);
+    const u32x4 b = *(const u32x4*)(dO + row * D + 8 * t);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(widen<TT>((uint16_t)(a[w] & 0xffffu)), widen<TT>((uint16_t)(b[w] & 0xffffu)), acc);
+      acc = fmaf(widen<TT>((uint16_t)(a[w] >> 16)), widen<TT>((uint16_t)(b[w] >> 16)), acc);
+    }
+    nl = -LSE[row] * inv_scale;
+  }
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, TPR);
+  if (t == 0) {
+    NL[prow] = nl;
+    ND[prow] = -acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  NW = 4 waves x 32 keys; query tiles of 32 rows.
+//
+// Register layouts (D = head dim; lane (x = lane % 32, h = lane / 32)):
+//   K and V rows (whole kernel): lane holds row[key0 + x][16c + 8h .. +7]
+//     for c = 0..D/16-1, the B operand of S = Q K^T and dP = dO V^T.
+//   S, dP (accumulators, 32 queries x 32 keys): register r of lane (x, h) is
+//     query 8(r/4) + 4h + r%4 of the tile and key key0 + x.
+//   dK^T, dV^T (accumulators): block b, register r of lane (x, h) is
+//     d-column 32b + 8(r/4) + 4h + r%4 of key key0 + x.
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_pad, int n_kblocks,
+    int total, float scale) {
+  constexpr int NW = 4, BQ = 32, CG = D / 32;
+  constexpr int TBLK = 2 * CG, TB = TBLK * 1024;  // 1 KB blocks and bytes of one 32-row tile
+  static_assert(TBLK % NW == 0, "tile blocks split evenly over the waves");
+  // [buffer][Q tile, dO tile, nl of its rows (1 KB), nd of its rows (1 KB)];
+  // the epilogue reuses it as the waves' output staging
+  constexpr int BUF = 2 * TB + 2048;
+  constexpr int SMEM = 2 * BUF > NW * 32 * 144 ? 2 * BUF : NW * 32 * 144;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = lane & 31, h = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, total);
+  const int bh = item / n_kblocks;
+  const int kb = item % n_kblocks;  // ascending: causal key blocks near 0 see the most queries
+  const size_t head = (size_t)bh * N * D;
+  const int kw = kb * 32 * NW + 32 * wave;  // this wave's first key
+  const int my_k = kw + x;
+
+  u32x4 kf[D / 16], vf[D / 16];
+  {
+    const uint16_t* kr = K + head + (size_t)my_k * D + 8 * h;
+    const uint16_t* vr = V + head + (size_t)my_k * D + 8 * h;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      kf[c] = my_k < N ? *(const u32x4*)(kr + 16 * c) : u32x4{0, 0, 0, 0};
+      vf[c] = my_k < N ? *(const u32x4*)(vr + 16 * c) : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) dk[b] = dv[b] = f32x16{};
+  const float c2 = scale * kLog2e;
+  const float* nl_row = NL + (size_t)bh * n_pad;
+  const float* nd_row = ND + (size_t)bh * n_pad;
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? kb * NW : 0;  // first tile holding a query >= the block's first key
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto load = [&](int t, int buf) {
+    const int r0 = t * BQ;
+    const unsigned base = lds0 + buf * BUF;
+    // the rows' statistics: one wave-wide load each, 128 bytes of data (the
+    // rest of the 1 KB reads past the descriptor's end and lands as zeros)
+    if (wave < 2) {
+      const float* src = (wave == 0 ? nl_row : nd_row) + r0;
+      dma16(buffer_desc(src, BQ * 4), base + 2 * TB + 1024 * wave, lane * 16);
+    }
+    const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * D, (unsigned)(N - r0) * D * 2);
+    const u32x4 dd = buffer_desc(dO + head + (size_t)r0 * D, (unsigned)(N - r0) * D * 2);
+#pragma unroll
+    for (int i = 0; i < TBLK / NW; ++i) {
+      const int blk = wave + i * NW;
+      const int el = TileLayout<D>::v_src(blk, lane);
+      dma16(dq, base + blk * 1024, el * 2);
+      dma16(dd, base + TB + blk * 1024, el * 2);
+    }
+  };
+  const int trl = tr_lane(lane);
+
+  if (qt0 < nqt) load(qt0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  for (int t = qt0; t < nqt; ++t) {
+    const int buf = (t - qt0) & 1;
+    if (t + 1 < nqt) load(t + 1, buf ^ 1);
+    const int q0 = t * BQ;
+    // queries q0..q0+31 all precede this wave's keys: nothing kept
+    if (!CAUSAL || q0 + BQ - 1 >= kw) {
+      const uint8_t* qt = smem + buf * BUF;
+      const uint8_t* dt = qt + TB;
+      f32x16 s, dp;
+      // initial accumulators: -lse/scale and -delta of the tile's rows
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 a = *(const f32x4*)(qt + 2 * TB + 4 * (8 * g + 4 * h));
+        const f32x4 b = *(const f32x4*)(qt + 2 * TB + 1024 + 4 * (8 * g + 4 * h));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[4 * g + e] = a[e];
+          dp[4 * g + e] = b[e];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        s = TT::mma(*(const u32x4*)(qt + rowmajor_a<D>(x, h, c)), kf[c], s);
+        dp = TT::mma(*(const u32x4*)(dt + rowmajor_a<D>(x, h, c)), vf[c], dp);
+      }
+      // P = exp(scale s - lse); dS = P (dP - delta); the diagonal tile keeps
+      // key <= query only
+      const bool diag = CAUSAL && q0 < kw + 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(s[r] * c2);
+        if (diag && my_k > q0 + 8 * (r >> 2) + 4 * h + (r & 3)) p = 0.f;
+        s[r] = p;
+        dp[r] = p * dp[r];
+      }
+      u32x4 pf[2], df[2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int r0 = 8 * kc;
+        pf[kc] = u32x4{TT::pack(s[r0 + 0], s[r0 + 1]), TT::pack(s[r0 + 2], s[r0 + 3]),
+                       TT::pack(s[r0 + 4], s[r0 + 5]), TT::pack(s[r0 + 6], s[r0 + 7])};
+        df[kc] = u32x4{TT::pack(dp[r0 + 0], dp[r0 + 1]), TT::pack(dp[r0 + 2], dp[r0 + 3]),
+                       TT::pack(dp[r0 + 4], dp[r0 + 5]), TT::pack(dp[r0 + 6], dp[r0 + 7])};
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          const int off = (kc * CG + b) * 1024 + trl;
+          dv[b] = TT::mma(tr_read(dt + off), pf[kc], dv[b]);
+          dk[b] = TT::mma(tr_read(qt + off), df[kc], dk[b]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+  // the tile buffers are free after the last barrier
+  uint8_t* stg = smem + wave * 32 * 144;
+  store_rows<TT, D>(dv, 1.f, stg, dV + head, kw, N, lane);
+  store_rows<TT, D>(dk, scale, stg, dK + head, kw, N, lane);
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  NW = 4 waves x 32 queries; key tiles of 64 keys: K row-major (read as
+// rows and, transposed, as K^T), V chunk-major (read as rows).
+//
+// Register layouts (lane (x, h)):
+//   Q and dO rows (whole kernel): row[q_first + x][16c + 8h .. +7], the B
+//     operands of S^T = K Q^T and dP^T = V dO^T.
+//   S^T, dP^T (accumulators, per 32-key block): register r of lane (x, h) is
+//     key 8(r/4) + 4h + r%4 of the block and query q_first + x.
+//   dQ^T (accumulator): block b, register r is d-column 32b + 8(r/4) + 4h + r%4.
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
+    uint16_t* __restrict__ dQ, int N, int n_pad, int n_qblocks, int total, float scale) {
+  constexpr int NW = 4, BR = 32 * NW, BC = 64, CG = D / 32;
+  using LY = TileLayout<D>;
+  constexpr int TB = LY::BYTES;
+  static_assert(LY::BLOCKS % NW == 0, "tile blocks split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TB];  // [buffer][K, V]
+  static_assert(NW * 32 * 144 <= 2 * 2 * TB, "output staging fits the tile buffers");
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = lane & 31, h = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, total);
+  const int bh = item / n_qblocks;
+  int qb = item % n_qblocks;
+  if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
+  const size_t head = (size_t)bh * N * D;
+  const int q_first = qb * BR + 32 * wave;
+  const int my_q = q_first + x;
+
+  u32x4 qf[D / 16], of[D / 16];
+  {
+    const uint16_t* qr = Q + head + (size_t)my_q * D + 8 * h;
+    const uint16_t* dr = dO + head + (size_t)my_q * D + 8 * h;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      qf[c] = my_q < N ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
+      of[c] = my_q < N ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
+    }
+  }
+  const float c2 = scale * kLog2e;
+  // (rows past N are never stored; the block's last rows may lie past the padding)
+  const float nl2 = my_q < N ? NL[(size_t)bh * n_pad + my_q] * c2 : 0.f;
+  const float nd = my_q < N ? ND[(size_t)bh * n_pad + my_q] : 0.f;
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) dq[b] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
+  const int T = (kv_end + BC - 1) / BC;
+  const int my_T = CAUSAL ? min(T, (q_first + 31) / BC + 1) : T;
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto load = [&](int j, int buf) {
+    const int k0 = j * BC;
+    const unsigned base = lds0 + buf * 2 * TB;
+    const unsigned bytes = (unsigned)(N - k0) * D * 2;
+    dma_tile<D, true, NW>(buffer_desc(K + head + (size_t)k0 * D, bytes), base, 0, wave, lane);
+    dma_tile<D, false, NW>(buffer_desc(V + head + (size_t)k0 * D, bytes), base + TB, 0, wave, lane);
+  };
+  const int trl = tr_lane(lane);
+  // A operand of V (chunk-major block layout), as in the forward kernel
+  const int v_lane = (x >> 4) * CG * 1024 + (h * 16 + (x & 15)) * 16;
+
+  if (T > 0) load(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  for (int j = 0; j < T; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < T) load(j + 1, buf ^ 1);
+    if (j < my_T) {
+      const uint8_t* kt = smem + buf * 2 * TB;
+      const uint8_t* vt = kt + TB;
+      const int k0 = j * BC;
+      // keys past the row (causal) or past N get no weight: a key past N has
+      // zero K and V rows, but its weight exp(-lse) need not be finite
+      const bool masked = (CAUSAL && k0 + BC - 1 > q_first) || (k0 + BC > N);
+      const int lim = min(CAUSAL ? my_q : N - 1, N - 1);
+#pragma unroll
+      for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
+        f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          st = TT::mma(*(const u32x4*)(kt + rowmajor_a<D>(32 * kb2 + x, h, c)), qf[c], st);
+          dpt = TT::mma(*(const u32x4*)(vt + v_lane + (2 * kb2 * CG + (c >> 1)) * 1024 + (c & 1) * 512),
+                        of[c], dpt);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(st[r], c2, nl2));
+          if (masked && k0 + 32 * kb2 + 8 * (r >> 2) + 4 * h + (r & 3) > lim) p = 0.f;
+          st[r] = p * (dpt[r] + nd);
+        }
+        u32x4 df[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const int r0 = 8 * kc;
+          df[kc] = u32x4{TT::pack(st[r0 + 0], st[r0 + 1]), TT::pack(st[r0 + 2], st[r0 + 3]),
+                         TT::pack(st[r0 + 4], st[r0 + 5]), TT::pack(st[r0 + 6], st[r0 + 7])};
+        }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b)
+            dq[b] = TT::mma(tr_read(kt + ((2 * kb2 + kc) * CG + b) * 1024 + trl), df[kc], dq[b]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+  uint8_t* stg = smem + wave * 32 * 144;
+  store_rows<TT, D>(dq, scale, stg, dQ + head, q_first, N, lane);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+size_t padded_rows(long long BH, int N) { return (size_t)BH * (size_t)((N + kRowPad - 1) / kRowPad * kRowPad); }
+
+template <class TT, int D>
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int BH, int N, float scale,
+                      bool causal, float* ws, hipStream_t st) {
+  const int n_pad = (N + kRowPad - 1) / kRowPad * kRowPad;
+  const long long prow = (long long)BH * n_pad;
+  float* nl = ws;
+  float* nd = ws + prow;
+  {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((attn_bwd_prep<TT, D>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256), 0,
+                       st, (const uint16_t*)o, (const uint16_t*)dout, lse, nl, nd, N, n_pad, prow,
+                       1.f / scale);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  const int nkb = (N + 127) / 128, nqb = (N + 127) / 128;
+  const int tk = nkb * BH, tq = nqb * BH;
+  if (causal) {
+    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, true>), dim3(tk), dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
+                       (uint16_t*)dk, (uint16_t*)dv, N, n_pad, nkb, tk, scale);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq<TT, D, true>), dim3(tq), dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
+                       (uint16_t*)dq, N, n_pad, nqb, tq, scale);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, false>), dim3(tk), dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
+                       (uint16_t*)dk, (uint16_t*)dv, N, n_pad, nkb, tk, scale);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq<TT, D, false>), dim3(tq), dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
+                       (uint16_t*)dq, N, n_pad, nqb, tq, scale);
+  }
+  return hipGetLastError();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_supported(int d, int dtype, int causal) {
+  if (causal != 0 && causal != 1) return 0;
+  return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16) && (d == 64 || d == 128);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0 || !fa_bwd_supported(d, dtype, causal)) return 0;
+  if ((long long)B * H > (1LL << 24) || (long long)B * H * N > 0x7fffffffLL) return 0;
+  return 2 * padded_rows((long long)B * H, N) * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 24) || BH * N > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (((long long)N + 127) / 128 * BH > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
+    return FA_ERR_UNSUPPORTED;
+  if (!fa_bwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
+  // per-head byte offsets (plus one tile of slack) fit the 32-bit buffer offsets
+  if (((long long)N + 128) * d * 2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, causal, dtype))
+    return FA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv,
+                        (const void*)workspace})
+    if (!aligned16(p)) return FA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  const int bh = (int)BH;
+  float* ws = (float*)workspace;
+  hipError_t e;
+  if (dtype == FA_DTYPE_BF16)
+    e = d == 64 ? launch_bwd<Bf16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st)
+                : launch_bwd<Bf16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st);
+  else
+    e = d == 64 ? launch_bwd<F16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st)
+                : launch_bwd<F16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

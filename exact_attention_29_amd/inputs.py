@@ -124,3 +124,13 @@ def peaked_key_rows(w: Workload):
         for h in range(w.H):
             out[(b, h)] = torch.randperm(w.N, generator=g)[:n_pk]
     return out
+
+
+def make_dout(B: int, H: int, N: int, d: int, dtype: str, seed: int):
+    """Host upstream gradient dL/dO [B, H, N, d]: i.i.d. N(0, 1) from its own
+    generator seeded with `seed`, cast to `dtype` (round to nearest even)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    x = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    td = _DTYPES[dtype]
+    return x.to(td) if td != torch.float32 else x

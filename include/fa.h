@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) FlashAttention forward library, libfa.so.
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention library, libfa.so: the
+ * forward pass and its gradients.
  *
  * The one operation is exact scaled dot-product attention,
  *     O = softmax(scale * Q K^T) V          (softmax over each query row),
@@ -126,6 +127,58 @@ size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
 int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for this
+ * problem: two fp32 row statistics per (batch, head, row), rows padded to a
+ * multiple of 32.  0 for invalid or unsupported arguments.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
+
+/*
+ * fa_bwd -- gradients of the attention fa_fwd computes, on one GPU.
+ *
+ * Given the forward inputs q, k, v, its outputs o and lse, and dout = dL/dO,
+ * writes for every (batch, head), with P_ij = exp(scale q_i.k_j - lse_i) over
+ * the kept pairs (j <= i when causal) and delta_i = dout_i . o_i:
+ *   dv_j = sum_i P_ij dout_i
+ *   dq_i = scale sum_j P_ij (dout_i . v_j - delta_i) k_j
+ *   dk_j = scale sum_i P_ij (dout_i . v_j - delta_i) q_i
+ * -- the chain rule through O = P V and the row softmax, with P recomputed
+ * tile by tile from the stored log-sum-exp instead of being kept ("FlashAttention"
+ * (ai360xpert), section "Recomputation in the backward pass"; the softmax and
+ * attention definitions of "The Details of Flash Attention", eqs. 1-4).
+ *
+ *   q, k, v, o, dout : device pointers, contiguous [B][H][N][d] of `dtype`;
+ *                      o and lse as written by fa_fwd for the same q, k, v,
+ *                      scale and causal (any o, lse are accepted; the
+ *                      formulas above use them as given).
+ *   lse             : device pointer, [B][H][N] fp32 (natural log).
+ *   dq, dk, dv      : device pointers, [B][H][N][d] of `dtype`, written
+ *                     (rounded from fp32 to nearest even).  They must not
+ *                     overlap the inputs or each other.
+ *   B, H, N, d, scale, causal, dtype : as for fa_fwd.  Supported: bf16 and
+ *                     fp16 with d = 64 or 128.
+ *   workspace       : device pointer, 16-byte aligned, at least
+ *                     fa_bwd_workspace_size(...) bytes (else
+ *                     FA_ERR_INVALID_ARG); contents on entry ignored, on
+ *                     return undefined; must stay allocated until the stream
+ *                     has run the call.
+ *   stream          : a hipStream_t passed as void*; NULL = the null stream.
+ *
+ * Asynchronous on `stream`; allocates nothing.  Every argument is checked
+ * before any HIP call; on an error code nothing is launched and no output is
+ * written.  Arithmetic: products of 16-bit operands accumulate in fp32; P and
+ * dS are rounded to the element type before their products.  No atomics: the
+ * result is bitwise reproducible run to run.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream);
+
+/* 1 when fa_bwd has kernels for (d, dtype, causal), else 0. */
+int fa_bwd_supported(int d, int dtype, int causal);
 
 /* 1 when fa_fwd has a kernel for (d, dtype, causal), else 0. */
 int fa_fwd_supported(int d, int dtype, int causal);

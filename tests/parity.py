@@ -18,20 +18,31 @@ TOL = {
 }
 
 
+# Gradient tolerances, relative to the largest element of the reference
+# gradient tensor (its natural scale; see the derivation in the gradient tests).
+TOL_BWD = {
+    torch.bfloat16: dict(max_rel=2e-2, mean_rel=2e-3),
+    torch.float16: dict(max_rel=4e-3, mean_rel=4e-4),
+}
+
+
 def sample_rows(B, H, N, seed, per_head_random=64, full_tile_heads=None, tile=128,
-                extra=None):
+                extra=None, heads=None):
     """Stratified, seeded sample of flat row ids (b*H + h)*N + i.
 
     Per head: the first and last rows, both sides of the first tile boundary,
     the middle, `per_head_random` uniform rows, and -- for the heads in
     `full_tile_heads` (default: all) -- every row of one random query tile.
-    `extra` maps (b, h) -> iterable of positions to add.
+    `extra` maps (b, h) -> iterable of positions to add.  `heads` (default:
+    all) restricts the sample to those (b, h).
     """
     rng = np.random.default_rng(seed)
     rows = []
     n_tiles = (N + tile - 1) // tile
     for b in range(B):
         for h in range(H):
+            if heads is not None and (b, h) not in heads:
+                continue
             base = (b * H + h) * N
             pos = {0, 1, tile - 1, tile, N // 2, N - 2, N - 1}
             pos.update(rng.integers(0, N, size=per_head_random).tolist())

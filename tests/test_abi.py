@@ -97,3 +97,46 @@ def test_python_wrapper_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attention(x, x, x)
+
+
+# ------------------------------------------------------------------ gradients
+def call_bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             B=1, H=1, N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_DTYPE_BF16,
+             ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                     a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                     a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_bwd_supported_table_and_workspace_size():
+    for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16):
+        for d in (64, 128):
+            assert fa.fa_bwd_supported(d, dt, 0) and fa.fa_bwd_supported(d, dt, 1)
+        assert not fa.fa_bwd_supported(256, dt, 0)
+    assert not fa.fa_bwd_supported(64, fa.FA_DTYPE_FP32, 0)
+    assert not fa.fa_bwd_supported(64, fa.FA_DTYPE_BF16, 2)
+    # two fp32 statistics per row, rows padded to a multiple of 32
+    assert fa.fa_bwd_workspace_size(2, 3, 100, 64, 1, fa.FA_DTYPE_BF16) == 2 * 6 * 128 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 32, 128, 0, fa.FA_DTYPE_FP16) == 2 * 32 * 4
+    assert fa.fa_bwd_workspace_size(0, 1, 16, 64, 0, fa.FA_DTYPE_BF16) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 16, 96, 0, fa.FA_DTYPE_BF16) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 16, 64, 0, fa.FA_DTYPE_FP32) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(o=None), dict(dout=None), dict(lse=None), dict(dq=None), dict(dv=None),
+    dict(B=0), dict(N=-3), dict(d=0), dict(causal=2), dict(scale=0.0), dict(scale=float("nan")),
+    dict(B=1 << 20, H=1 << 20), dict(ws=None), dict(ws_bytes=16),
+])
+def test_bwd_invalid_arguments(kw):
+    assert call_bwd(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d=96), dict(dtype=fa.FA_DTYPE_FP32), dict(dtype=9), dict(q=FAKE + 8),
+    dict(dk=FAKE + 2), dict(ws=FAKE + 4),
+])
+def test_bwd_unsupported_configurations(kw):
+    assert call_bwd(**kw) == fa.FA_ERR_UNSUPPORTED
