@@ -1,10 +1,15 @@
 """Benchmark: attention forward TFLOPS and fraction of the MI355X bf16 MFMA peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--pass fwd|bwd]
 
 A step is one fa_fwd call (the whole forward pass) over one batch of the
 workload, inputs already resident in device memory.  W untimed steps, then K
 timed steps between two synchronizations; one JSON line on stdout.
+
+--pass bwd times the gradients instead: one fa_bwd call (its three kernels)
+per step, with the forward outputs O, lse and a seeded dL/dO resident, counted
+as 10*B*H*N^2*d algorithmic FLOPs (halved for causal): the five products
+S = Q K^T, dV = P^T dO, dP = dO V^T, dQ = dS K and dK = dS^T Q.
 
 Extra objects on the line:
   roofline     -- the kernel's achieved TFLOP/s (algorithmic FLOPs per launch
@@ -38,38 +43,43 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (1 GPU)"
+METRIC_BWD = "attention bwd TFLOPS and % of MI355X bf16 MFMA peak (1 GPU)"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_FP32_TFLOPS = 157.3    # 256 CU x 256 FLOP/clk x 2.4 GHz, dense MFMA
-KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_29_amd", "csrc", n)
-               for n in ("fa_fwd.hip", "fa_device.h")]
+KERNEL_SRCS = {p: [os.path.join(ROOT, "exact_attention_29_amd", "csrc", n)
+                   for n in (f"fa_{p}.hip", "fa_device.h")] for p in ("fwd", "bwd")}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the forward kernels' sources (the file and the shared header)."""
+def kernel_source_hash(pass_: str = "fwd") -> str:
+    """Hash of one pass's kernel sources (its file and the shared header)."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[pass_]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def kernel_tag(w) -> str:
-    """Name of the kernel instance a workload runs, as used by profiles/."""
-    kern = "attn_fwd_f32" if w.dtype == "fp32" else "attn_fwd_sp"
+def kernel_tag(w, pass_: str = "fwd") -> str:
+    """Name of what a workload's timed step runs, as used by profiles/: the
+    forward kernel instance, or the whole gradient call."""
+    if pass_ == "bwd":
+        kern = "fa_bwd"  # the whole call: row statistics, dK/dV and dQ kernels
+    else:
+        kern = "attn_fwd_f32" if w.dtype == "fp32" else "attn_fwd_sp"
     mask = "causal" if w.causal else "noncausal"
     return f"{kern}_{w.dtype}_{mask}_B{w.B}_H{w.H}_N{w.N}_d{w.d}"
 
 
-def read_traffic(w):
+def read_traffic(w, pass_: str = "fwd"):
     """HBM bytes per launch from profiles/<kernel tag>.traffic.md, if that
     summary was taken from the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_tag(w)}.traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag(w, pass_)}.traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
     b = re.search(r"HBM bytes per launch:\s*`?([0-9.eE+]+)", text)
-    if not h or not b or h.group(1) != kernel_source_hash():
+    if not h or not b or h.group(1) != kernel_source_hash(pass_):
         return None
     return float(b.group(1))
 
@@ -127,12 +137,44 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s: float, seed: int = 0):
     }, parity
 
 
+def cpu_baseline_bwd(w, q, k, v, g, dq, dk, dv, target_s: float):
+    """Time the gradient oracle on whole heads of the workload (as many as fit
+    about target_s, at least one), in the same algorithmic-FLOP unit."""
+    import oracle
+
+    B, H, N, d = w.B, w.H, w.N, w.d
+    per_head = 10.0 * N * N * d / (2.0 if w.causal else 1.0)
+    heads, secs, errs = 0, 0.0, []
+    nt = oracle.thread_count(0)
+    for idx in range(B * H):
+        b, h = divmod(idx, H)
+        rows = np.arange(idx * N, (idx + 1) * N, dtype=np.int64)
+        t0 = time.perf_counter()
+        rq, rk, rv = oracle.attn_bwd(q, k, v, g, w.scale, w.causal, rows, rows)
+        secs += time.perf_counter() - t0
+        heads += 1
+        for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+            x = got[b, h].double().cpu().numpy()
+            errs.append(float(np.abs(x - ref).max()) / max(float(np.abs(ref).max()), 1e-2))
+        if secs >= target_s:
+            break
+    return {
+        "value": heads * per_head / secs / 1e12, "unit": "TFLOPS", "cores": int(nt),
+        "kind": "oracle",
+        "sample": (f"all rows of {heads} of {B * H} heads of the workload (dq, dk, dv), FLOPs "
+                   f"counted 10*N^2*d per head{' halved for causal' if w.causal else ''}; "
+                   f"{secs:.1f} s of oracle time"),
+        "seconds": secs, "gflop": heads * per_head / 1e9,
+    }, {"heads": heads, "max_abs_over_max_ref": max(errs)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
@@ -151,18 +193,36 @@ def main() -> int:
         return 0
 
     import exact_attention_29_amd as fa
-    from exact_attention_29_amd.inputs import WORKLOADS, workload_inputs
+    from exact_attention_29_amd.inputs import WORKLOADS, make_dout, workload_inputs
 
     w = WORKLOADS[args.workload]
+    bwd = args.pass_ == "bwd"
+    if bwd and not fa.fa_bwd_supported(w.d, fa.FA_DTYPE_BF16 if w.dtype == "bf16" else
+                                       fa.FA_DTYPE_FP16 if w.dtype == "fp16" else fa.FA_DTYPE_FP32,
+                                       int(w.causal)):
+        print(f"no gradient kernels for workload {args.workload} ({w.dtype}, d={w.d})",
+              file=sys.stderr)
+        return 1
     q_h, k_h, v_h = workload_inputs(w)
     dev = torch.device("cuda:0")
     q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    def step():
+    if bwd:
+        g_h = make_dout(w.B, w.H, w.N, w.d, w.dtype, 100 + args.workload)
+        g = g_h.to(dev)
         fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+        def step():
+            fa.attention_bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
+                             dv=dv, stream=stream)
+        flops = 2.5 * w.flops
+    else:
+        def step():
+            fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        flops = w.flops
 
     for _ in range(args.warmup):
         step()
@@ -182,27 +242,36 @@ def main() -> int:
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     ms_per_step = wall * 1e3 / args.steps
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype in ("bf16", "fp16") else PEAK_FP32_TFLOPS
-    traffic = read_traffic(w)
-    algo_bytes = (4 * w.B * w.H * w.N * w.d * (2 if w.dtype != "fp32" else 4)
-                  + 4 * w.B * w.H * w.N)
+    traffic = read_traffic(w, args.pass_)
+    elem = 2 if w.dtype != "fp32" else 4
+    if bwd:  # read Q, K, V, O, dO, lse; write dQ, dK, dV
+        algo_bytes = 8 * w.B * w.H * w.N * w.d * elem + 4 * w.B * w.H * w.N
+    else:    # read Q, K, V; write O, lse
+        algo_bytes = 4 * w.B * w.H * w.N * w.d * elem + 4 * w.B * w.H * w.N
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "metric": METRIC_BWD if bwd else METRIC, "value": round(value, 2), "unit": "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) per the workload recipe)",
-        "config": {**w.as_dict(), "flops_per_step": w.flops,
+        "config": {**w.as_dict(), "pass": args.pass_, "flops_per_step": flops,
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 4),
                      "algorithmic_bytes": algo_bytes,
-                     "kernel_source_sha256_16": kernel_source_hash()},
+                     "kernel_source_sha256_16": kernel_source_hash(args.pass_)},
     }
+    if bwd:
+        line["roofline"]["timed"] = "whole fa_bwd call (row statistics, dK/dV and dQ kernels)"
     if not args.no_cpu_baseline:
-        cb, par = cpu_baseline(w, q_h, k_h, v_h, o, lse, args.cpu_seconds)
+        if bwd:
+            cb, par = cpu_baseline_bwd(w, q_h, k_h, v_h, g_h, dq, dk, dv, args.cpu_seconds)
+        else:
+            cb, par = cpu_baseline(w, q_h, k_h, v_h, o, lse, args.cpu_seconds)
         line["cpu_baseline"] = cb
         line["parity_on_cpu_sample"] = par
     print(json.dumps(line), flush=True)
