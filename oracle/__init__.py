@@ -46,6 +46,13 @@ def lib():
             ctypes.c_double, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_longlong,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_attn_rows_ex.restype = ctypes.c_int
+        L.oracle_attn_rows_ex.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+            ctypes.c_longlong, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.oracle_attn_bwd.restype = ctypes.c_int
         L.oracle_attn_bwd.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -106,6 +113,50 @@ def attention(q, k, v, scale: float, causal: bool, threads: int = 0):
     B, H, N, d = q.shape
     o, lse = attn_rows(q, k, v, scale, causal, None, threads)
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+def attn_rows_ex(q, k, v, scale: float, causal: bool, rows=None, k_len=None, threads: int = 0):
+    """Oracle attention for query and key sequences of different lengths,
+    with optional per-batch valid key counts (oracle.h, oracle_attn_rows_ex).
+
+    q: host [B, H, Nq, d]; k, v: host [B, H, Nk, d], one dtype.  rows: flat
+    query-row ids (b*H + h)*Nq + i (None: all).  k_len: B valid key counts or
+    None.  Returns (o [n_rows, d], lse [n_rows]) float64 numpy arrays; rows
+    with no kept key give o = 0, lse = -inf.
+    """
+    q, k, v = _as_cpu(q), _as_cpu(k), _as_cpu(v)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _CODES:
+        raise ValueError(f"unsupported dtype combination {q.dtype}/{k.dtype}/{v.dtype}")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if rows is None:
+        rows = np.arange(B * H * Nq, dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    kl = None
+    if k_len is not None:
+        kl = np.ascontiguousarray(np.asarray(k_len, dtype=np.int64))
+        if kl.shape != (B,):
+            raise ValueError("k_len must hold one count per batch")
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib().oracle_attn_rows_ex(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _CODES[q.dtype], B, H, Nq, Nk, d,
+        float(scale), int(bool(causal)), None if kl is None else kl.ctypes.data,
+        rows.ctypes.data, n, o.ctypes.data, lse.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_rows_ex failed with code {rc}")
+    return o, lse
+
+
+def attention_ex(q, k, v, scale: float, causal: bool, k_len=None, threads: int = 0):
+    """All rows of attn_rows_ex; returns (o [B,H,Nq,d], lse [B,H,Nq])."""
+    B, H, Nq, d = q.shape
+    o, lse = attn_rows_ex(q, k, v, scale, causal, None, k_len, threads)
+    return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
 
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=None,

@@ -58,34 +58,49 @@ int oracle_thread_count(int threads) {
 typedef struct {
   const void *q, *k, *v;
   int dtype;
-  long long N, d;
+  long long H, Nq, Nk, d;
   double scale;
   int causal;
+  const long long* k_len; /* per-batch valid keys, or NULL (all Nk) */
   const long long* rows;
   long long n_rows;
   double *o_out, *lse_out;
   long long next; /* shared work counter, advanced atomically */
 } job_t;
 
-/* One query row r = (b*H + h)*N + i, three passes.  `qrow` (d doubles) and
- * `s` (N doubles) are this thread's scratch: s holds the row's scaled scores,
- * so passes 2 and 3 reuse the dot products of the score step. */
+/* One query row r = (b*H + h)*Nq + i, three passes.  `qrow` (d doubles) and
+ * `s` (Nk doubles) are this thread's scratch: s holds the row's scaled scores,
+ * so passes 2 and 3 reuse the dot products of the score step.
+ * The kept keys J_i are a prefix 0 .. nkeys-1 of the head's keys: keys below
+ * the batch's valid length L, and, when causal, at most i + (L - Nq). */
 static void one_row(const job_t* jb, long long r, double* qrow, double* s,
                     double* o, double* lse) {
-  const long long N = jb->N, d = jb->d;
-  const long long head = r / N;                  /* b*H + h */
-  const long long i = r % N;                     /* query position */
-  const long long base = head * N * d;           /* start of this head */
-  const long long nkeys = jb->causal ? i + 1 : N; /* |J_i| */
+  const long long Nq = jb->Nq, Nk = jb->Nk, d = jb->d;
+  const long long head = r / Nq;                 /* b*H + h */
+  const long long i = r % Nq;                    /* query position */
+  const long long b = head / jb->H;
+  const long long qbase = head * Nq * d;         /* this head's query rows */
+  const long long kbase = head * Nk * d;         /* this head's key / value rows */
+  long long L = jb->k_len ? jb->k_len[b] : Nk;   /* valid keys of this batch */
+  if (L < 0) L = 0;
+  if (L > Nk) L = Nk;
+  long long nkeys = L;                           /* |J_i| */
+  if (jb->causal && i + (L - Nq) + 1 < nkeys) nkeys = i + (L - Nq) + 1;
+  if (nkeys < 0) nkeys = 0;
 
+  for (long long c = 0; c < d; ++c) o[c] = 0.0;
+  if (nkeys == 0) { /* no kept key: the empty sum, o = 0 and lse = ln 0 */
+    *lse = -INFINITY;
+    return;
+  }
   for (long long c = 0; c < d; ++c)
-    qrow[c] = oracle_load(jb->q, jb->dtype, base + i * d + c);
+    qrow[c] = oracle_load(jb->q, jb->dtype, qbase + i * d + c);
 
   /* scores s_j = scale * <q_i, k_j> for j in J_i */
   for (long long j = 0; j < nkeys; ++j) {
     double dot = 0.0;
     for (long long c = 0; c < d; ++c)
-      dot += qrow[c] * oracle_load(jb->k, jb->dtype, base + j * d + c);
+      dot += qrow[c] * oracle_load(jb->k, jb->dtype, kbase + j * d + c);
     s[j] = jb->scale * dot;
   }
 
@@ -99,11 +114,10 @@ static void one_row(const job_t* jb, long long r, double* qrow, double* s,
   for (long long j = 0; j < nkeys; ++j) l += exp(s[j] - m);
 
   /* pass 3: o = sum (exp(s_j - m) / l) v_j */
-  for (long long c = 0; c < d; ++c) o[c] = 0.0;
   for (long long j = 0; j < nkeys; ++j) {
     const double w = exp(s[j] - m) / l;
     for (long long c = 0; c < d; ++c)
-      o[c] += w * oracle_load(jb->v, jb->dtype, base + j * d + c);
+      o[c] += w * oracle_load(jb->v, jb->dtype, kbase + j * d + c);
   }
   *lse = m + log(l);
 }
@@ -111,7 +125,7 @@ static void one_row(const job_t* jb, long long r, double* qrow, double* s,
 static void* worker(void* arg) {
   job_t* jb = (job_t*)arg;
   double* qrow = (double*)malloc((size_t)jb->d * sizeof(double));
-  double* s = (double*)malloc((size_t)jb->N * sizeof(double));
+  double* s = (double*)malloc((size_t)jb->Nk * sizeof(double));
   if (!qrow || !s) {
     free(qrow);
     free(s);
@@ -132,16 +146,25 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype,
                      double scale, int causal,
                      const long long* rows, long long n_rows,
                      double* o_out, double* lse_out, int threads) {
+  return oracle_attn_rows_ex(q, k, v, dtype, B, H, N, N, d, scale, causal, NULL, rows, n_rows,
+                             o_out, lse_out, threads);
+}
+
+int oracle_attn_rows_ex(const void* q, const void* k, const void* v, int dtype,
+                        long long B, long long H, long long Nq, long long Nk, long long d,
+                        double scale, int causal, const long long* k_len,
+                        const long long* rows, long long n_rows,
+                        double* o_out, double* lse_out, int threads) {
   if (!q || !k || !v || !o_out || !lse_out || (n_rows > 0 && !rows)) return -1;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || n_rows < 0) return -1;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || n_rows < 0) return -1;
   if (causal != 0 && causal != 1) return -1;
   if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return -1;
-  const long long total = B * H * N;
+  const long long total = B * H * Nq;
   for (long long t = 0; t < n_rows; ++t)
     if (rows[t] < 0 || rows[t] >= total) return -1;
   if (n_rows == 0) return 0;
 
-  job_t jb = {q, k, v, dtype, N, d, scale, causal, rows, n_rows,
+  job_t jb = {q, k, v, dtype, H, Nq, Nk, d, scale, causal, k_len, rows, n_rows,
               o_out, lse_out, 0};
   int nt = oracle_thread_count(threads);
   if (nt > n_rows) nt = (int)n_rows;

@@ -67,6 +67,28 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype,
                      double* o_out, double* lse_out, int threads);
 
 /*
+ * oracle_attn_rows_ex -- the same definition for query and key sequences of
+ * different lengths and per-batch padding of the keys (the n x m scores and
+ * the "causal attention or padding" mask of the ScaledDotProductAttention
+ * listing in "Transformer Attention: A Mathematical Deep Dive"):
+ *   q : [B][H][Nq][d];  k, v : [B][H][Nk][d];  rows (b*H + h)*Nq + i.
+ *   k_len : host array of B valid key counts (each clamped to [0, Nk]), or
+ *           NULL for Nk.  With L = the batch's count,
+ *           J_i = {j < L}                      (non-causal)
+ *               = {j < L, j <= i + (L - Nq)}   (causal, bottom-right aligned:
+ *                                               the last query sees every
+ *                                               valid key; Nq = Nk = L gives
+ *                                               the lower triangle)
+ *   A row with J_i empty gets o = 0 and lse = -inf (the empty sum).
+ * oracle_attn_rows is this with Nq = Nk = N and k_len = NULL.
+ */
+int oracle_attn_rows_ex(const void* q, const void* k, const void* v, int dtype,
+                        long long B, long long H, long long Nq, long long Nk, long long d,
+                        double scale, int causal, const long long* k_len,
+                        const long long* rows, long long n_rows,
+                        double* o_out, double* lse_out, int threads);
+
+/*
  * oracle_attn_bwd -- gradients of the same attention (oracle_bwd.c):
  * for an upstream gradient dout = dL/do ([B][H][N][d], type `dtype`), the
  * gradients dL/dq of the query rows q_rows (flat ids (b*H + h)*N + i) and
