@@ -124,7 +124,8 @@ template <class TT, int D, bool CAUSAL, int NW, int NS, bool PERSIST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int N, int n_qtiles, int total_items, int slot, float scale) {
+    int Nq, int Nk, int H, const int* __restrict__ k_len, int n_qtiles, int total_items, int slot,
+    float scale) {
   constexpr int BR = 32 * NW, BC = 64;
   using LY = TileLayout<D>;
   constexpr int TB = LY::BYTES, CG = LY::CG;
@@ -154,7 +155,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int bh = work / n_qtiles;
     int qt = work % n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
-    const size_t head = (size_t)bh * N * D;
+    // keys kept for query i: j < nk and, when causal, j <= i + diag (the last
+    // query row is aligned with the last valid key)
+    const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
+    const int diag = nk - Nq;
+    const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
     const int q_first = qt * BR + 32 * wave;
     const int my_q = q_first + lq;
 
@@ -163,29 +168,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const uint16_t* qrow = Q + head + (size_t)my_q * D + 8 * hf;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
-        qf[c] = (my_q < N) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
+        qf[c] = (my_q < Nq) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
     }
 
-    const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
-    const int T = (kv_end + BC - 1) / BC;
-    const int my_T = CAUSAL ? min(T, (q_first + 31) / BC + 1) : T;
+    const int kv_end = CAUSAL ? min(nk, (qt + 1) * BR + diag) : nk;
+    const int T = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+    const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
+    const int my_T = CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
 
-    const uint16_t* const kbase = K + head;
-    const uint16_t* const vbase = V + head;
+    const uint16_t* const kbase = K + khead;
+    const uint16_t* const vbase = V + khead;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
     // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer (st+1) % NS.
     // Each tile gets a descriptor starting at its first key row (scalar
     // arithmetic), so the per-lane offsets are the same for every tile; the
-    // record count ends at row N, so rows past N read as zero.
+    // record count ends at the last valid key, so rows past it read as zero.
     auto load_stage = [&](int st) {
       const unsigned base = lds0 + ((st + 1) % NS) * 2 * TB;
       if (st + 1 < T) {
         const int k0 = (st + 1) * BC;
-        dma_tile<D, false, NW>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base, 0, wave, lane);
+        dma_tile<D, false, NW>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(nk - k0) * D * 2), base, 0, wave, lane);
       }
       if (st >= 0) {
         const int k0 = st * BC;
-        dma_tile<D, true, NW>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(N - k0) * D * 2), base + TB, 0, wave, lane);
+        dma_tile<D, true, NW>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(nk - k0) * D * 2), base + TB, 0, wave, lane);
       }
     };
     auto stage_buf = [&](int st) { return (st + 1) % NS; };
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool keep = key < N && (!CAUSAL || key <= my_q);
+            const bool keep = key < nk && (!CAUSAL || key <= my_q + diag);
             if (!keep) sv[b][r] = -INFINITY;
           }
       }
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       l_run += ls[0] + ls[1];
       lw_run += lws[0] + lws[1];
     };
-    auto tile_masked = [&](int t) { return (CAUSAL && t * BC + BC - 1 > q_first) || (t * BC + BC > N); };
+    auto tile_masked = [&](int t) { return (CAUSAL && t * BC + BC - 1 > q_first + diag) || (t * BC + BC > nk); };
 
     // One steady-state step (tile j's softmax and product, tile j+1's scores
     // and statistics), written in issue order and fenced so that every MFMA is
@@ -342,9 +348,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int i = 0; i < VP && i < NPV; ++i) vop[i] = vload(i);
       if (mask_next) {
-        // keys past the row (causal) or past N score -inf: lane (q, h) keeps
-        // key offsets 32b + 8(r/4) + r%4 <= lim within tile t_next
-        const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - (t_next * BC + 4 * hf);
+        // keys past the row (causal) or past the valid keys score -inf: lane
+        // (q, h) keeps key offsets 32b + 8(r/4) + r%4 <= lim within tile t_next
+        const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1) - (t_next * BC + 4 * hf);
 #pragma unroll
         for (int b = 0; b < BC / 32; ++b)
 #pragma unroll
@@ -380,13 +386,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
       __builtin_amdgcn_s_setprio(0);
       // tile j+1's statistics; a row whose keys in this tile are all masked
-      // keeps its max (tile 0 gave every row a finite one)
+      // keeps its max (the kept keys are a prefix, so tile 0 gave every row
+      // with a kept key a finite one; a row without any stays at -inf)
       const float mt = half_max(max3(mt0, mt1, mt1));
       m_run = fmaxf(m_run, mt);
       const float mc_cand = m_run * c2;
       const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
       if (resc) {
-        const float alpha = fast_exp2(mc_run - mc_cand);
+        const float alpha = mc_cand == -INFINITY ? 1.f : fast_exp2(mc_run - mc_cand);
         mc_run = mc_cand;
         l_run *= alpha;
         lw_run *= alpha;
@@ -412,15 +419,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // s_waitcnt takes an immediate, so each reachable count (a multiple of half
     // a stage, at most NS-2 full stages) gets its own instruction
     auto wait_keep = [&](int keep) {
-      constexpr int H = NDMA / 2;
+      constexpr int HS = NDMA / 2;  // loads of half a stage
       static_assert((NS - 2) * NDMA <= 63, "vmcnt is a 6-bit count");
       if constexpr (NS >= 4) {
-        if (keep >= 4 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * H)); return; }
-        if (keep == 3 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * H)); return; }
+        if (keep >= 4 * HS) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * HS)); return; }
+        if (keep == 3 * HS) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * HS)); return; }
       }
       if constexpr (NS >= 3) {
-        if (keep >= 2 * H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * H)); return; }
-        if (keep == H) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(H)); return; }
+        if (keep >= 2 * HS) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * HS)); return; }
+        if (keep == HS) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(HS)); return; }
       }
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     };
@@ -446,7 +453,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       wait_keep(keep);
     }
     __syncthreads();
-    if (0 < my_T) {
+    // Every wave scores tile 0 when the block has one, even a wave whose rows
+    // keep no key (causal, more queries than keys): its scores are then all
+    // masked, so the steady steps below see -inf instead of stale registers.
+    if (0 < T) {
       bool resc;
       qk(smem + stage_buf(-1) * 2 * TB, sA);
       part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
@@ -506,7 +516,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float l_tot = half_sum(l_run);
     const float lw_tot = half_sum(lw_run);
     {
-      const float inv = __builtin_amdgcn_rcpf(lw_tot);  // rows past N: finite, not stored
+      // a row without kept keys has lw = 0 and O = 0 (rows past Nq: not stored)
+      const float inv = lw_tot > 0.f ? __builtin_amdgcn_rcpf(lw_tot) : 0.f;
       uint8_t* stg = smem + wave * kOStageBytes;
 #pragma unroll
       for (int r = 0; r < D / 64; ++r) {
@@ -523,11 +534,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int i = 0; i < 4; ++i) {
           const int row = 8 * i + (lane >> 3);
           const u32x4 v = *(const u32x4*)(stg + row * kOStageRow + 16 * (lane & 7));
-          if (q_first + row < N)
+          if (q_first + row < Nq)
             *(u32x4*)(O + head + (size_t)(q_first + row) * D + 64 * r + 8 * (lane & 7)) = v;
         }
       }
-      if (hf == 0 && my_q < N) LSE[(size_t)bh * N + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      // a row without kept keys: -inf + ln 0 = -inf, the log of the empty sum
+      if (hf == 0 && my_q < Nq) LSE[(size_t)bh * Nq + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
     if (tid == 0) s_item = next;
     __syncthreads();
@@ -558,8 +570,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 template <int DSL, int DS, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
-    float scale, int n_split, int tps, float* __restrict__ Opart, float* __restrict__ LSEpart) {
+    float* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int H,
+    const int* __restrict__ k_len, int n_qtiles, int total_wg, float scale, int n_split, int tps,
+    float* __restrict__ Opart, float* __restrict__ LSEpart) {
   constexpr int D = DSL * DS, NB = DSL / 32, BC = 32;
   __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
 
@@ -571,7 +584,9 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int bh = work / n_qtiles;
   int qt = work % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;
-  const size_t head = (size_t)bh * N * D;
+  const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernel
+  const int diag = nk - Nq;
+  const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
   const int q_first = qt * 32;
   const int my_q = q_first + lq;
   const int col0 = wave * DSL;
@@ -581,7 +596,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
 #pragma unroll
     for (int u = 0; u < DSL / 8; ++u)
-      qf[u] = (my_q < N) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+      qf[u] = (my_q < Nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
   }
   f32x16 o[NB];
 #pragma unroll
@@ -589,8 +604,8 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   // running state as in the 16-bit kernel: raw max, exponent reference, sum
   float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
   const float c2 = scale * kLog2e;
-  const int kv_end = CAUSAL ? min(N, q_first + 32) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  const int kv_end = CAUSAL ? min(nk, q_first + 32 + diag) : nk;
+  const int ntiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
   const int j_begin = SPLIT ? split * tps : 0;
   const int j_end = SPLIT ? min(ntiles, j_begin + tps) : ntiles;
 
@@ -600,10 +615,10 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     f32x16 s = f32x16{};
     {
       const int key = k0 + lq;
-      const float* krow = K + head + (size_t)key * D + col0 + 4 * hf;
+      const float* krow = K + khead + (size_t)key * D + col0 + 4 * hf;
 #pragma unroll
       for (int u = 0; u < DSL / 8; ++u) {
-        const f32x4 kv = key < N ? *(const f32x4*)(krow + 8 * u) : f32x4{0, 0, 0, 0};
+        const f32x4 kv = key < nk ? *(const f32x4*)(krow + 8 * u) : f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[v], qf[u][v], s, 0, 0, 0);
       }
@@ -616,12 +631,12 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
       for (int w = 1; w < DS; ++w) s += red[w * 64 + lane];
       __syncthreads();
     }
-    const bool need_mask = (CAUSAL && k0 + BC - 1 > q_first) || (k0 + BC > N);
+    const bool need_mask = (CAUSAL && k0 + BC - 1 > q_first + diag) || (k0 + BC > nk);
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (!(key < N && (!CAUSAL || key <= my_q))) s[r] = -INFINITY;
+        if (!(key < nk && (!CAUSAL || key <= my_q + diag))) s[r] = -INFINITY;
       }
     }
     float mt = s[0];
@@ -648,9 +663,9 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float* vrow = V + head + (size_t)key * D + col0 + NB * lq;
+      const float* vrow = V + khead + (size_t)key * D + col0 + NB * lq;
       float vv[NB];
-      if (key < N) {
+      if (key < nk) {
         if constexpr (NB == 4) {
           const f32x4 t = *(const f32x4*)vrow;
           vv[0] = t[0]; vv[1] = t[1]; vv[2] = t[2]; vv[3] = t[3];
@@ -671,10 +686,10 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   }
 
   const float l_tot = half_sum(l_run);
-  if (my_q < N) {
+  if (my_q < Nq) {
     // a split may hold no kept key of this row: weight 0, lse -inf
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* orow = (SPLIT ? Opart + (size_t)split * ((size_t)N * D * (total_wg / (n_qtiles * n_split))) : O) +
+    float* orow = (SPLIT ? Opart + (size_t)split * ((size_t)Nq * D * (total_wg / (n_qtiles * n_split))) : O) +
                   head + (size_t)my_q * D + col0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -691,9 +706,9 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     if (hf == 0 && wave == 0) {
       const float lse_row = l_tot > 0.f ? (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
       if (SPLIT)
-        LSEpart[(size_t)split * N * (total_wg / (n_qtiles * n_split)) + (size_t)bh * N + my_q] = lse_row;
+        LSEpart[(size_t)split * Nq * (total_wg / (n_qtiles * n_split)) + (size_t)bh * Nq + my_q] = lse_row;
       else
-        LSE[(size_t)bh * N + my_q] = lse_row;
+        LSE[(size_t)bh * Nq + my_q] = lse_row;
     }
   }
 }
@@ -715,6 +730,11 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
   if (threadIdx.x / TPR >= RPB || row >= rows) return;
   float m = -INFINITY;
   for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, LSEpart[(size_t)sp * rows + row]);
+  if (m == -INFINITY) {  // no split kept a key of this row: the empty sum
+    *(f32x4*)(O + (size_t)row * D + 4 * t) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t == 0) LSE[row] = -INFINITY;
+    return;
+  }
   float sum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < n_split; ++sp) {
@@ -746,9 +766,16 @@ hipError_t compute_units(int* cus) {
   return hipSuccess;
 }
 
+// Shape of one call: Nq query rows and Nk key rows per head, optional
+// per-batch valid key counts (device array, clamped to [0, Nk] on the GPU).
+struct Shape {
+  int BH, H, Nq, Nk;
+  const int* k_len;
+};
+
 template <class TT, int D>
-hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                     int N, float scale, bool causal, hipStream_t st) {
+hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const Shape& sh, float scale, bool causal, hipStream_t st) {
   // d = 128: 8 waves (256 query rows) per workgroup halve the K/V tile
   // loads per FLOP, and one persistent workgroup per CU claims work items
   // (no gap between items, no idle XCD at the end).  d = 64: 4 waves, two
@@ -756,8 +783,8 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   constexpr int NW = D == 128 ? 8 : 4, NS = 2;
   constexpr bool PERSIST = D == 128;
   static std::atomic<unsigned> launches{0};
-  const int nq = (N + 32 * NW - 1) / (32 * NW);
-  const int total = nq * BH;
+  const int nq = (sh.Nq + 32 * NW - 1) / (32 * NW);
+  const int total = nq * sh.BH;
   int grid_wg = total, slot = 0;
   if (PERSIST) {
     int cus = 0;
@@ -768,12 +795,12 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   const dim3 grid(grid_wg), block(64 * NW);
   if (causal)
     hipLaunchKernelGGL((attn_fwd_sp<TT, D, true, NW, NS, PERSIST>), grid, block, 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N,
-                       nq, total, slot, scale);
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale);
   else
     hipLaunchKernelGGL((attn_fwd_sp<TT, D, false, NW, NS, PERSIST>), grid, block, 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N,
-                       nq, total, slot, scale);
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale);
   return hipGetLastError();
 }
 
@@ -784,60 +811,60 @@ struct SplitPlan {
   size_t bytes = 0;  // workspace: n_split*rows*d floats of partial O, then n_split*rows of lse
 };
 
-SplitPlan plan_split(long long BH, int N, int d, int dtype) {
+SplitPlan plan_split(long long BH, int Nq, int Nk, int d, int dtype) {
   SplitPlan p;
   if (dtype != FA_DTYPE_FP32) return p;
   int cus = 0;
   if (compute_units(&cus) != hipSuccess) return p;
-  const long long ntiles = (N + 31) / 32, items = ntiles * BH;
+  const long long items = (long long)((Nq + 31) / 32) * BH, ntiles = (Nk + 31) / 32;
   if (items >= cus) return p;
   long long sp = std::min<long long>((cus + items - 1) / items, ntiles / 4);
   if (sp < 2) return p;
   p.tps = (int)((ntiles + sp - 1) / sp);
   p.n_split = (int)((ntiles + p.tps - 1) / p.tps);
   if (p.n_split < 2) return SplitPlan{};
-  const size_t rows = (size_t)BH * N;
+  const size_t rows = (size_t)BH * Nq;
   p.bytes = (size_t)p.n_split * rows * (size_t)(d + 1) * sizeof(float);
   return p;
 }
 
 template <int DSL, int DS>
-hipError_t launch32(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                    int N, float scale, bool causal, hipStream_t st, const SplitPlan& plan,
-                    void* ws) {
+hipError_t launch32(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const Shape& sh, float scale, bool causal, hipStream_t st,
+                    const SplitPlan& plan, void* ws) {
   constexpr int D = DSL * DS;
-  const int nq = (N + 31) / 32;
+  const int nq = (sh.Nq + 31) / 32;
   if (plan.n_split > 1) {
-    const int total = nq * BH * plan.n_split;
+    const int total = nq * sh.BH * plan.n_split;
     float* opart = (float*)ws;
-    float* lpart = opart + (size_t)plan.n_split * BH * N * D;
+    float* lpart = opart + (size_t)plan.n_split * sh.BH * sh.Nq * D;
     const dim3 grid(total), block(DS * 64);
     if (causal)
       hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true, true>), grid, block, 0, st, (const float*)q,
-                         (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale,
-                         plan.n_split, plan.tps, opart, lpart);
+                         (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
+                         sh.k_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
     else
       hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false, true>), grid, block, 0, st, (const float*)q,
-                         (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale,
-                         plan.n_split, plan.tps, opart, lpart);
+                         (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
+                         sh.k_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     constexpr int RPB = D / 4 >= 256 ? 1 : 256 / (D / 4);
-    const int rows = BH * N;
+    const int rows = sh.BH * sh.Nq;
     hipLaunchKernelGGL((attn_combine_f32<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
                        (const float*)opart, (const float*)lpart, (float*)o, lse, rows,
                        plan.n_split);
     return hipGetLastError();
   }
-  const int total = nq * BH;
+  const int total = nq * sh.BH;
   const dim3 grid(total), block(DS * 64);
   if (causal)
     hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true, false>), grid, block, 0, st, (const float*)q,
-                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale, 1, 0,
-                       nullptr, nullptr);
+                       (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
+                       sh.k_len, nq, total, scale, 1, 0, nullptr, nullptr);
   else
     hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false, false>), grid, block, 0, st, (const float*)q,
-                       (const float*)k, (const float*)v, (float*)o, lse, N, nq, total, scale, 1, 0,
-                       nullptr, nullptr);
+                       (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
+                       sh.k_len, nq, total, scale, 1, 0, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -860,47 +887,46 @@ namespace {
 
 // Argument checks shared by the entry points (no HIP call).
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
-               int B, int H, int N, int d, float scale, int causal, int dtype) {
+               int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   const long long BH = (long long)B * H;
   if (BH > (1LL << 24)) return FA_ERR_INVALID_ARG;
-  const long long nq_max = (N + 31) / 32;  // most query tiles any kernel uses
+  const long long nq_max = (Nq + 31) / 32;  // most query tiles any kernel uses
   if (nq_max * BH > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_INVALID_ARG;  // row index of lse
+  if (BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return FA_ERR_INVALID_ARG;  // row ids
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
     return FA_ERR_UNSUPPORTED;
   if (!fa_fwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
   // per-head byte offsets (plus one tile of slack) must fit the 32-bit
   // offsets of the buffer loads
   const long long elem = dtype == FA_DTYPE_FP32 ? 4 : 2;
-  if (((long long)N + 128) * d * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (((long long)std::max(Nq, Nk) + 128) * d * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
-int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int N, int d, float scale, int causal, int dtype, const SplitPlan& plan, void* ws,
+int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, const Shape& sh,
+             int d, float scale, int causal, int dtype, const SplitPlan& plan, void* ws,
              void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool c = causal != 0;
-  const int bh = B * H;
   hipError_t e = hipSuccess;
   if (dtype == FA_DTYPE_BF16) {
-    e = d == 64 ? launch_sp<Bf16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                : launch_sp<Bf16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    e = d == 64 ? launch_sp<Bf16, 64>(q, k, v, o, lse, sh, scale, c, st)
+                : launch_sp<Bf16, 128>(q, k, v, o, lse, sh, scale, c, st);
   } else if (dtype == FA_DTYPE_FP16) {
-    e = d == 64 ? launch_sp<F16, 64>(q, k, v, o, lse, bh, N, scale, c, st)
-                : launch_sp<F16, 128>(q, k, v, o, lse, bh, N, scale, c, st);
+    e = d == 64 ? launch_sp<F16, 64>(q, k, v, o, lse, sh, scale, c, st)
+                : launch_sp<F16, 128>(q, k, v, o, lse, sh, scale, c, st);
   } else {
     switch (d) {
-      case 64: e = launch32<64, 1>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
-      case 128: e = launch32<128, 1>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
-      case 256: e = launch32<128, 2>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
-      case 512: e = launch32<128, 4>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
-      default: e = launch32<128, 8>(q, k, v, o, lse, bh, N, scale, c, st, plan, ws); break;
+      case 64: e = launch32<64, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 128: e = launch32<128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 256: e = launch32<128, 2>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 512: e = launch32<128, 4>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      default: e = launch32<128, 8>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
     }
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -910,32 +936,44 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 extern "C" {
 
+size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (causal != 0 && causal != 1)) return 0;
+  if (!fa_fwd_supported(d, dtype, causal)) return 0;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 24) || BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return 0;
+  return plan_split(BH, Nq, Nk, d, dtype).bytes;
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int d, float scale, int causal, int dtype, const int* k_len,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (int err = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype); err != FA_OK)
+    return err;
+  if (((uintptr_t)k_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  const Shape sh{B * H, H, Nq, Nk, k_len};
+  if (workspace == nullptr || workspace_bytes == 0)
+    return dispatch(q, k, v, o, lse, sh, d, scale, causal, dtype, SplitPlan{}, nullptr, stream);
+  const SplitPlan plan = plan_split((long long)B * H, Nq, Nk, d, dtype);
+  if (workspace_bytes < plan.bytes) return FA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return FA_ERR_UNSUPPORTED;
+  return dispatch(q, k, v, o, lse, sh, d, scale, causal, dtype, plan, workspace, stream);
+}
+
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int N, int d, float scale, int causal, int dtype, void* stream) {
-  if (int err = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype); err != FA_OK)
-    return err;
-  return dispatch(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, SplitPlan{}, nullptr, stream);
+  return fa_fwd_ex(q, k, v, o, lse, B, H, N, N, d, scale, causal, dtype, nullptr, nullptr, 0,
+                   stream);
 }
 
 size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) {
-  if (B <= 0 || H <= 0 || N <= 0 || (causal != 0 && causal != 1)) return 0;
-  if (!fa_fwd_supported(d, dtype, causal)) return 0;
-  if ((long long)B * H > (1LL << 24) || (long long)B * H * N > 0x7fffffffLL) return 0;
-  return plan_split((long long)B * H, N, d, dtype).bytes;
+  return fa_fwd_ex_workspace_size(B, H, N, N, d, causal, dtype);
 }
 
 int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int N, int d, float scale, int causal, int dtype, void* workspace,
               size_t workspace_bytes, void* stream) {
-  if (int err = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype); err != FA_OK)
-    return err;
-  if (workspace == nullptr || workspace_bytes == 0)
-    return dispatch(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, SplitPlan{}, nullptr,
-                    stream);
-  const SplitPlan plan = plan_split((long long)B * H, N, d, dtype);
-  if (workspace_bytes < plan.bytes) return FA_ERR_INVALID_ARG;
-  if (!aligned16(workspace)) return FA_ERR_UNSUPPORTED;
-  return dispatch(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, plan, workspace, stream);
+  return fa_fwd_ex(q, k, v, o, lse, B, H, N, N, d, scale, causal, dtype, nullptr, workspace,
+                   workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -948,6 +986,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 }  // extern "C"

@@ -129,6 +129,34 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_ex -- fa_fwd for query and key sequences of different lengths and
+ * per-batch key padding: the n x m scores and the "causal attention or
+ * padding" mask of the ScaledDotProductAttention listing in "Transformer
+ * Attention: A Mathematical Deep Dive" (query (batch, n, d_k), key and value
+ * (batch, m, d)).
+ *   q, o    : device pointers, [B][H][Nq][d];  lse: [B][H][Nq] fp32.
+ *   k, v    : device pointers, [B][H][Nk][d].
+ *   k_len   : device pointer to B int32 valid key counts (4-byte aligned;
+ *             each clamped to [0, Nk] when read), or NULL for Nk.  With L the
+ *             batch's count, key j is kept for query i iff j < L and, when
+ *             causal, j <= i + (L - Nq): the last query row is aligned with
+ *             the last valid key (Nq = Nk = L gives the lower triangle).
+ *             Keys at or past L are never read.
+ *   workspace, workspace_bytes : as for fa_fwd_ws, sized by
+ *             fa_fwd_ex_workspace_size for the same shapes.
+ * A query row with no kept key (L = 0, or causal with i + L - Nq < 0) gets
+ * O = 0 and lse = -inf: the empty sum.  Everything else -- arguments,
+ * ownership, errors, asynchrony, arithmetic -- is as for fa_fwd; fa_fwd is
+ * fa_fwd_ex with Nq = Nk = N, k_len = NULL and no workspace.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+              const int* k_len, void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_fwd_workspace_size for fa_fwd_ex's shapes (0: none needed, or invalid). */
+size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype);
+
+/*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for this
  * problem: two fp32 row statistics per (batch, head, row), rows padded to a
  * multiple of 32.  0 for invalid or unsupported arguments.
@@ -186,7 +214,7 @@ int fa_fwd_supported(int d, int dtype, int causal);
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* fa_status_string(int status);
 
-/* Library version, major*10000 + minor*100 + patch. */
+/* Library version, major*10000 + minor*100 + patch (200: 0.2.0). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -140,3 +140,44 @@ def test_bwd_invalid_arguments(kw):
 ])
 def test_bwd_unsupported_configurations(kw):
     assert call_bwd(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ unequal lengths, key padding
+def call_ex(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=16, Nk=40, d=64, scale=0.125,
+             causal=0, dtype=fa.FA_DTYPE_BF16, k_len=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                        a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["k_len"],
+                        a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Nq=0), dict(Nk=0), dict(Nk=-4), dict(q=None), dict(lse=None), dict(causal=3),
+    dict(scale=-2.0), dict(B=1 << 16, H=1 << 16),
+])
+def test_ex_invalid_arguments(kw):
+    assert call_ex(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=80), dict(k_len=FAKE + 2), dict(k=FAKE + 8),
+                                dict(dtype=fa.FA_DTYPE_FP32, d=32)])
+def test_ex_unsupported_configurations(kw):
+    assert call_ex(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_ex_workspace_size_matches_the_square_entry_point():
+    for dt, d in ((fa.FA_DTYPE_FP32, 64), (fa.FA_DTYPE_FP32, 1024), (fa.FA_DTYPE_BF16, 128)):
+        for N in (64, 300, 1024):
+            assert fa.fa_fwd_ex_workspace_size(1, 1, N, N, d, 0, dt) == \
+                fa.fa_fwd_workspace_size(1, 1, N, d, 0, dt)
+    assert fa.fa_fwd_ex_workspace_size(1, 1, 0, 5, 64, 0, fa.FA_DTYPE_FP32) == 0
+    assert fa.fa_fwd_ex_workspace_size(1, 1, 5, 0, 64, 0, fa.FA_DTYPE_FP32) == 0
+
+
+def test_python_wrapper_rejects_mismatched_shapes():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    y = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention(x, y, y)
