@@ -60,6 +60,13 @@ def lib():
             ctypes.c_double, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_attn_bwd_ex.restype = ctypes.c_int
+        L.oracle_attn_bwd_ex.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+            ctypes.c_longlong, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.oracle_thread_count.restype = ctypes.c_int
         L.oracle_thread_count.argtypes = [ctypes.c_int]
         L.oracle_load.restype = ctypes.c_double
@@ -195,6 +202,53 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0):
     B, H, N, d = q.shape
     dq, dk, dv = attn_bwd(q, k, v, dout, scale, causal, None, None, threads)
     return dq.reshape(B, H, N, d), dk.reshape(B, H, N, d), dv.reshape(B, H, N, d)
+
+
+def attn_bwd_ex(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=None,
+                k_len=None, threads: int = 0):
+    """Oracle gradients for unequal lengths and key padding (oracle_attn_bwd_ex).
+
+    q, dout: host [B, H, Nq, d]; k, v: host [B, H, Nk, d], one dtype.  q_rows:
+    flat ids (b*H + h)*Nq + i; k_rows: flat ids (b*H + h)*Nk + j (None: all).
+    k_len: B valid key counts or None.  Returns (dq [n_q, d], dk [n_k, d],
+    dv [n_k, d]) float64 numpy arrays.
+    """
+    q, k, v, dout = _as_cpu(q), _as_cpu(k), _as_cpu(v), _as_cpu(dout)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape != dout.shape \
+            or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in _CODES:
+        raise ValueError("q, k, v, dout must share one supported dtype")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    qr = np.arange(B * H * Nq, dtype=np.int64) if q_rows is None else q_rows
+    kr = np.arange(B * H * Nk, dtype=np.int64) if k_rows is None else k_rows
+    qr = np.ascontiguousarray(np.asarray(qr, dtype=np.int64))
+    kr = np.ascontiguousarray(np.asarray(kr, dtype=np.int64))
+    kl = None
+    if k_len is not None:
+        kl = np.ascontiguousarray(np.asarray(k_len, dtype=np.int64))
+        if kl.shape != (B,):
+            raise ValueError("k_len must hold one count per batch")
+    dq = np.empty((qr.shape[0], d), dtype=np.float64)
+    dk = np.empty((kr.shape[0], d), dtype=np.float64)
+    dv = np.empty((kr.shape[0], d), dtype=np.float64)
+    rc = lib().oracle_attn_bwd_ex(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), _CODES[q.dtype],
+        B, H, Nq, Nk, d, float(scale), int(bool(causal)), None if kl is None else kl.ctypes.data,
+        qr.ctypes.data, qr.shape[0], kr.ctypes.data, kr.shape[0],
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd_ex failed with code {rc}")
+    return dq, dk, dv
+
+
+def attention_bwd_ex(q, k, v, dout, scale: float, causal: bool, k_len=None, threads: int = 0):
+    """All rows of attn_bwd_ex; returns (dq [B,H,Nq,d], dk, dv [B,H,Nk,d])."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dq, dk, dv = attn_bwd_ex(q, k, v, dout, scale, causal, None, None, k_len, threads)
+    return dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d)
 
 
 def timed_attn_rows(q, k, v, scale, causal, rows, threads: int = 0):

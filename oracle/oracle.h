@@ -104,6 +104,20 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dou
                     const long long* k_rows, long long n_k,
                     double* dq_out, double* dk_out, double* dv_out, int threads);
 
+/*
+ * oracle_attn_bwd_ex -- the gradients of oracle_attn_rows_ex's attention
+ * (query rows (b*H + h)*Nq + i, key rows (b*H + h)*Nk + j, k_len as there):
+ * the same chain rule summed over the kept pairs only.  A query row that
+ * keeps no key has dq = 0; a key that no query keeps has dk = dv = 0.
+ * oracle_attn_bwd is this with Nq = Nk = N and k_len = NULL.
+ */
+int oracle_attn_bwd_ex(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                       long long B, long long H, long long Nq, long long Nk, long long d,
+                       double scale, int causal, const long long* k_len,
+                       const long long* q_rows, long long n_q,
+                       const long long* k_rows, long long n_k,
+                       double* dq_out, double* dk_out, double* dv_out, int threads);
+
 /* Number of threads a call with `threads` would use. */
 int oracle_thread_count(int threads);
 

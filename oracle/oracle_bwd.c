@@ -33,9 +33,10 @@
 typedef struct {
   const void *q, *k, *v, *g;
   int dtype;
-  long long N, d;
+  long long H, Nq, Nk, d;
   double scale;
   int causal;
+  const long long* k_len; /* per-batch valid keys, or NULL (all Nk) */
   /* per touched head: lse and D of every query row, [n_heads][N] */
   const long long* heads; /* touched heads, ascending */
   long long n_heads;
@@ -64,70 +65,95 @@ static long long head_slot(const bjob_t* jb, long long head) {
   return lo;
 }
 
-static double score(const bjob_t* jb, long long base, long long i, long long j) {
+/* valid keys L of the batch that head `head` (= b*H + h) belongs to */
+static long long valid_keys(const bjob_t* jb, long long head) {
+  long long L = jb->k_len ? jb->k_len[head / jb->H] : jb->Nk;
+  if (L < 0) L = 0;
+  if (L > jb->Nk) L = jb->Nk;
+  return L;
+}
+
+/* |J_i|: query i keeps keys 0 .. nkeys-1 (j < L and, causal, j <= i + L - Nq) */
+static long long kept_keys(const bjob_t* jb, long long head, long long i) {
+  const long long L = valid_keys(jb, head);
+  long long n = L;
+  if (jb->causal && i + (L - jb->Nq) + 1 < n) n = i + (L - jb->Nq) + 1;
+  return n < 0 ? 0 : n;
+}
+
+/* s_ij = scale * <q_i, k_j> of head `head` */
+static double score(const bjob_t* jb, long long head, long long i, long long j) {
+  const long long d = jb->d, qb = head * jb->Nq * d, kb = head * jb->Nk * d;
   double dot = 0.0;
-  for (long long c = 0; c < jb->d; ++c)
-    dot += ld(jb, jb->q, base + i * jb->d + c) * ld(jb, jb->k, base + j * jb->d + c);
+  for (long long c = 0; c < d; ++c)
+    dot += ld(jb, jb->q, qb + i * d + c) * ld(jb, jb->k, kb + j * d + c);
   return jb->scale * dot;
 }
 
-/* phase 0: lse_i and D_i = <g_i, o_i> of query row i of touched head slot hs */
+/* phase 0: lse_i and D_i = <g_i, o_i> of query row i of touched head slot hs
+ * (an empty row: lse = -inf, o = 0, D = 0) */
 static void stats_row(const bjob_t* jb, long long hs, long long i, double* s, double* o) {
-  const long long N = jb->N, d = jb->d, base = jb->heads[hs] * N * d;
-  const long long nkeys = jb->causal ? i + 1 : N;
+  const long long Nq = jb->Nq, d = jb->d, head = jb->heads[hs];
+  const long long kb = head * jb->Nk * d;
+  const long long nkeys = kept_keys(jb, head, i);
   double m = -INFINITY, l = 0.0;
   for (long long j = 0; j < nkeys; ++j) {
-    s[j] = score(jb, base, i, j);
+    s[j] = score(jb, head, i, j);
     if (s[j] > m) m = s[j];
   }
   for (long long j = 0; j < nkeys; ++j) l += exp(s[j] - m);
   for (long long c = 0; c < d; ++c) o[c] = 0.0;
   for (long long j = 0; j < nkeys; ++j) {
     const double w = exp(s[j] - m) / l;
-    for (long long c = 0; c < d; ++c) o[c] += w * ld(jb, jb->v, base + j * d + c);
+    for (long long c = 0; c < d; ++c) o[c] += w * ld(jb, jb->v, kb + j * d + c);
   }
   double Di = 0.0;
-  for (long long c = 0; c < d; ++c) Di += ld(jb, jb->g, base + i * d + c) * o[c];
-  jb->lse[hs * N + i] = m + log(l);
-  jb->D[hs * N + i] = Di;
+  for (long long c = 0; c < d; ++c) Di += ld(jb, jb->g, head * Nq * d + i * d + c) * o[c];
+  jb->lse[hs * Nq + i] = nkeys > 0 ? m + log(l) : -INFINITY;
+  jb->D[hs * Nq + i] = Di;
 }
 
 /* dP_ij = <g_i, v_j> */
-static double dprob(const bjob_t* jb, long long base, long long i, long long j) {
+static double dprob(const bjob_t* jb, long long head, long long i, long long j) {
+  const long long d = jb->d, qb = head * jb->Nq * d, kb = head * jb->Nk * d;
   double dot = 0.0;
-  for (long long c = 0; c < jb->d; ++c)
-    dot += ld(jb, jb->g, base + i * jb->d + c) * ld(jb, jb->v, base + j * jb->d + c);
+  for (long long c = 0; c < d; ++c)
+    dot += ld(jb, jb->g, qb + i * d + c) * ld(jb, jb->v, kb + j * d + c);
   return dot;
 }
 
-/* phase 1: dq of flat row r = head*N + i */
+/* phase 1: dq of flat query row r = head*Nq + i */
 static void dq_row(const bjob_t* jb, long long t) {
-  const long long N = jb->N, d = jb->d, r = jb->q_rows[t];
-  const long long head = r / N, i = r % N, base = head * N * d, hs = head_slot(jb, head);
-  const long long nkeys = jb->causal ? i + 1 : N;
+  const long long Nq = jb->Nq, d = jb->d, r = jb->q_rows[t];
+  const long long head = r / Nq, i = r % Nq, hs = head_slot(jb, head);
+  const long long kb = head * jb->Nk * d;
+  const long long nkeys = kept_keys(jb, head, i);
   double* out = jb->dq + t * d;
   for (long long c = 0; c < d; ++c) out[c] = 0.0;
   for (long long j = 0; j < nkeys; ++j) {
-    const double P = exp(score(jb, base, i, j) - jb->lse[hs * N + i]);
-    const double dS = P * (dprob(jb, base, i, j) - jb->D[hs * N + i]);
-    for (long long c = 0; c < d; ++c) out[c] += dS * ld(jb, jb->k, base + j * d + c);
+    const double P = exp(score(jb, head, i, j) - jb->lse[hs * Nq + i]);
+    const double dS = P * (dprob(jb, head, i, j) - jb->D[hs * Nq + i]);
+    for (long long c = 0; c < d; ++c) out[c] += dS * ld(jb, jb->k, kb + j * d + c);
   }
   for (long long c = 0; c < d; ++c) out[c] *= jb->scale;
 }
 
-/* phase 2: dk and dv of flat key row r = head*N + j */
+/* phase 2: dk and dv of flat key row r = head*Nk + j, summed over the query
+ * rows that keep key j */
 static void dkv_row(const bjob_t* jb, long long t) {
-  const long long N = jb->N, d = jb->d, r = jb->k_rows[t];
-  const long long head = r / N, j = r % N, base = head * N * d, hs = head_slot(jb, head);
+  const long long Nq = jb->Nq, Nk = jb->Nk, d = jb->d, r = jb->k_rows[t];
+  const long long head = r / Nk, j = r % Nk, hs = head_slot(jb, head);
+  const long long qb = head * Nq * d;
   double* dk = jb->dk + t * d;
   double* dv = jb->dv + t * d;
   for (long long c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
-  for (long long i = jb->causal ? j : 0; i < N; ++i) {
-    const double P = exp(score(jb, base, i, j) - jb->lse[hs * N + i]);
-    const double dS = P * (dprob(jb, base, i, j) - jb->D[hs * N + i]);
+  for (long long i = 0; i < Nq; ++i) {
+    if (j >= kept_keys(jb, head, i)) continue;
+    const double P = exp(score(jb, head, i, j) - jb->lse[hs * Nq + i]);
+    const double dS = P * (dprob(jb, head, i, j) - jb->D[hs * Nq + i]);
     for (long long c = 0; c < d; ++c) {
-      dv[c] += P * ld(jb, jb->g, base + i * d + c);
-      dk[c] += dS * ld(jb, jb->q, base + i * d + c);
+      dv[c] += P * ld(jb, jb->g, qb + i * d + c);
+      dk[c] += dS * ld(jb, jb->q, qb + i * d + c);
     }
   }
   for (long long c = 0; c < d; ++c) dk[c] *= jb->scale;
@@ -138,7 +164,7 @@ static void* bworker(void* arg) {
   double* s = NULL;
   double* o = NULL;
   if (jb->phase == 0) {
-    s = (double*)malloc((size_t)jb->N * sizeof(double));
+    s = (double*)malloc((size_t)jb->Nk * sizeof(double));
     o = (double*)malloc((size_t)jb->d * sizeof(double));
     if (!s || !o) {
       free(s);
@@ -150,7 +176,7 @@ static void* bworker(void* arg) {
     long long t = __atomic_fetch_add(&jb->next, 1, __ATOMIC_RELAXED);
     if (t >= jb->n_items) break;
     if (jb->phase == 0)
-      stats_row(jb, t / jb->N, t % jb->N, s, o);
+      stats_row(jb, t / jb->Nq, t % jb->Nq, s, o);
     else if (jb->phase == 1)
       dq_row(jb, t);
     else
@@ -196,31 +222,40 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dou
                     const long long* q_rows, long long n_q,
                     const long long* k_rows, long long n_k,
                     double* dq_out, double* dk_out, double* dv_out, int threads) {
+  return oracle_attn_bwd_ex(q, k, v, dout, dtype, B, H, N, N, d, scale, causal, NULL, q_rows,
+                            n_q, k_rows, n_k, dq_out, dk_out, dv_out, threads);
+}
+
+int oracle_attn_bwd_ex(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                       long long B, long long H, long long Nq, long long Nk, long long d,
+                       double scale, int causal, const long long* k_len,
+                       const long long* q_rows, long long n_q,
+                       const long long* k_rows, long long n_k,
+                       double* dq_out, double* dk_out, double* dv_out, int threads) {
   if (!q || !k || !v || !dout) return -1;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || n_q < 0 || n_k < 0) return -1;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || n_q < 0 || n_k < 0) return -1;
   if ((n_q > 0 && (!q_rows || !dq_out)) || (n_k > 0 && (!k_rows || !dk_out || !dv_out)))
     return -1;
   if (causal != 0 && causal != 1) return -1;
   if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return -1;
-  const long long total = B * H * N;
   for (long long t = 0; t < n_q; ++t)
-    if (q_rows[t] < 0 || q_rows[t] >= total) return -1;
+    if (q_rows[t] < 0 || q_rows[t] >= B * H * Nq) return -1;
   for (long long t = 0; t < n_k; ++t)
-    if (k_rows[t] < 0 || k_rows[t] >= total) return -1;
+    if (k_rows[t] < 0 || k_rows[t] >= B * H * Nk) return -1;
   if (n_q + n_k == 0) return 0;
 
   /* the heads the requested rows live in, sorted and unique */
   long long* heads = (long long*)malloc((size_t)(n_q + n_k) * sizeof(long long));
   if (!heads) return -2;
   long long nh = 0;
-  for (long long t = 0; t < n_q; ++t) heads[nh++] = q_rows[t] / N;
-  for (long long t = 0; t < n_k; ++t) heads[nh++] = k_rows[t] / N;
+  for (long long t = 0; t < n_q; ++t) heads[nh++] = q_rows[t] / Nq;
+  for (long long t = 0; t < n_k; ++t) heads[nh++] = k_rows[t] / Nk;
   qsort(heads, (size_t)nh, sizeof(long long), cmp_ll);
   long long u = 0;
   for (long long t = 0; t < nh; ++t)
     if (u == 0 || heads[t] != heads[u - 1]) heads[u++] = heads[t];
-  double* lse = (double*)malloc((size_t)(u * N) * sizeof(double));
-  double* D = (double*)malloc((size_t)(u * N) * sizeof(double));
+  double* lse = (double*)malloc((size_t)(u * Nq) * sizeof(double));
+  double* D = (double*)malloc((size_t)(u * Nq) * sizeof(double));
   if (!lse || !D) {
     free(heads);
     free(lse);
@@ -230,11 +265,12 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   bjob_t jb;
   memset(&jb, 0, sizeof jb);
   jb.q = q; jb.k = k; jb.v = v; jb.g = dout; jb.dtype = dtype;
-  jb.N = N; jb.d = d; jb.scale = scale; jb.causal = causal;
+  jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.d = d; jb.scale = scale; jb.causal = causal;
+  jb.k_len = k_len;
   jb.heads = heads; jb.n_heads = u; jb.lse = lse; jb.D = D;
   jb.q_rows = q_rows; jb.k_rows = k_rows; jb.n_q = n_q; jb.n_k = n_k;
   jb.dq = dq_out; jb.dk = dk_out; jb.dv = dv_out;
-  int rc = run_phase(&jb, 0, u * N, threads);
+  int rc = run_phase(&jb, 0, u * Nq, threads);
   if (rc == 0) rc = run_phase(&jb, 1, n_q, threads);
   if (rc == 0) rc = run_phase(&jb, 2, n_k, threads);
   free(heads);
