@@ -62,6 +62,12 @@ def library():
             ctypes.c_void_p]
         L.fa_bwd_workspace_size.restype = ctypes.c_size_t
         L.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 6
+        L.fa_bwd_ex.restype = ctypes.c_int
+        L.fa_bwd_ex.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_size_t, ctypes.c_void_p]
+        L.fa_bwd_ex_workspace_size.restype = ctypes.c_size_t
+        L.fa_bwd_ex_workspace_size.argtypes = [ctypes.c_int] * 7
         L.fa_bwd_supported.restype = ctypes.c_int
         L.fa_bwd_supported.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.fa_status_string.restype = ctypes.c_char_p
@@ -224,54 +230,86 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
                             int(causal), int(dtype), workspace, int(workspace_bytes), stream)
 
 
+def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+              B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int, dtype: int,
+              k_len: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    """The raw C entry point for unequal lengths and key padding."""
+    return library().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d,
+                               ctypes.c_float(scale), int(causal), int(dtype), k_len, workspace,
+                               int(workspace_bytes), stream)
+
+
+def fa_bwd_ex_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, causal: int,
+                             dtype: int) -> int:
+    return int(library().fa_bwd_ex_workspace_size(int(B), int(H), int(Nq), int(Nk), int(d),
+                                                  int(causal), int(dtype)))
+
+
 def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                   lse: torch.Tensor, dout: torch.Tensor, causal: bool = False,
                   scale: float | None = None, dq: torch.Tensor | None = None,
                   dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
-                  stream: torch.cuda.Stream | None = None):
+                  stream: torch.cuda.Stream | None = None, k_len: torch.Tensor | None = None):
     """Gradients (dq, dk, dv) of the attention `attention()` computes.
 
-    q, k, v, o, dout: contiguous device tensors [B, H, N, d] of one 16-bit
-    dtype; o and lse as returned by attention() for the same arguments.  The
-    workspace comes from torch's allocator on `stream`.  Asynchronous on
-    `stream` (default: torch's current stream).
+    q, o, dout: contiguous device tensors [B, H, Nq, d]; k, v: [B, H, Nk, d];
+    one 16-bit dtype; o and lse as returned by attention() for the same
+    arguments (k_len included).  The workspace comes from torch's allocator on
+    `stream`.  Asynchronous on `stream` (default: torch's current stream).
+    Equal lengths without k_len run through fa_bwd, other shapes fa_bwd_ex.
     """
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    for name, t, like in (("q", q, q), ("o", o, q), ("dout", dout, q), ("k", k, k), ("v", v, k)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
             raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous tensor like q")
-    if q.dim() != 4 or q.dtype not in _DTYPE_CODE:
-        raise ValueError(f"q must be [B, H, N, d] of a supported dtype, got {tuple(q.shape)} {q.dtype}")
+        if not t.is_contiguous() or t.shape != like.shape or t.dtype != q.dtype \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like {'q' if like is q else 'k'}")
+    if q.dim() != 4 or q.dtype not in _DTYPE_CODE or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q must be [B, H, Nq, d] and k [B, H, Nk, d] of a supported dtype, "
+                         f"got {tuple(q.shape)}, {tuple(k.shape)} {q.dtype}")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32 \
             or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
+    if k_len is not None:
+        if not isinstance(k_len, torch.Tensor) or k_len.dtype != torch.int32 \
+                or k_len.shape != (B,) or not k_len.is_contiguous() or k_len.device != q.device:
+            raise ValueError("k_len must be a contiguous int32 device tensor [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     outs = []
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
         if t is None:
-            t = torch.empty_like(q)
-        elif t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous tensor like q")
+            t = torch.empty_like(like)
+        elif t.shape != like.shape or t.dtype != q.dtype or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like {'q' if like is q else 'k'}")
         outs.append(t)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     code = _DTYPE_CODE[q.dtype]
+    square = Nk == N and k_len is None
     with torch.cuda.device(q.device):
-        ws_bytes = fa_bwd_workspace_size(B, H, N, d, int(bool(causal)), code)
+        ws_bytes = fa_bwd_ex_workspace_size(B, H, N, Nk, d, int(bool(causal)), code)
         if ws_bytes == 0:
             raise ValueError(f"fa_bwd: {fa_status_string(FA_ERR_UNSUPPORTED)} "
                              f"(d={d}, dtype={q.dtype})")
         with torch.cuda.stream(stream):
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                    lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
-                    B, H, N, d, float(scale), int(bool(causal)), code, ws.data_ptr(), ws_bytes,
-                    stream.cuda_stream)
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr())
+        if square:
+            st = fa_bwd(*ptrs, B, H, N, d, float(scale), int(bool(causal)), code, ws.data_ptr(),
+                        ws_bytes, stream.cuda_stream)
+        else:
+            st = fa_bwd_ex(*ptrs, B, H, N, Nk, d, float(scale), int(bool(causal)), code,
+                           None if k_len is None else k_len.data_ptr(), ws.data_ptr(), ws_bytes,
+                           stream.cuda_stream)
         ws.record_stream(stream)
     if st != FA_OK:
-        raise FaError(st, "fa_bwd") if st == FA_ERR_HIP else ValueError(
-            f"fa_bwd: {fa_status_string(st)} (status {st})")
+        where = "fa_bwd" if square else "fa_bwd_ex"
+        raise FaError(st, where) if st == FA_ERR_HIP else ValueError(
+            f"{where}: {fa_status_string(st)} (status {st})")
     return tuple(outs)

@@ -125,6 +125,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const uint16_t* __restrict_
                                                      float* __restrict__ NL, float* __restrict__ ND,
                                                      int N, int n_pad, long long padded_rows,
                                                      float inv_scale) {
+  // N: query rows per head (the rows of O, dO and lse)
   constexpr int TPR = D / 8, RPB = 256 / TPR;
   const int t = threadIdx.x % TPR;
   const long long prow = (long long)blockIdx.x * RPB + threadIdx.x / TPR;  // padded row id
@@ -141,7 +142,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const uint16_t* __restrict_
       acc = fmaf(widen<TT>((uint16_t)(a[w] & 0xffffu)), widen<TT>((uint16_t)(b[w] & 0xffffu)), acc);
       acc = fmaf(widen<TT>((uint16_t)(a[w] >> 16)), widen<TT>((uint16_t)(b[w] >> 16)), acc);
     }
-    nl = -LSE[row] * inv_scale;
+    // a row that kept no key (lse = -inf) keeps P = 0 without an infinite step
+    const float l = LSE[row];
+    nl = l == -INFINITY ? -INFINITY : -l * inv_scale;
   }
 #pragma unroll
   for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, TPR);
@@ -165,8 +168,8 @@ template <class TT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_pad, int n_kblocks,
-    int total, float scale) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int H,
+    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale) {
   constexpr int NW = 4, BQ = 32, CG = D / 32;
   constexpr int TBLK = 2 * CG, TB = TBLK * 1024;  // 1 KB blocks and bytes of one 32-row tile
   static_assert(TBLK % NW == 0, "tile blocks split evenly over the waves");
@@ -181,18 +184,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int item = xcd_remap(blockIdx.x, total);
   const int bh = item / n_kblocks;
   const int kb = item % n_kblocks;  // ascending: causal key blocks near 0 see the most queries
-  const size_t head = (size_t)bh * N * D;
-  const int kw = kb * 32 * NW + 32 * wave;  // this wave's first key
+  // as in the forward: key j is kept for query i iff j < nk and, when causal,
+  // j <= i + diag
+  const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
+  const int diag = nk - Nq;
+  const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const int k0 = kb * 32 * NW;              // the block's first key
+  const int kw = k0 + 32 * wave;            // this wave's first key
   const int my_k = kw + x;
 
   u32x4 kf[D / 16], vf[D / 16];
   {
-    const uint16_t* kr = K + head + (size_t)my_k * D + 8 * h;
-    const uint16_t* vr = V + head + (size_t)my_k * D + 8 * h;
+    const uint16_t* kr = K + khead + (size_t)my_k * D + 8 * h;
+    const uint16_t* vr = V + khead + (size_t)my_k * D + 8 * h;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      kf[c] = my_k < N ? *(const u32x4*)(kr + 16 * c) : u32x4{0, 0, 0, 0};
-      vf[c] = my_k < N ? *(const u32x4*)(vr + 16 * c) : u32x4{0, 0, 0, 0};
+      kf[c] = my_k < nk ? *(const u32x4*)(kr + 16 * c) : u32x4{0, 0, 0, 0};
+      vf[c] = my_k < nk ? *(const u32x4*)(vr + 16 * c) : u32x4{0, 0, 0, 0};
     }
   }
   f32x16 dk[D / 32], dv[D / 32];
@@ -202,8 +210,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float* nl_row = NL + (size_t)bh * n_pad;
   const float* nd_row = ND + (size_t)bh * n_pad;
 
-  const int nqt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? kb * NW : 0;  // first tile holding a query >= the block's first key
+  const int nqt = (Nq + BQ - 1) / BQ;
+  // first tile holding a query that keeps a key of this block (q + diag >= k0);
+  // a block wholly past the valid keys has none and only writes zeros
+  const int qt0 = k0 >= nk ? nqt : CAUSAL ? max(0, k0 - diag) / BQ : 0;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto load = [&](int t, int buf) {
     const int r0 = t * BQ;
@@ -214,8 +224,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float* src = (wave == 0 ? nl_row : nd_row) + r0;
       dma16(buffer_desc(src, BQ * 4), base + 2 * TB + 1024 * wave, lane * 16);
     }
-    const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * D, (unsigned)(N - r0) * D * 2);
-    const u32x4 dd = buffer_desc(dO + head + (size_t)r0 * D, (unsigned)(N - r0) * D * 2);
+    const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * D, (unsigned)(Nq - r0) * D * 2);
+    const u32x4 dd = buffer_desc(dO + head + (size_t)r0 * D, (unsigned)(Nq - r0) * D * 2);
 #pragma unroll
     for (int i = 0; i < TBLK / NW; ++i) {
       const int blk = wave + i * NW;
@@ -233,8 +243,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int buf = (t - qt0) & 1;
     if (t + 1 < nqt) load(t + 1, buf ^ 1);
     const int q0 = t * BQ;
-    // queries q0..q0+31 all precede this wave's keys: nothing kept
-    if (!CAUSAL || q0 + BQ - 1 >= kw) {
+    // nothing kept when this wave's keys are all padding, or all above the
+    // last query row of the tile
+    if (kw < nk && (!CAUSAL || q0 + BQ - 1 + diag >= kw)) {
       const uint8_t* qt = smem + buf * BUF;
       const uint8_t* dt = qt + TB;
       f32x16 s, dp;
@@ -254,13 +265,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         s = TT::mma(*(const u32x4*)(qt + rowmajor_a<D>(x, h, c)), kf[c], s);
         dp = TT::mma(*(const u32x4*)(dt + rowmajor_a<D>(x, h, c)), vf[c], dp);
       }
-      // P = exp(scale s - lse); dS = P (dP - delta); the diagonal tile keeps
-      // key <= query only
-      const bool diag = CAUSAL && q0 < kw + 32;
+      // P = exp(scale s - lse); dS = P (dP - delta); a tile across the
+      // diagonal or the end of the valid keys keeps key <= query + diag and
+      // key < nk only
+      const bool mask = (CAUSAL && q0 + diag < kw + 31) || kw + 31 >= nk;
+      const int lim = my_k >= nk ? 0x7fffffff : CAUSAL ? my_k - diag : -0x7fffffff;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(s[r] * c2);
-        if (diag && my_k > q0 + 8 * (r >> 2) + 4 * h + (r & 3)) p = 0.f;
+        if (mask && q0 + 8 * (r >> 2) + 4 * h + (r & 3) < lim) p = 0.f;
         s[r] = p;
         dp[r] = p * dp[r];
       }
@@ -287,9 +300,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
   // the tile buffers are free after the last barrier
+  // every key row is written, those past the valid keys as zeros
   uint8_t* stg = smem + wave * 32 * 144;
-  store_rows<TT, D>(dv, 1.f, stg, dV + head, kw, N, lane);
-  store_rows<TT, D>(dk, scale, stg, dK + head, kw, N, lane);
+  store_rows<TT, D>(dv, 1.f, stg, dV + khead, kw, Nk, lane);
+  store_rows<TT, D>(dk, scale, stg, dK + khead, kw, Nk, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -306,7 +320,8 @@ template <class TT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
-    uint16_t* __restrict__ dQ, int N, int n_pad, int n_qblocks, int total, float scale) {
+    uint16_t* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
+    int n_qblocks, int total, float scale) {
   constexpr int NW = 4, BR = 32 * NW, BC = 64, CG = D / 32;
   using LY = TileLayout<D>;
   constexpr int TB = LY::BYTES;
@@ -320,7 +335,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int bh = item / n_qblocks;
   int qb = item % n_qblocks;
   if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
-  const size_t head = (size_t)bh * N * D;
+  const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the dK/dV kernel
+  const int diag = nk - Nq;
+  const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
   const int q_first = qb * BR + 32 * wave;
   const int my_q = q_first + x;
 
@@ -330,28 +347,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* dr = dO + head + (size_t)my_q * D + 8 * h;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      qf[c] = my_q < N ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
-      of[c] = my_q < N ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
+      qf[c] = my_q < Nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
+      of[c] = my_q < Nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
     }
   }
   const float c2 = scale * kLog2e;
   // (rows past N are never stored; the block's last rows may lie past the padding)
-  const float nl2 = my_q < N ? NL[(size_t)bh * n_pad + my_q] * c2 : 0.f;
-  const float nd = my_q < N ? ND[(size_t)bh * n_pad + my_q] : 0.f;
+  const float nl2 = my_q < Nq ? NL[(size_t)bh * n_pad + my_q] * c2 : 0.f;
+  const float nd = my_q < Nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
   f32x16 dq[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) dq[b] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
-  const int T = (kv_end + BC - 1) / BC;
-  const int my_T = CAUSAL ? min(T, (q_first + 31) / BC + 1) : T;
+  const int kv_end = CAUSAL ? min(nk, (qb + 1) * BR + diag) : nk;
+  const int T = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
+  const int my_T = CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto load = [&](int j, int buf) {
     const int k0 = j * BC;
     const unsigned base = lds0 + buf * 2 * TB;
-    const unsigned bytes = (unsigned)(N - k0) * D * 2;
-    dma_tile<D, true, NW>(buffer_desc(K + head + (size_t)k0 * D, bytes), base, 0, wave, lane);
-    dma_tile<D, false, NW>(buffer_desc(V + head + (size_t)k0 * D, bytes), base + TB, 0, wave, lane);
+    const unsigned bytes = (unsigned)(nk - k0) * D * 2;
+    dma_tile<D, true, NW>(buffer_desc(K + khead + (size_t)k0 * D, bytes), base, 0, wave, lane);
+    dma_tile<D, false, NW>(buffer_desc(V + khead + (size_t)k0 * D, bytes), base + TB, 0, wave, lane);
   };
   const int trl = tr_lane(lane);
   // A operand of V (chunk-major block layout), as in the forward kernel
@@ -367,10 +385,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const uint8_t* kt = smem + buf * 2 * TB;
       const uint8_t* vt = kt + TB;
       const int k0 = j * BC;
-      // keys past the row (causal) or past N get no weight: a key past N has
-      // zero K and V rows, but its weight exp(-lse) need not be finite
-      const bool masked = (CAUSAL && k0 + BC - 1 > q_first) || (k0 + BC > N);
-      const int lim = min(CAUSAL ? my_q : N - 1, N - 1);
+      // keys past the row (causal) or past the valid keys get no weight: such
+      // a key has zero K and V rows, but its weight exp(-lse) need not be finite
+      const bool masked = (CAUSAL && k0 + BC - 1 > q_first + diag) || (k0 + BC > nk);
+      const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1);
 #pragma unroll
       for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
         f32x16 st = f32x16{}, dpt = f32x16{};
@@ -404,7 +422,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
   uint8_t* stg = smem + wave * 32 * 144;
-  store_rows<TT, D>(dq, scale, stg, dQ + head, q_first, N, lane);
+  store_rows<TT, D>(dq, scale, stg, dQ + head, q_first, Nq, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,37 +431,37 @@ size_t padded_rows(long long BH, int N) { return (size_t)BH * (size_t)((N + kRow
 
 template <class TT, int D>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv, int BH, int N, float scale,
-                      bool causal, float* ws, hipStream_t st) {
-  const int n_pad = (N + kRowPad - 1) / kRowPad * kRowPad;
+                      const float* lse, void* dq, void* dk, void* dv, int BH, int H, int Nq, int Nk,
+                      const int* k_len, float scale, bool causal, float* ws, hipStream_t st) {
+  const int n_pad = (Nq + kRowPad - 1) / kRowPad * kRowPad;
   const long long prow = (long long)BH * n_pad;
   float* nl = ws;
   float* nd = ws + prow;
   {
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((attn_bwd_prep<TT, D>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256), 0,
-                       st, (const uint16_t*)o, (const uint16_t*)dout, lse, nl, nd, N, n_pad, prow,
+                       st, (const uint16_t*)o, (const uint16_t*)dout, lse, nl, nd, Nq, n_pad, prow,
                        1.f / scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  const int nkb = (N + 127) / 128, nqb = (N + 127) / 128;
+  const int nkb = (Nk + 127) / 128, nqb = (Nq + 127) / 128;
   const int tk = nkb * BH, tq = nqb * BH;
   if (causal) {
     hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, true>), dim3(tk), dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dk, (uint16_t*)dv, N, n_pad, nkb, tk, scale);
+                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq<TT, D, true>), dim3(tq), dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dq, N, n_pad, nqb, tq, scale);
+                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
   } else {
     hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, false>), dim3(tk), dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dk, (uint16_t*)dv, N, n_pad, nkb, tk, scale);
+                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq<TT, D, false>), dim3(tq), dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dq, N, n_pad, nqb, tq, scale);
+                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
   }
   return hipGetLastError();
 }
@@ -459,44 +477,59 @@ int fa_bwd_supported(int d, int dtype, int causal) {
   return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16) && (d == 64 || d == 128);
 }
 
+size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !fa_bwd_supported(d, dtype, causal)) return 0;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 24) || BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return 0;
+  return 2 * padded_rows(BH, Nq) * sizeof(float);
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) {
-  if (B <= 0 || H <= 0 || N <= 0 || !fa_bwd_supported(d, dtype, causal)) return 0;
-  if ((long long)B * H > (1LL << 24) || (long long)B * H * N > 0x7fffffffLL) return 0;
-  return 2 * padded_rows((long long)B * H, N) * sizeof(float);
+  return fa_bwd_ex_workspace_size(B, H, N, N, d, causal, dtype);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+              float scale, int causal, int dtype, const int* k_len, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 24) || BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((((long long)Nq + 127) / 128 + ((long long)Nk + 127) / 128) * BH > 0x7fffffffLL)
+    return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
+    return FA_ERR_UNSUPPORTED;
+  if (!fa_bwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
+  // per-head byte offsets (plus one tile of slack) fit the 32-bit buffer offsets
+  if (((long long)(Nq > Nk ? Nq : Nk) + 128) * d * 2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa_bwd_ex_workspace_size(B, H, Nq, Nk, d, causal, dtype))
+    return FA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv,
+                        (const void*)workspace})
+    if (!aligned16(p)) return FA_ERR_UNSUPPORTED;
+  if (((uintptr_t)k_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  const int bh = (int)BH;
+  float* ws = (float*)workspace;
+  hipError_t e;
+  if (dtype == FA_DTYPE_BF16)
+    e = d == 64 ? launch_bwd<Bf16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
+                : launch_bwd<Bf16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+  else
+    e = d == 64 ? launch_bwd<F16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
+                : launch_bwd<F16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
            float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
            void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
-  const long long BH = (long long)B * H;
-  if (BH > (1LL << 24) || BH * N > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  if (((long long)N + 127) / 128 * BH > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
-    return FA_ERR_UNSUPPORTED;
-  if (!fa_bwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
-  // per-head byte offsets (plus one tile of slack) fit the 32-bit buffer offsets
-  if (((long long)N + 128) * d * 2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
-  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, causal, dtype))
-    return FA_ERR_INVALID_ARG;
-  for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv,
-                        (const void*)workspace})
-    if (!aligned16(p)) return FA_ERR_UNSUPPORTED;
-  hipStream_t st = (hipStream_t)stream;
-  const int bh = (int)BH;
-  float* ws = (float*)workspace;
-  hipError_t e;
-  if (dtype == FA_DTYPE_BF16)
-    e = d == 64 ? launch_bwd<Bf16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st)
-                : launch_bwd<Bf16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st);
-  else
-    e = d == 64 ? launch_bwd<F16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st)
-                : launch_bwd<F16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, N, scale, causal, ws, st);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, N, d, scale, causal, dtype, nullptr,
+                   workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

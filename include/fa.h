@@ -205,6 +205,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
            void* stream);
 
+/*
+ * fa_bwd_ex -- fa_bwd for fa_fwd_ex's shapes: q, o, dout, dq are
+ * [B][H][Nq][d], k, v, dk, dv [B][H][Nk][d], lse [B][H][Nq]; k_len as for
+ * fa_fwd_ex (NULL: all Nk keys valid).  The sums run over the kept pairs of
+ * fa_fwd_ex: a query row that keeps no key gets dq = 0, a key no query keeps
+ * (padding, or past every row's causal limit) gets dk = dv = 0 -- every row of
+ * dq, dk and dv is written.  The workspace must hold
+ * fa_bwd_ex_workspace_size(...) bytes.  fa_bwd is fa_bwd_ex with Nq = Nk = N
+ * and k_len = NULL; everything else is as for fa_bwd.
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+              float scale, int causal, int dtype, const int* k_len, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Workspace of fa_bwd_ex: two fp32 statistics per (batch, head, query row),
+ * rows padded to a multiple of 32; 0 for invalid or unsupported arguments. */
+size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype);
+
 /* 1 when fa_bwd has kernels for (d, dtype, causal), else 0. */
 int fa_bwd_supported(int d, int dtype, int causal);
 

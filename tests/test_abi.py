@@ -181,3 +181,23 @@ def test_python_wrapper_rejects_mismatched_shapes():
     y = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attention(x, y, y)
+
+
+def test_bwd_ex_checks_arguments_first():
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                B=1, H=1, Nq=16, Nk=40, d=64, scale=0.125, causal=0, dtype=fa.FA_DTYPE_BF16,
+                k_len=None, ws=FAKE, ws_bytes=1 << 20)
+
+    def run(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                            a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                            a["causal"], a["dtype"], a["k_len"], a["ws"], a["ws_bytes"], None)
+    for kw in (dict(Nq=0), dict(Nk=0), dict(dk=None), dict(ws=None), dict(ws_bytes=4), dict(causal=5)):
+        assert run(**kw) == fa.FA_ERR_INVALID_ARG, kw
+    for kw in (dict(k_len=FAKE + 1), dict(d=32), dict(dtype=fa.FA_DTYPE_FP32)):
+        assert run(**kw) == fa.FA_ERR_UNSUPPORTED, kw
+    assert fa.fa_bwd_ex_workspace_size(2, 3, 100, 7, 64, 1, fa.FA_DTYPE_BF16) == 2 * 6 * 128 * 4
+    assert fa.fa_bwd_ex_workspace_size(2, 3, 100, 100, 64, 1, fa.FA_DTYPE_BF16) == \
+        fa.fa_bwd_workspace_size(2, 3, 100, 64, 1, fa.FA_DTYPE_BF16)

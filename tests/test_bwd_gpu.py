@@ -121,3 +121,32 @@ def test_rejected_calls_raise():
     qb = q.to(torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attention_bwd(qb, qb, qb, qb, lse[:, :, :8], qb)
+
+
+# ------------------------------------------------------------------ unequal lengths, key padding
+@pytest.mark.parametrize("dt,d", [("bf16", 64), ("bf16", 128), ("fp16", 128)])
+@pytest.mark.parametrize("Nq,Nk,k_len", [(77, 300, None), (300, 77, None), (129, 1, None),
+                                         (190, 333, [333, 150, 0]), (64, 64, [40, 64, 1])])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unequal_lengths_and_padding_match_gradient_oracle(dt, d, Nq, Nk, k_len, causal):
+    B, H = 3, 2
+    seed = 5000 + Nq + 3 * Nk + d + int(causal)
+    q, _, _ = make_qkv(B, H, Nq, d, dt, seed)
+    _, k, v = make_qkv(B, H, Nk, d, dt, seed + 1)
+    g = make_dout(B, H, Nq, d, dt, seed + 2)
+    scale = 1 / math.sqrt(d)
+    kl = None if k_len is None else torch.tensor(k_len, dtype=torch.int32, device="cuda")
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, g))
+    o, lse = fa.attention(qc, kc, vc, causal=causal, scale=scale, k_len=kl)
+    dq, dk, dv = fa.attention_bwd(qc, kc, vc, o, lse, gc, causal=causal, scale=scale, k_len=kl)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd_ex(q, k, v, g, scale, causal, k_len)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        check(errors(got, ref), DT[dt], name)
+    # structural zeros are exact: keys past a batch's count (no query keeps
+    # them) and query rows that keep no key
+    lens = [Nk] * B if k_len is None else [min(max(x, 0), Nk) for x in k_len]
+    for b, L in enumerate(lens):
+        assert torch.all(dk[b, :, L:] == 0) and torch.all(dv[b, :, L:] == 0)
+        empty = [i for i in range(Nq) if L == 0 or (causal and i + L - Nq < 0)]
+        assert torch.all(dq[b, :, empty] == 0)
