@@ -164,15 +164,14 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const uint16_t* __restrict_
 //     query 8(r/4) + 4h + r%4 of the tile and key key0 + x.
 //   dK^T, dV^T (accumulators): block b, register r of lane (x, h) is
 //     d-column 32b + 8(r/4) + 4h + r%4 of key key0 + x.
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(
+template <class TT, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int H,
     const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale) {
-  constexpr int NW = 4, BQ = 32, CG = D / 32;
+  constexpr int BQ = 32, CG = D / 32;
   constexpr int TBLK = 2 * CG, TB = TBLK * 1024;  // 1 KB blocks and bytes of one 32-row tile
-  static_assert(TBLK % NW == 0, "tile blocks split evenly over the waves");
   // [buffer][Q tile, dO tile, nl of its rows (1 KB), nd of its rows (1 KB)];
   // the epilogue reuses it as the waves' output staging
   constexpr int BUF = 2 * TB + 2048;
@@ -227,11 +226,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * D, (unsigned)(Nq - r0) * D * 2);
     const u32x4 dd = buffer_desc(dO + head + (size_t)r0 * D, (unsigned)(Nq - r0) * D * 2);
 #pragma unroll
-    for (int i = 0; i < TBLK / NW; ++i) {
+    for (int i = 0; i < (TBLK + NW - 1) / NW; ++i) {
       const int blk = wave + i * NW;
-      const int el = TileLayout<D>::v_src(blk, lane);
-      dma16(dq, base + blk * 1024, el * 2);
-      dma16(dd, base + TB + blk * 1024, el * 2);
+      if (blk < TBLK) {  // with more waves than blocks, some waves load none
+        const int el = TileLayout<D>::v_src(blk, lane);
+        dma16(dq, base + blk * 1024, el * 2);
+        dma16(dd, base + TB + blk * 1024, el * 2);
+      }
     }
   };
   const int trl = tr_lane(lane);
@@ -316,18 +317,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //   S^T, dP^T (accumulators, per 32-key block): register r of lane (x, h) is
 //     key 8(r/4) + 4h + r%4 of the block and query q_first + x.
 //   dQ^T (accumulator): block b, register r is d-column 32b + 8(r/4) + 4h + r%4.
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(
+template <class TT, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     uint16_t* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
     int n_qblocks, int total, float scale) {
-  constexpr int NW = 4, BR = 32 * NW, BC = 64, CG = D / 32;
+  constexpr int BR = 32 * NW, BC = 64, CG = D / 32;
   using LY = TileLayout<D>;
   constexpr int TB = LY::BYTES;
   static_assert(LY::BLOCKS % NW == 0, "tile blocks split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TB];  // [buffer][K, V]
-  static_assert(NW * 32 * 144 <= 2 * 2 * TB, "output staging fits the tile buffers");
+  // [buffer][K, V]; the epilogue reuses it as the waves' output staging
+  constexpr int SMEM = 2 * 2 * TB > NW * 32 * 144 ? 2 * 2 * TB : NW * 32 * 144;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = lane & 31, h = lane >> 5;
@@ -444,22 +446,26 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                        1.f / scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  const int nkb = (Nk + 127) / 128, nqb = (Nq + 127) / 128;
+  // 4 waves (128 keys, 128 query rows) per workgroup; 8 were measured slower
+  // on every workload shape, though they halve the re-streamed tiles
+  constexpr int NWK = 4, NWQ = 4;
+  const int nkb = (Nk + 32 * NWK - 1) / (32 * NWK), nqb = (Nq + 32 * NWQ - 1) / (32 * NWQ);
   const int tk = nkb * BH, tq = nqb * BH;
+  const dim3 bk(64 * NWK), bq(64 * NWQ);
   if (causal) {
-    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, true>), dim3(tk), dim3(256), 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, true, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq<TT, D, true>), dim3(tq), dim3(256), 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dq<TT, D, true, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, false>), dim3(tk), dim3(256), 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, false, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq<TT, D, false>), dim3(tq), dim3(256), 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dq<TT, D, false, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
   }
