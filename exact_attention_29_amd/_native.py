@@ -253,7 +253,7 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     """Gradients (dq, dk, dv) of the attention `attention()` computes.
 
     q, o, dout: contiguous device tensors [B, H, Nq, d]; k, v: [B, H, Nk, d];
-    one 16-bit dtype; o and lse as returned by attention() for the same
+    one dtype (bf16, fp16, or fp32); o and lse as returned by attention() for the same
     arguments (k_len included).  The workspace comes from torch's allocator on
     `stream`.  Asynchronous on `stream` (default: torch's current stream).
     Equal lengths without k_len run through fa_bwd, other shapes fa_bwd_ex.

@@ -428,6 +428,307 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------------------
+// fp32 gradients.  Like the fp32 forward kernel: v_mfma_f32_32x32x2_f32, each
+// lane supplying one element per operand, operands read from global memory
+// (L2) straight into registers in operand order, no LDS staging.  A
+// workgroup has DS waves; wave w owns head-dim columns [w*DSL, (w+1)*DSL),
+// and the partial S and dP of the waves are summed through LDS in fixed
+// wave order, so every wave sees bitwise the same values.
+//   S-type products contract column w*DSL + 8u + 4h + v at step (u, v): lane
+//     (x, h) supplies row x's element of it (16-byte loads).
+//   The products over 32 rows of the tile (dV^T, dK^T, dQ^T) take step r =
+//     accumulator register r (row 8(r/4) + 4h + r%4); their output block b,
+//     row i is column w*DSL + NB*i + b (NB = DSL/32), so one lane's NB values
+//     of a row are contiguous.
+
+// Row statistics from fp32 O and dO: TPR threads per row (at most a wave).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_f32(const float* __restrict__ O,
+                                                         const float* __restrict__ dO,
+                                                         const float* __restrict__ LSE,
+                                                         float* __restrict__ NL, float* __restrict__ ND,
+                                                         int N, int n_pad, long long padded_rows,
+                                                         float inv_scale) {
+  constexpr int TPR = D / 4 < 64 ? D / 4 : 64, RPB = 256 / TPR, CH = D / (4 * TPR);
+  const int t = threadIdx.x % TPR;
+  const long long prow = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (prow >= padded_rows) return;  // whole rows only: TPR divides the wave
+  const long long bh = prow / n_pad;
+  const int i = (int)(prow % n_pad);
+  float acc = 0.f, nl = 0.f;
+  if (i < N) {
+    const size_t row = (size_t)bh * N + i;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const f32x4 a = *(const f32x4*)(O + row * D + 4 * (t + TPR * c));
+      const f32x4 b = *(const f32x4*)(dO + row * D + 4 * (t + TPR * c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf(a[e], b[e], acc);
+    }
+    const float l = LSE[row];
+    nl = l == -INFINITY ? -INFINITY : -l * inv_scale;
+  }
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, TPR);
+  if (t == 0) {
+    NL[prow] = nl;
+    ND[prow] = -acc;
+  }
+}
+
+// load NB contiguous floats (zeros when !ok)
+template <int NB>
+__device__ __forceinline__ void load_nb(const float* p, bool ok, float (&out)[NB]) {
+  if (!ok) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) out[b] = 0.f;
+    return;
+  }
+  if constexpr (NB == 8) {
+    const f32x4 t = *(const f32x4*)p, u = *(const f32x4*)(p + 4);
+    out[0] = t[0]; out[1] = t[1]; out[2] = t[2]; out[3] = t[3];
+    out[4] = u[0]; out[5] = u[1]; out[6] = u[2]; out[7] = u[3];
+  } else if constexpr (NB == 4) {
+    const f32x4 t = *(const f32x4*)p;
+    out[0] = t[0]; out[1] = t[1]; out[2] = t[2]; out[3] = t[3];
+  } else if constexpr (NB == 2) {
+    const f32x2 t = *(const f32x2*)p;
+    out[0] = t[0]; out[1] = t[1];
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) out[b] = p[b];
+  }
+}
+
+// Sum of the DS waves' partial s and dp (fixed wave order).
+template <int DS>
+__device__ __forceinline__ void sum_waves(f32x16* red, f32x16& s, f32x16& dp, int wave, int lane) {
+  if constexpr (DS > 1) {
+    red[wave * 64 + lane] = s;
+    red[(DS + wave) * 64 + lane] = dp;
+    __syncthreads();
+    s = red[lane];
+    dp = red[DS * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < DS; ++w) {
+      s += red[w * 64 + lane];
+      dp += red[(DS + w) * 64 + lane];
+    }
+    __syncthreads();
+  }
+}
+
+// dK, dV of 32 keys per workgroup.  S and dP in (query x key) orientation:
+// register r of lane (x, h) is query q0 + 8(r/4) + 4h + r%4, key k0 + x.
+template <int DSL, int DS, bool CAUSAL>
+__global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
+    float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int H,
+    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale) {
+  constexpr int D = DSL * DS, NB = DSL / 32;
+  __shared__ f32x16 red[DS > 1 ? 2 * DS * 64 : 1];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = lane & 31, h = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, total);
+  const int bh = item / n_kblocks, kb = item % n_kblocks;
+  const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernels
+  const int diag = nk - Nq;
+  const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const int k0 = kb * 32, my_k = k0 + x, col0 = wave * DSL;
+
+  // The block's K and V rows are held in registers for the whole kernel when
+  // a wave's share is 128 columns or fewer; with 256 columns each 16-byte
+  // piece is read from L2 where a product uses it, to stay within the wave's
+  // 512 registers.
+  constexpr bool HOLD = DSL <= 128;
+  constexpr int NF = HOLD ? DSL / 8 : 1;
+  const float* kr = K + khead + (size_t)my_k * D + col0 + 4 * h;
+  const float* vr = V + khead + (size_t)my_k * D + col0 + 4 * h;
+  f32x4 kf[NF], vf[NF];
+  if (HOLD) {
+#pragma unroll
+    for (int u = 0; u < NF; ++u) {
+      kf[u] = my_k < nk ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
+      vf[u] = my_k < nk ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 dk[NB], dv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dk[b] = dv[b] = f32x16{};
+  const float c2 = scale * kLog2e;
+  const float* nl_row = NL + (size_t)bh * n_pad;
+  const float* nd_row = ND + (size_t)bh * n_pad;
+  const int nqt = (Nq + 31) / 32;
+  const int qt0 = k0 >= nk ? nqt : CAUSAL ? max(0, k0 - diag) / 32 : 0;
+  const bool edge_k = k0 + 31 >= nk;  // some keys of the block are padding
+  const int lim = my_k >= nk ? 0x7fffffff : CAUSAL ? my_k - diag : -0x7fffffff;
+
+  for (int t = qt0; t < nqt; ++t) {
+    const int q0 = t * 32;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    {
+      const bool ok = q0 + x < Nq;
+      const float* qr = Q + head + (size_t)(q0 + x) * D + col0 + 4 * h;
+      const float* gr = dO + head + (size_t)(q0 + x) * D + col0 + 4 * h;
+#pragma unroll
+      for (int u = 0; u < DSL / 8; ++u) {
+        const f32x4 qa = ok ? *(const f32x4*)(qr + 8 * u) : f32x4{0, 0, 0, 0};
+        const f32x4 ga = ok ? *(const f32x4*)(gr + 8 * u) : f32x4{0, 0, 0, 0};
+        const f32x4 ka = HOLD ? kf[HOLD ? u : 0]
+                              : (my_k < nk ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0});
+        const f32x4 va = HOLD ? vf[HOLD ? u : 0]
+                              : (my_k < nk ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[v], ka[v], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[v], va[v], dp, 0, 0, 0);
+        }
+      }
+    }
+    sum_waves<DS>(red, s, dp, wave, lane);
+    // P = exp(scale s - lse), dS = P (dP - delta); keys past the valid ones or
+    // past a row's causal limit get no weight
+    const bool mask = (CAUSAL && q0 + diag < k0 + 31) || edge_k;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 a = *(const f32x4*)(nl_row + q0 + 8 * g + 4 * h);
+      const f32x4 b = *(const f32x4*)(nd_row + q0 + 8 * g + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float p = fast_exp2((s[r] + a[e]) * c2);
+        if (mask && q0 + 8 * g + 4 * h + e < lim) p = 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] + b[e]);
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over the tile's 32 rows
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      float gv[NB], qv[NB];
+      load_nb<NB>(dO + head + (size_t)q * D + col0 + NB * x, q < Nq, gv);
+      load_nb<NB>(Q + head + (size_t)q * D + col0 + NB * x, q < Nq, qv);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        dv[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(gv[b], s[r], dv[b], 0, 0, 0);
+        dk[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[b], dp[r], dk[b], 0, 0, 0);
+      }
+    }
+  }
+  if (my_k < Nk) {  // every key row, those past the valid keys as zeros
+    float* kr = dK + khead + (size_t)my_k * D + col0;
+    float* vr = dV + khead + (size_t)my_k * D + col0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        kr[NB * i + b] = dk[b][r] * scale;
+        vr[NB * i + b] = dv[b][r];
+      }
+    }
+  }
+}
+
+// dQ of 32 query rows per workgroup.  S^T and dP^T: register r of lane (x, h)
+// is key k0 + 8(r/4) + 4h + r%4, query q0 + x.
+template <int DSL, int DS, bool CAUSAL>
+__global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
+    float* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
+    int n_qblocks, int total, float scale) {
+  constexpr int D = DSL * DS, NB = DSL / 32;
+  __shared__ f32x16 red[DS > 1 ? 2 * DS * 64 : 1];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = lane & 31, h = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, total);
+  const int bh = item / n_qblocks;
+  int qb = item % n_qblocks;
+  if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
+  const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
+  const int diag = nk - Nq;
+  const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const int q0 = qb * 32, my_q = q0 + x, col0 = wave * DSL;
+
+  // Q and dO rows in registers, or read where used with 256 columns per wave
+  // (as K and V in the dK/dV kernel)
+  constexpr bool HOLD = DSL <= 128;
+  constexpr int NF = HOLD ? DSL / 8 : 1;
+  const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * h;
+  const float* grow = dO + head + (size_t)my_q * D + col0 + 4 * h;
+  f32x4 qf[NF], gf[NF];
+  if (HOLD) {
+#pragma unroll
+    for (int u = 0; u < NF; ++u) {
+      qf[u] = my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+      gf[u] = my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
+    }
+  }
+  const float c2 = scale * kLog2e;
+  const float nl2 = my_q < Nq ? NL[(size_t)bh * n_pad + my_q] * c2 : 0.f;
+  const float nd = my_q < Nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
+  f32x16 dq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
+  const int kv_end = CAUSAL ? min(nk, q0 + 32 + diag) : nk;
+  const int T = kv_end > 0 ? (kv_end + 31) / 32 : 0;
+  const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1);
+
+  for (int j = 0; j < T; ++j) {
+    const int k0 = j * 32;
+    f32x16 st = f32x16{}, dpt = f32x16{};
+    {
+      const bool ok = k0 + x < nk;
+      const float* kr = K + khead + (size_t)(k0 + x) * D + col0 + 4 * h;
+      const float* vr = V + khead + (size_t)(k0 + x) * D + col0 + 4 * h;
+#pragma unroll
+      for (int u = 0; u < DSL / 8; ++u) {
+        const f32x4 ka = ok ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
+        const f32x4 va = ok ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
+        const f32x4 qa = HOLD ? qf[HOLD ? u : 0]
+                              : (my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0});
+        const f32x4 ga = HOLD ? gf[HOLD ? u : 0]
+                              : (my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          st = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[v], qa[v], st, 0, 0, 0);
+          dpt = __builtin_amdgcn_mfma_f32_32x32x2f32(va[v], ga[v], dpt, 0, 0, 0);
+        }
+      }
+    }
+    sum_waves<DS>(red, st, dpt, wave, lane);
+    const bool masked = (CAUSAL && k0 + 31 > q0 + diag) || (k0 + 32 > nk);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(fmaf(st[r], c2, nl2));
+      if (masked && k0 + 8 * (r >> 2) + 4 * h + (r & 3) > lim) p = 0.f;
+      st[r] = p * (dpt[r] + nd);
+    }
+    // dQ^T += K^T dS^T over the tile's 32 keys
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      float kv[NB];
+      load_nb<NB>(K + khead + (size_t)key * D + col0 + NB * x, key < nk, kv);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) dq[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[b], st[r], dq[b], 0, 0, 0);
+    }
+  }
+  if (my_q < Nq) {
+    float* qr = dQ + head + (size_t)my_q * D + col0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) qr[NB * i + b] = dq[b][r] * scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 size_t padded_rows(long long BH, int N) { return (size_t)BH * (size_t)((N + kRowPad - 1) / kRowPad * kRowPad); }
 
@@ -472,6 +773,46 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   return hipGetLastError();
 }
 
+template <int DSL, int DS>
+hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv, int BH,
+                          int H, int Nq, int Nk, const int* k_len, float scale, bool causal,
+                          float* ws, hipStream_t st) {
+  constexpr int D = DSL * DS;
+  const int n_pad = (Nq + kRowPad - 1) / kRowPad * kRowPad;
+  const long long prow = (long long)BH * n_pad;
+  float* nl = ws;
+  float* nd = ws + prow;
+  {
+    constexpr int TPR = D / 4 < 64 ? D / 4 : 64, RPB = 256 / TPR;
+    hipLaunchKernelGGL((attn_bwd_prep_f32<D>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256),
+                       0, st, (const float*)o, (const float*)dout, lse, nl, nd, Nq, n_pad, prow,
+                       1.f / scale);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  const int nkb = (Nk + 31) / 32, nqb = (Nq + 31) / 32;
+  const int tk = nkb * BH, tq = nqb * BH;
+  const dim3 blk(64 * DS);
+  if (causal) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DS, true>), dim3(tk), blk, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
+                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DS, true>), dim3(tq), blk, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
+                       Nk, H, k_len, n_pad, nqb, tq, scale);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DS, false>), dim3(tk), blk, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
+                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DS, false>), dim3(tq), blk, 0, st, (const float*)q,
+                       (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
+                       Nk, H, k_len, n_pad, nqb, tq, scale);
+  }
+  return hipGetLastError();
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -480,7 +821,9 @@ extern "C" {
 
 int fa_bwd_supported(int d, int dtype, int causal) {
   if (causal != 0 && causal != 1) return 0;
-  return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16) && (d == 64 || d == 128);
+  if (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16) return d == 64 || d == 128;
+  if (dtype == FA_DTYPE_FP32) return d == 64 || d == 128 || d == 256 || d == 512 || d == 1024;
+  return 0;
 }
 
 size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
@@ -510,7 +853,8 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
     return FA_ERR_UNSUPPORTED;
   if (!fa_bwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
   // per-head byte offsets (plus one tile of slack) fit the 32-bit buffer offsets
-  if (((long long)(Nq > Nk ? Nq : Nk) + 128) * d * 2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  const long long elem = dtype == FA_DTYPE_FP32 ? 4 : 2;
+  if (((long long)(Nq > Nk ? Nq : Nk) + 128) * d * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < fa_bwd_ex_workspace_size(B, H, Nq, Nk, d, causal, dtype))
     return FA_ERR_INVALID_ARG;
   for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv,
@@ -521,12 +865,21 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   const int bh = (int)BH;
   float* ws = (float*)workspace;
   hipError_t e;
-  if (dtype == FA_DTYPE_BF16)
+  if (dtype == FA_DTYPE_BF16) {
     e = d == 64 ? launch_bwd<Bf16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
                 : launch_bwd<Bf16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
-  else
+  } else if (dtype == FA_DTYPE_FP16) {
     e = d == 64 ? launch_bwd<F16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
                 : launch_bwd<F16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+  } else {
+    switch (d) {
+      case 64: e = launch_bwd_f32<64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
+      case 128: e = launch_bwd_f32<128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
+      case 256: e = launch_bwd_f32<128, 2>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
+      case 512: e = launch_bwd_f32<128, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
+      default: e = launch_bwd_f32<256, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
+    }
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

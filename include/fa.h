@@ -183,10 +183,12 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
  *                      formulas above use them as given).
  *   lse             : device pointer, [B][H][N] fp32 (natural log).
  *   dq, dk, dv      : device pointers, [B][H][N][d] of `dtype`, written
- *                     (rounded from fp32 to nearest even).  They must not
+ *                     (fp32, or rounded from fp32 to nearest even for the
+ *                     16-bit types).  They must not
  *                     overlap the inputs or each other.
  *   B, H, N, d, scale, causal, dtype : as for fa_fwd.  Supported: bf16 and
- *                     fp16 with d = 64 or 128.
+ *                     fp16 with d = 64 or 128; fp32 with d = 64, 128, 256,
+ *                     512 or 1024.
  *   workspace       : device pointer, 16-byte aligned, at least
  *                     fa_bwd_workspace_size(...) bytes (else
  *                     FA_ERR_INVALID_ARG); contents on entry ignored, on
@@ -197,7 +199,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
  * Asynchronous on `stream`; allocates nothing.  Every argument is checked
  * before any HIP call; on an error code nothing is launched and no output is
  * written.  Arithmetic: products of 16-bit operands accumulate in fp32; P and
- * dS are rounded to the element type before their products.  No atomics: the
+ * dS are rounded to the element type before their products.  fp32 operands
+ * take fp32 products throughout (no reduced-precision inputs).  No atomics: the
  * result is bitwise reproducible run to run.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -23,6 +23,7 @@ TOL = {
 TOL_BWD = {
     torch.bfloat16: dict(max_rel=2e-2, mean_rel=2e-3),
     torch.float16: dict(max_rel=4e-3, mean_rel=4e-4),
+    torch.float32: dict(max_rel=1e-4, mean_rel=1e-5),
 }
 
 

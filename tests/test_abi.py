@@ -115,14 +115,18 @@ def test_bwd_supported_table_and_workspace_size():
         for d in (64, 128):
             assert fa.fa_bwd_supported(d, dt, 0) and fa.fa_bwd_supported(d, dt, 1)
         assert not fa.fa_bwd_supported(256, dt, 0)
-    assert not fa.fa_bwd_supported(64, fa.FA_DTYPE_FP32, 0)
+    for d in (64, 128, 256, 512, 1024):
+        assert fa.fa_bwd_supported(d, fa.FA_DTYPE_FP32, 0) and fa.fa_bwd_supported(d, fa.FA_DTYPE_FP32, 1)
+    for d in (32, 96, 2048):
+        assert not fa.fa_bwd_supported(d, fa.FA_DTYPE_FP32, 0)
     assert not fa.fa_bwd_supported(64, fa.FA_DTYPE_BF16, 2)
     # two fp32 statistics per row, rows padded to a multiple of 32
     assert fa.fa_bwd_workspace_size(2, 3, 100, 64, 1, fa.FA_DTYPE_BF16) == 2 * 6 * 128 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 32, 128, 0, fa.FA_DTYPE_FP16) == 2 * 32 * 4
     assert fa.fa_bwd_workspace_size(0, 1, 16, 64, 0, fa.FA_DTYPE_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 16, 96, 0, fa.FA_DTYPE_BF16) == 0
-    assert fa.fa_bwd_workspace_size(1, 1, 16, 64, 0, fa.FA_DTYPE_FP32) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 16, 1024, 0, fa.FA_DTYPE_FP32) == 2 * 32 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 16, 48, 0, fa.FA_DTYPE_FP32) == 0
 
 
 @pytest.mark.parametrize("kw", [
@@ -135,7 +139,7 @@ def test_bwd_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(d=96), dict(dtype=fa.FA_DTYPE_FP32), dict(dtype=9), dict(q=FAKE + 8),
+    dict(d=96), dict(dtype=fa.FA_DTYPE_FP32, d=32), dict(dtype=9), dict(q=FAKE + 8),
     dict(dk=FAKE + 2), dict(ws=FAKE + 4),
 ])
 def test_bwd_unsupported_configurations(kw):
@@ -196,7 +200,7 @@ def test_bwd_ex_checks_arguments_first():
                             a["causal"], a["dtype"], a["k_len"], a["ws"], a["ws_bytes"], None)
     for kw in (dict(Nq=0), dict(Nk=0), dict(dk=None), dict(ws=None), dict(ws_bytes=4), dict(causal=5)):
         assert run(**kw) == fa.FA_ERR_INVALID_ARG, kw
-    for kw in (dict(k_len=FAKE + 1), dict(d=32), dict(dtype=fa.FA_DTYPE_FP32)):
+    for kw in (dict(k_len=FAKE + 1), dict(d=32), dict(dtype=fa.FA_DTYPE_FP32, d=2048)):
         assert run(**kw) == fa.FA_ERR_UNSUPPORTED, kw
     assert fa.fa_bwd_ex_workspace_size(2, 3, 100, 7, 64, 1, fa.FA_DTYPE_BF16) == 2 * 6 * 128 * 4
     assert fa.fa_bwd_ex_workspace_size(2, 3, 100, 100, 64, 1, fa.FA_DTYPE_BF16) == \

@@ -19,7 +19,7 @@ from exact_attention_29_amd.inputs import WORKLOADS, make_dout, make_qkv, worklo
 from tests import parity
 
 pytestmark = pytest.mark.gpu
-DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -117,14 +117,63 @@ def test_rejected_calls_raise():
     q = torch.zeros(1, 1, 16, 64, device="cuda", dtype=torch.float32)
     o, lse = fa.attention(q, q, q)
     with pytest.raises(ValueError):
-        fa.attention_bwd(q, q, q, o, lse, q)  # fp32 has no gradient kernels
+        fa.attention_bwd(q, q, q, o, lse, q.to(torch.bfloat16))  # mixed dtypes
     qb = q.to(torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attention_bwd(qb, qb, qb, qb, lse[:, :, :8], qb)
+    q2 = torch.zeros(1, 1, 16, 2048, device="cuda", dtype=torch.float32)
+    with pytest.raises(ValueError):  # no gradient kernel for d = 2048
+        fa.attention_bwd(q2, q2, q2, q2, lse, q2)
+
+
+def check_one_key(dq, dk, q, k, v, g, scale, rq, rk):
+    """fp32 problems with one key (Nk = 1): P = 1 on every kept pair and
+    dS = dP - delta = 0, so dq and dk vanish identically (the oracle's are
+    exact zeros) and the GPU's are fp32 rounding of the two cancelling dot
+    products dO.v and dO.o.  Each has error at most gamma_d sum |dO||v|
+    (gamma_d ~ d u, the standard bound for a dot product of length d); o = P v
+    adds a few ulp of v, and exp2 a few of P: |dS_i| <= (2d + 8) u sum|dO_i| 2|v|
+    with u = 2^-24, dq_i = scale dS_i k and dk = scale sum_i dS_i q_i."""
+    assert np.abs(rq).max() == 0 and np.abs(rk).max() == 0
+    d = q.shape[-1]
+    u = 2.0 ** -24
+    dS = (2 * d + 8) * u * (g.double().abs() * 2 * v.double().abs()).sum(-1, keepdim=True)
+    bq = scale * dS * k.double().abs()
+    bk = scale * (dS * q.double().abs()).sum(-2, keepdim=True)
+    aq, ak = dq.cpu().double().abs(), dk.cpu().double().abs()
+    print("one key: |dq|/bound", float((aq / bq).max()), "|dk|/bound", float((ak / bk).max()))
+    assert torch.all(aq <= bq) and torch.all(ak <= bk)
+
+
+# ------------------------------------------------------------------ fp32
+# fp32 inputs run every product in full fp32 (v_mfma_f32_32x32x2_f32): the
+# only error sources are fp32 rounding of the sums and of exp2, so the
+# gradients are held to 1e-4 of their scale (as the fp32 forward output is
+# held to 1e-4), with a mean bound ten times tighter.
+FP32 = [(d, causal, N) for d in (64, 128, 256, 512, 1024) for causal in (False, True)
+        for N in (1, 65, 200)]
+
+
+@pytest.mark.parametrize("d,causal,N", FP32)
+def test_fp32_shapes_match_gradient_oracle(d, causal, N):
+    seed = 6000 + 7 * N + d + int(causal)
+    B, H = (2, 3) if d <= 256 else (1, 2)
+    q, k, v = make_qkv(B, H, N, d, "fp32", seed)
+    g = make_dout(B, H, N, d, "fp32", seed + 1)
+    scale = 1 / math.sqrt(d)
+    dq, dk, dv = run(q, k, v, g, causal, scale)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, g, scale, causal)
+    if N == 1:
+        check_one_key(dq, dk, q, k, v, g, scale, rq, rk)
+        check(errors(dv, rv), torch.float32, "dv")
+        return
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        check(errors(got, ref), torch.float32, name)
 
 
 # ------------------------------------------------------------------ unequal lengths, key padding
-@pytest.mark.parametrize("dt,d", [("bf16", 64), ("bf16", 128), ("fp16", 128)])
+@pytest.mark.parametrize("dt,d", [("bf16", 64), ("bf16", 128), ("fp16", 128), ("fp32", 64),
+                                  ("fp32", 512)])
 @pytest.mark.parametrize("Nq,Nk,k_len", [(77, 300, None), (300, 77, None), (129, 1, None),
                                          (190, 333, [333, 150, 0]), (64, 64, [40, 64, 1])])
 @pytest.mark.parametrize("causal", [False, True])
@@ -141,8 +190,12 @@ def test_unequal_lengths_and_padding_match_gradient_oracle(dt, d, Nq, Nk, k_len,
     dq, dk, dv = fa.attention_bwd(qc, kc, vc, o, lse, gc, causal=causal, scale=scale, k_len=kl)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_bwd_ex(q, k, v, g, scale, causal, k_len)
+    vanish = dt == "fp32" and Nk == 1  # see check_one_key
+    if vanish:
+        check_one_key(dq, dk, q, k, v, g, scale, rq, rk)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        check(errors(got, ref), DT[dt], name)
+        if not (vanish and name != "dv"):
+            check(errors(got, ref), DT[dt], name)
     # structural zeros are exact: keys past a batch's count (no query keeps
     # them) and query rows that keep no key
     lens = [Nk] * B if k_len is None else [min(max(x, 0), Nk) for x in k_len]
