@@ -35,6 +35,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <initializer_list>
 
 #include "fa.h"
@@ -525,13 +526,15 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int H,
-    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale) {
+    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale, int n_split,
+    float* __restrict__ part, long long part_stride) {
   constexpr int D = DSL * DS, NB = DSL / 32;
   __shared__ f32x16 red[DS > 1 ? 2 * DS * 64 : 1];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = lane & 31, h = lane >> 5;
   const int item = xcd_remap(blockIdx.x, total);
-  const int bh = item / n_kblocks, kb = item % n_kblocks;
+  const int split = item % n_split, work = item / n_split;  // a block's splits are neighbours
+  const int bh = work / n_kblocks, kb = work % n_kblocks;
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernels
   const int diag = nk - Nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
@@ -560,11 +563,15 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
   const float* nl_row = NL + (size_t)bh * n_pad;
   const float* nd_row = ND + (size_t)bh * n_pad;
   const int nqt = (Nq + 31) / 32;
-  const int qt0 = k0 >= nk ? nqt : CAUSAL ? max(0, k0 - diag) / 32 : 0;
+  const int qt_first = k0 >= nk ? nqt : CAUSAL ? max(0, k0 - diag) / 32 : 0;
+  // this workgroup's share of the block's query tiles (all of them unsplit)
+  const int span = nqt - qt_first;
+  const int qt0 = qt_first + (int)((long long)span * split / n_split);
+  const int qt1 = qt_first + (int)((long long)span * (split + 1) / n_split);
   const bool edge_k = k0 + 31 >= nk;  // some keys of the block are padding
   const int lim = my_k >= nk ? 0x7fffffff : CAUSAL ? my_k - diag : -0x7fffffff;
 
-  for (int t = qt0; t < nqt; ++t) {
+  for (int t = qt0; t < qt1; ++t) {
     const int q0 = t * 32;
     f32x16 s = f32x16{}, dp = f32x16{};
     {
@@ -618,8 +625,11 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
     }
   }
   if (my_k < Nk) {  // every key row, those past the valid keys as zeros
-    float* kr = dK + khead + (size_t)my_k * D + col0;
-    float* vr = dV + khead + (size_t)my_k * D + col0;
+    // split: partial sums to the workspace, dK parts then dV parts
+    float* kout = part ? part + (size_t)split * part_stride : dK;
+    float* vout = part ? part + (size_t)(n_split + split) * part_stride : dV;
+    float* kr = kout + khead + (size_t)my_k * D + col0;
+    float* vr = vout + khead + (size_t)my_k * D + col0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * h + (r & 3);
@@ -639,14 +649,16 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     float* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
-    int n_qblocks, int total, float scale) {
+    int n_qblocks, int total, float scale, int n_split, float* __restrict__ part,
+    long long part_stride) {
   constexpr int D = DSL * DS, NB = DSL / 32;
   __shared__ f32x16 red[DS > 1 ? 2 * DS * 64 : 1];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = lane & 31, h = lane >> 5;
   const int item = xcd_remap(blockIdx.x, total);
-  const int bh = item / n_qblocks;
-  int qb = item % n_qblocks;
+  const int split = item % n_split, work = item / n_split;
+  const int bh = work / n_qblocks;
+  int qb = work % n_qblocks;
   if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
   const int diag = nk - Nq;
@@ -675,9 +687,10 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
   for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
   const int kv_end = CAUSAL ? min(nk, q0 + 32 + diag) : nk;
   const int T = kv_end > 0 ? (kv_end + 31) / 32 : 0;
+  const int j0 = (int)((long long)T * split / n_split), j1 = (int)((long long)T * (split + 1) / n_split);
   const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1);
 
-  for (int j = 0; j < T; ++j) {
+  for (int j = j0; j < j1; ++j) {
     const int k0 = j * 32;
     f32x16 st = f32x16{}, dpt = f32x16{};
     {
@@ -718,7 +731,8 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
     }
   }
   if (my_q < Nq) {
-    float* qr = dQ + head + (size_t)my_q * D + col0;
+    float* qout = part ? part + (size_t)split * part_stride : dQ;  // split: a partial sum
+    float* qr = qout + head + (size_t)my_q * D + col0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * h + (r & 3);
@@ -773,11 +787,52 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   return hipGetLastError();
 }
 
+// out = sum of n_split partial tensors of n floats each (stride apart), added
+// in split order so the result does not depend on timing.
+__global__ __launch_bounds__(256) void attn_bwd_sum_f32(const float* __restrict__ part,
+                                                        float* __restrict__ out, long long n,
+                                                        long long stride, int n_split) {
+  const long long n4 = n / 4;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * 256) {
+    f32x4 acc = ((const f32x4*)part)[i];
+    for (int sp = 1; sp < n_split; ++sp) acc += ((const f32x4*)(part + sp * stride))[i];
+    ((f32x4*)out)[i] = acc;
+  }
+}
+
+// fp32 problems with fewer key (query) blocks than compute units split each
+// block's query (key) tiles over `kv` (`q`) workgroups; their partial dK and
+// dV (dQ) go to the workspace after the row statistics and are summed by
+// attn_bwd_sum_f32.  Each split keeps at least two tiles.
+struct BwdSplit {
+  int kv = 1, q = 1;
+  size_t bytes = 0;  // partial sums
+};
+
+BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int d, int dtype) {
+  BwdSplit p;
+  if (dtype != FA_DTYPE_FP32) return p;
+  int cus = 0;
+  if (compute_units(&cus) != hipSuccess) return p;
+  const long long nkb = (Nk + 31) / 32, nqb = (Nq + 31) / 32;
+  auto pick = [&](long long blocks, long long tiles) {
+    if (blocks >= cus) return 1;
+    const long long sp = std::min<long long>((cus + blocks - 1) / blocks, tiles / 2);
+    return sp < 2 ? 1 : (int)sp;
+  };
+  p.kv = pick(nkb * BH, nqb);
+  p.q = pick(nqb * BH, nkb);
+  if (p.kv > 1) p.bytes += (size_t)p.kv * 2 * BH * Nk * d * sizeof(float);
+  if (p.q > 1) p.bytes += (size_t)p.q * BH * Nq * d * sizeof(float);
+  return p;
+}
+
 template <int DSL, int DS>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int BH,
                           int H, int Nq, int Nk, const int* k_len, float scale, bool causal,
-                          float* ws, hipStream_t st) {
+                          float* ws, const BwdSplit& sp, hipStream_t st) {
   constexpr int D = DSL * DS;
   const int n_pad = (Nq + kRowPad - 1) / kRowPad * kRowPad;
   const long long prow = (long long)BH * n_pad;
@@ -791,26 +846,42 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int nkb = (Nk + 31) / 32, nqb = (Nq + 31) / 32;
-  const int tk = nkb * BH, tq = nqb * BH;
+  const int tk = nkb * BH * sp.kv, tq = nqb * BH * sp.q;
+  const long long kstride = (long long)BH * Nk * D, qstride = (long long)BH * Nq * D;
+  float* kvpart = sp.kv > 1 ? ws + 2 * prow : nullptr;
+  float* qpart = sp.q > 1 ? ws + 2 * prow + (sp.kv > 1 ? 2 * sp.kv * kstride : 0) : nullptr;
   const dim3 blk(64 * DS);
   if (causal) {
     hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DS, true>), dim3(tk), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
-                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
+                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DS, true>), dim3(tq), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
-                       Nk, H, k_len, n_pad, nqb, tq, scale);
+                       Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
   } else {
     hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DS, false>), dim3(tk), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
-                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
+                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DS, false>), dim3(tq), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
-                       Nk, H, k_len, n_pad, nqb, tq, scale);
+                       Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
   }
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  auto sum = [&](const float* part, void* out, long long n, int n_split) {
+    const long long blocks = std::min<long long>((n / 4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(attn_bwd_sum_f32, dim3((unsigned)blocks), dim3(256), 0, st, part,
+                       (float*)out, n, n, n_split);
+    return hipGetLastError();
+  };
+  if (sp.kv > 1) {
+    if (hipError_t e = sum(kvpart, dk, kstride, sp.kv); e != hipSuccess) return e;
+    if (hipError_t e = sum(kvpart + sp.kv * kstride, dv, kstride, sp.kv); e != hipSuccess) return e;
+  }
+  if (sp.q > 1)
+    if (hipError_t e = sum(qpart, dq, qstride, sp.q); e != hipSuccess) return e;
+  return hipSuccess;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -830,7 +901,7 @@ size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal,
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !fa_bwd_supported(d, dtype, causal)) return 0;
   const long long BH = (long long)B * H;
   if (BH > (1LL << 24) || BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return 0;
-  return 2 * padded_rows(BH, Nq) * sizeof(float);
+  return 2 * padded_rows(BH, Nq) * sizeof(float) + plan_bwd_split(BH, Nq, Nk, d, dtype).bytes;
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) {
@@ -864,6 +935,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   hipStream_t st = (hipStream_t)stream;
   const int bh = (int)BH;
   float* ws = (float*)workspace;
+  const BwdSplit sp = plan_bwd_split(BH, Nq, Nk, d, dtype);
   hipError_t e;
   if (dtype == FA_DTYPE_BF16) {
     e = d == 64 ? launch_bwd<Bf16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
@@ -873,11 +945,11 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
                 : launch_bwd<F16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
   } else {
     switch (d) {
-      case 64: e = launch_bwd_f32<64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
-      case 128: e = launch_bwd_f32<128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
-      case 256: e = launch_bwd_f32<128, 2>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
-      case 512: e = launch_bwd_f32<128, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
-      default: e = launch_bwd_f32<256, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st); break;
+      case 64: e = launch_bwd_f32<64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      case 128: e = launch_bwd_f32<128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      case 256: e = launch_bwd_f32<128, 2>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      case 512: e = launch_bwd_f32<128, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      default: e = launch_bwd_f32<256, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
     }
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -1,13 +1,16 @@
 // fa_device.h -- device helpers shared by the forward and backward kernels of
 // libfa.so (gfx950): vector types, constants, element-type traits for the
 // 16-bit MFMA, cross-half reductions, the XCD-aware id remap, the LDS tile
-// layout and the buffer loads that write straight to LDS.
+// layout and the buffer loads that write straight to LDS; on the host, the
+// device's compute-unit count.
 #ifndef FA_DEVICE_H
 #define FA_DEVICE_H
 
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <atomic>
 
 namespace fa_dev {
 
@@ -165,6 +168,23 @@ __device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0
     const int el = key0 * D + (IS_V ? L::v_src(blk, lane) : L::k_src(blk, lane));
     dma16(desc, lds_tile + blk * 1024, el * 2);
   }
+}
+
+// host side
+// Compute units of the current device, queried once per device.
+inline hipError_t compute_units(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && (*cus = cache[dev].load(std::memory_order_relaxed)) > 0)
+    return hipSuccess;
+  if (hipError_t e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+      e != hipSuccess)
+    return e;
+  if (*cus <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
+  return hipSuccess;
 }
 
 }  // namespace fa_dev

@@ -750,21 +750,6 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
 
 // ---------------------------------------------------------------------------
 // host side
-// Compute units of the current device, queried once per device.
-hipError_t compute_units(int* cus) {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDevices && (*cus = cache[dev].load(std::memory_order_relaxed)) > 0)
-    return hipSuccess;
-  if (hipError_t e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
-      e != hipSuccess)
-    return e;
-  if (*cus <= 0) return hipErrorInvalidDevice;
-  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
-  return hipSuccess;
-}
 
 // Shape of one call: Nq query rows and Nk key rows per head, optional
 // per-batch valid key counts (device array, clamped to [0, Nk] on the GPU).

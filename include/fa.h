@@ -159,7 +159,10 @@ size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal,
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for this
  * problem: two fp32 row statistics per (batch, head, row), rows padded to a
- * multiple of 32.  0 for invalid or unsupported arguments.
+ * multiple of 32; for fp32 problems with fewer query or key blocks (32 rows)
+ * than the current device has compute units, also the fp32 partial sums of
+ * the split that spreads each block's work over several workgroups.  Depends
+ * on the current device.  0 for invalid or unsupported arguments.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
 
@@ -224,7 +227,8 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               size_t workspace_bytes, void* stream);
 
 /* Workspace of fa_bwd_ex: two fp32 statistics per (batch, head, query row),
- * rows padded to a multiple of 32; 0 for invalid or unsupported arguments. */
+ * rows padded to a multiple of 32, plus the partial sums of fa_bwd_workspace_size
+ * for small fp32 grids; 0 for invalid or unsupported arguments. */
 size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype);
 
 /* 1 when fa_bwd has kernels for (d, dtype, causal), else 0. */
