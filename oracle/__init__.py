@@ -67,6 +67,20 @@ def lib():
             ctypes.c_longlong, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_attn_rows_gen.restype = ctypes.c_int
+        L.oracle_attn_rows_gen.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_attn_bwd_gen.restype = ctypes.c_int
+        L.oracle_attn_bwd_gen.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+            ctypes.c_longlong, ctypes.c_longlong, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.oracle_thread_count.restype = ctypes.c_int
         L.oracle_thread_count.argtypes = [ctypes.c_int]
         L.oracle_load.restype = ctypes.c_double
@@ -124,21 +138,22 @@ def attention(q, k, v, scale: float, causal: bool, threads: int = 0):
 
 def attn_rows_ex(q, k, v, scale: float, causal: bool, rows=None, k_len=None, threads: int = 0):
     """Oracle attention for query and key sequences of different lengths,
-    with optional per-batch valid key counts (oracle.h, oracle_attn_rows_ex).
+    with optional per-batch valid key counts and a value head dim of its own
+    (oracle.h, oracle_attn_rows_gen).
 
-    q: host [B, H, Nq, d]; k, v: host [B, H, Nk, d], one dtype.  rows: flat
-    query-row ids (b*H + h)*Nq + i (None: all).  k_len: B valid key counts or
-    None.  Returns (o [n_rows, d], lse [n_rows]) float64 numpy arrays; rows
-    with no kept key give o = 0, lse = -inf.
+    q: host [B, H, Nq, dk]; k: [B, H, Nk, dk]; v: [B, H, Nk, dv], one dtype.
+    rows: flat query-row ids (b*H + h)*Nq + i (None: all).  k_len: B valid
+    key counts or None.  Returns (o [n_rows, dv], lse [n_rows]) float64 numpy
+    arrays; rows with no kept key give o = 0, lse = -inf.
     """
     q, k, v = _as_cpu(q), _as_cpu(k), _as_cpu(v)
-    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
-            or q.shape[3] != k.shape[3]:
-        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape[:3] != v.shape[:3] \
+            or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, dk], k [B, H, Nk, dk] and v [B, H, Nk, dv]")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _CODES:
         raise ValueError(f"unsupported dtype combination {q.dtype}/{k.dtype}/{v.dtype}")
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    B, H, Nq, dk = q.shape
+    Nk, d = k.shape[2], v.shape[3]
     if rows is None:
         rows = np.arange(B * H * Nq, dtype=np.int64)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
@@ -150,18 +165,18 @@ def attn_rows_ex(q, k, v, scale: float, causal: bool, rows=None, k_len=None, thr
     n = rows.shape[0]
     o = np.empty((n, d), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
-    rc = lib().oracle_attn_rows_ex(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), _CODES[q.dtype], B, H, Nq, Nk, d,
+    rc = lib().oracle_attn_rows_gen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _CODES[q.dtype], B, H, Nq, Nk, dk, d,
         float(scale), int(bool(causal)), None if kl is None else kl.ctypes.data,
         rows.ctypes.data, n, o.ctypes.data, lse.ctypes.data, int(threads))
     if rc != 0:
-        raise ValueError(f"oracle_attn_rows_ex failed with code {rc}")
+        raise ValueError(f"oracle_attn_rows_gen failed with code {rc}")
     return o, lse
 
 
 def attention_ex(q, k, v, scale: float, causal: bool, k_len=None, threads: int = 0):
-    """All rows of attn_rows_ex; returns (o [B,H,Nq,d], lse [B,H,Nq])."""
-    B, H, Nq, d = q.shape
+    """All rows of attn_rows_ex; returns (o [B,H,Nq,dv], lse [B,H,Nq])."""
+    B, H, Nq, d = q.shape[:3] + v.shape[3:]
     o, lse = attn_rows_ex(q, k, v, scale, causal, None, k_len, threads)
     return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
 
@@ -206,21 +221,24 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0):
 
 def attn_bwd_ex(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=None,
                 k_len=None, threads: int = 0):
-    """Oracle gradients for unequal lengths and key padding (oracle_attn_bwd_ex).
+    """Oracle gradients for unequal lengths, key padding and a value head dim
+    of its own (oracle_attn_bwd_gen).
 
-    q, dout: host [B, H, Nq, d]; k, v: host [B, H, Nk, d], one dtype.  q_rows:
-    flat ids (b*H + h)*Nq + i; k_rows: flat ids (b*H + h)*Nk + j (None: all).
-    k_len: B valid key counts or None.  Returns (dq [n_q, d], dk [n_k, d],
-    dv [n_k, d]) float64 numpy arrays.
+    q: host [B, H, Nq, dk]; k: [B, H, Nk, dk]; v: [B, H, Nk, dv]; dout:
+    [B, H, Nq, dv], one dtype.  q_rows: flat ids (b*H + h)*Nq + i; k_rows:
+    flat ids (b*H + h)*Nk + j (None: all).  k_len: B valid key counts or None.
+    Returns (dq [n_q, dk], dk [n_k, dk], dv [n_k, dv]) float64 numpy arrays.
     """
     q, k, v, dout = _as_cpu(q), _as_cpu(k), _as_cpu(v), _as_cpu(dout)
-    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape != dout.shape \
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or dout.dim() != 4 \
+            or k.shape[:3] != v.shape[:3] or dout.shape != q.shape[:3] + v.shape[3:] \
             or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
-        raise ValueError("q, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+        raise ValueError("q must be [B, H, Nq, dk], k [B, H, Nk, dk], v [B, H, Nk, dv] and "
+                         "dout [B, H, Nq, dv]")
     if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in _CODES:
         raise ValueError("q, k, v, dout must share one supported dtype")
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Nk, d_v = k.shape[2], v.shape[3]
     qr = np.arange(B * H * Nq, dtype=np.int64) if q_rows is None else q_rows
     kr = np.arange(B * H * Nk, dtype=np.int64) if k_rows is None else k_rows
     qr = np.ascontiguousarray(np.asarray(qr, dtype=np.int64))
@@ -232,23 +250,25 @@ def attn_bwd_ex(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=N
             raise ValueError("k_len must hold one count per batch")
     dq = np.empty((qr.shape[0], d), dtype=np.float64)
     dk = np.empty((kr.shape[0], d), dtype=np.float64)
-    dv = np.empty((kr.shape[0], d), dtype=np.float64)
-    rc = lib().oracle_attn_bwd_ex(
+    dv = np.empty((kr.shape[0], d_v), dtype=np.float64)
+    rc = lib().oracle_attn_bwd_gen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), _CODES[q.dtype],
-        B, H, Nq, Nk, d, float(scale), int(bool(causal)), None if kl is None else kl.ctypes.data,
+        B, H, Nq, Nk, d, d_v, float(scale), int(bool(causal)),
+        None if kl is None else kl.ctypes.data,
         qr.ctypes.data, qr.shape[0], kr.ctypes.data, kr.shape[0],
         dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(threads))
     if rc != 0:
-        raise ValueError(f"oracle_attn_bwd_ex failed with code {rc}")
+        raise ValueError(f"oracle_attn_bwd_gen failed with code {rc}")
     return dq, dk, dv
 
 
 def attention_bwd_ex(q, k, v, dout, scale: float, causal: bool, k_len=None, threads: int = 0):
-    """All rows of attn_bwd_ex; returns (dq [B,H,Nq,d], dk, dv [B,H,Nk,d])."""
+    """All rows of attn_bwd_ex; returns (dq [B,H,Nq,dk], dk [B,H,Nk,dk],
+    dv [B,H,Nk,dv])."""
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Nk, d_v = k.shape[2], v.shape[3]
     dq, dk, dv = attn_bwd_ex(q, k, v, dout, scale, causal, None, None, k_len, threads)
-    return dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d)
+    return dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d_v)
 
 
 def timed_attn_rows(q, k, v, scale, causal, rows, threads: int = 0):

@@ -58,7 +58,7 @@ int oracle_thread_count(int threads) {
 typedef struct {
   const void *q, *k, *v;
   int dtype;
-  long long H, Nq, Nk, d;
+  long long H, Nq, Nk, dk, dv; /* head dims: q and k rows dk, v and o rows dv */
   double scale;
   int causal;
   const long long* k_len; /* per-batch valid keys, or NULL (all Nk) */
@@ -68,19 +68,21 @@ typedef struct {
   long long next; /* shared work counter, advanced atomically */
 } job_t;
 
-/* One query row r = (b*H + h)*Nq + i, three passes.  `qrow` (d doubles) and
+/* One query row r = (b*H + h)*Nq + i, three passes.  `qrow` (dk doubles) and
  * `s` (Nk doubles) are this thread's scratch: s holds the row's scaled scores,
- * so passes 2 and 3 reuse the dot products of the score step.
+ * so passes 2 and 3 reuse the dot products of the score step.  The scores
+ * contract the dk columns of q and k; the output has the dv columns of v.
  * The kept keys J_i are a prefix 0 .. nkeys-1 of the head's keys: keys below
  * the batch's valid length L, and, when causal, at most i + (L - Nq). */
 static void one_row(const job_t* jb, long long r, double* qrow, double* s,
                     double* o, double* lse) {
-  const long long Nq = jb->Nq, Nk = jb->Nk, d = jb->d;
+  const long long Nq = jb->Nq, Nk = jb->Nk, dk = jb->dk, dv = jb->dv;
   const long long head = r / Nq;                 /* b*H + h */
   const long long i = r % Nq;                    /* query position */
   const long long b = head / jb->H;
-  const long long qbase = head * Nq * d;         /* this head's query rows */
-  const long long kbase = head * Nk * d;         /* this head's key / value rows */
+  const long long qbase = head * Nq * dk;        /* this head's query rows */
+  const long long kbase = head * Nk * dk;        /* this head's key rows */
+  const long long vbase = head * Nk * dv;        /* this head's value rows */
   long long L = jb->k_len ? jb->k_len[b] : Nk;   /* valid keys of this batch */
   if (L < 0) L = 0;
   if (L > Nk) L = Nk;
@@ -88,19 +90,19 @@ static void one_row(const job_t* jb, long long r, double* qrow, double* s,
   if (jb->causal && i + (L - Nq) + 1 < nkeys) nkeys = i + (L - Nq) + 1;
   if (nkeys < 0) nkeys = 0;
 
-  for (long long c = 0; c < d; ++c) o[c] = 0.0;
+  for (long long c = 0; c < dv; ++c) o[c] = 0.0;
   if (nkeys == 0) { /* no kept key: the empty sum, o = 0 and lse = ln 0 */
     *lse = -INFINITY;
     return;
   }
-  for (long long c = 0; c < d; ++c)
-    qrow[c] = oracle_load(jb->q, jb->dtype, qbase + i * d + c);
+  for (long long c = 0; c < dk; ++c)
+    qrow[c] = oracle_load(jb->q, jb->dtype, qbase + i * dk + c);
 
   /* scores s_j = scale * <q_i, k_j> for j in J_i */
   for (long long j = 0; j < nkeys; ++j) {
     double dot = 0.0;
-    for (long long c = 0; c < d; ++c)
-      dot += qrow[c] * oracle_load(jb->k, jb->dtype, kbase + j * d + c);
+    for (long long c = 0; c < dk; ++c)
+      dot += qrow[c] * oracle_load(jb->k, jb->dtype, kbase + j * dk + c);
     s[j] = jb->scale * dot;
   }
 
@@ -116,15 +118,15 @@ static void one_row(const job_t* jb, long long r, double* qrow, double* s,
   /* pass 3: o = sum (exp(s_j - m) / l) v_j */
   for (long long j = 0; j < nkeys; ++j) {
     const double w = exp(s[j] - m) / l;
-    for (long long c = 0; c < d; ++c)
-      o[c] += w * oracle_load(jb->v, jb->dtype, kbase + j * d + c);
+    for (long long c = 0; c < dv; ++c)
+      o[c] += w * oracle_load(jb->v, jb->dtype, vbase + j * dv + c);
   }
   *lse = m + log(l);
 }
 
 static void* worker(void* arg) {
   job_t* jb = (job_t*)arg;
-  double* qrow = (double*)malloc((size_t)jb->d * sizeof(double));
+  double* qrow = (double*)malloc((size_t)jb->dk * sizeof(double));
   double* s = (double*)malloc((size_t)jb->Nk * sizeof(double));
   if (!qrow || !s) {
     free(qrow);
@@ -134,7 +136,7 @@ static void* worker(void* arg) {
   for (;;) {
     long long t = __atomic_fetch_add(&jb->next, 1, __ATOMIC_RELAXED);
     if (t >= jb->n_rows) break;
-    one_row(jb, jb->rows[t], qrow, s, jb->o_out + t * jb->d, jb->lse_out + t);
+    one_row(jb, jb->rows[t], qrow, s, jb->o_out + t * jb->dv, jb->lse_out + t);
   }
   free(qrow);
   free(s);
@@ -155,8 +157,17 @@ int oracle_attn_rows_ex(const void* q, const void* k, const void* v, int dtype,
                         double scale, int causal, const long long* k_len,
                         const long long* rows, long long n_rows,
                         double* o_out, double* lse_out, int threads) {
+  return oracle_attn_rows_gen(q, k, v, dtype, B, H, Nq, Nk, d, d, scale, causal, k_len, rows,
+                              n_rows, o_out, lse_out, threads);
+}
+
+int oracle_attn_rows_gen(const void* q, const void* k, const void* v, int dtype,
+                         long long B, long long H, long long Nq, long long Nk, long long dk,
+                         long long dv, double scale, int causal, const long long* k_len,
+                         const long long* rows, long long n_rows,
+                         double* o_out, double* lse_out, int threads) {
   if (!q || !k || !v || !o_out || !lse_out || (n_rows > 0 && !rows)) return -1;
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || n_rows < 0) return -1;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || dk <= 0 || dv <= 0 || n_rows < 0) return -1;
   if (causal != 0 && causal != 1) return -1;
   if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return -1;
   const long long total = B * H * Nq;
@@ -164,7 +175,7 @@ int oracle_attn_rows_ex(const void* q, const void* k, const void* v, int dtype,
     if (rows[t] < 0 || rows[t] >= total) return -1;
   if (n_rows == 0) return 0;
 
-  job_t jb = {q, k, v, dtype, H, Nq, Nk, d, scale, causal, k_len, rows, n_rows,
+  job_t jb = {q, k, v, dtype, H, Nq, Nk, dk, dv, scale, causal, k_len, rows, n_rows,
               o_out, lse_out, 0};
   int nt = oracle_thread_count(threads);
   if (nt > n_rows) nt = (int)n_rows;

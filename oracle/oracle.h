@@ -89,6 +89,20 @@ int oracle_attn_rows_ex(const void* q, const void* k, const void* v, int dtype,
                         double* o_out, double* lse_out, int threads);
 
 /*
+ * oracle_attn_rows_gen -- oracle_attn_rows_ex with the value head dim apart
+ * from the query/key one (Q of shape (n, d_k), K (m, d_k), V (m, d_v):
+ * "Transformer Attention: A Mathematical Deep Dive", the scaled dot-product
+ * attention definition): q [B][H][Nq][dk], k [B][H][Nk][dk], v [B][H][Nk][dv];
+ * the scores contract the dk columns, o_out is [n_rows][dv].
+ * oracle_attn_rows_ex is this with dk = dv = d.
+ */
+int oracle_attn_rows_gen(const void* q, const void* k, const void* v, int dtype,
+                         long long B, long long H, long long Nq, long long Nk, long long dk,
+                         long long dv, double scale, int causal, const long long* k_len,
+                         const long long* rows, long long n_rows,
+                         double* o_out, double* lse_out, int threads);
+
+/*
  * oracle_attn_bwd -- gradients of the same attention (oracle_bwd.c):
  * for an upstream gradient dout = dL/do ([B][H][N][d], type `dtype`), the
  * gradients dL/dq of the query rows q_rows (flat ids (b*H + h)*N + i) and
@@ -117,6 +131,20 @@ int oracle_attn_bwd_ex(const void* q, const void* k, const void* v, const void* 
                        const long long* q_rows, long long n_q,
                        const long long* k_rows, long long n_k,
                        double* dq_out, double* dk_out, double* dv_out, int threads);
+
+/*
+ * oracle_attn_bwd_gen -- the gradients of oracle_attn_rows_gen's attention:
+ * q [B][H][Nq][dk], k [B][H][Nk][dk], v [B][H][Nk][dv], dout [B][H][Nq][dv];
+ * dq_out [n_q][dk], dk_out [n_k][dk], dv_out [n_k][dv].  dP_ij = <g_i, v_j>
+ * and D_i = <g_i, o_i> contract the dv columns, the scores and dq, dk the dk
+ * columns.  oracle_attn_bwd_ex is this with dk = dv = d.
+ */
+int oracle_attn_bwd_gen(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                        long long B, long long H, long long Nq, long long Nk, long long dk,
+                        long long dv, double scale, int causal, const long long* k_len,
+                        const long long* q_rows, long long n_q,
+                        const long long* k_rows, long long n_k,
+                        double* dq_out, double* dk_out, double* dv_out, int threads);
 
 /* Number of threads a call with `threads` would use. */
 int oracle_thread_count(int threads);

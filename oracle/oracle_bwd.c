@@ -33,7 +33,7 @@
 typedef struct {
   const void *q, *k, *v, *g;
   int dtype;
-  long long H, Nq, Nk, d;
+  long long H, Nq, Nk, d_qk, d_v; /* q, k rows have d_qk columns; v, o, g rows d_v */
   double scale;
   int causal;
   const long long* k_len; /* per-batch valid keys, or NULL (all Nk) */
@@ -81,9 +81,9 @@ static long long kept_keys(const bjob_t* jb, long long head, long long i) {
   return n < 0 ? 0 : n;
 }
 
-/* s_ij = scale * <q_i, k_j> of head `head` */
+/* s_ij = scale * <q_i, k_j> of head `head` (over the d_qk columns) */
 static double score(const bjob_t* jb, long long head, long long i, long long j) {
-  const long long d = jb->d, qb = head * jb->Nq * d, kb = head * jb->Nk * d;
+  const long long d = jb->d_qk, qb = head * jb->Nq * d, kb = head * jb->Nk * d;
   double dot = 0.0;
   for (long long c = 0; c < d; ++c)
     dot += ld(jb, jb->q, qb + i * d + c) * ld(jb, jb->k, kb + j * d + c);
@@ -93,8 +93,8 @@ static double score(const bjob_t* jb, long long head, long long i, long long j) 
 /* phase 0: lse_i and D_i = <g_i, o_i> of query row i of touched head slot hs
  * (an empty row: lse = -inf, o = 0, D = 0) */
 static void stats_row(const bjob_t* jb, long long hs, long long i, double* s, double* o) {
-  const long long Nq = jb->Nq, d = jb->d, head = jb->heads[hs];
-  const long long kb = head * jb->Nk * d;
+  const long long Nq = jb->Nq, d = jb->d_v, head = jb->heads[hs];
+  const long long kb = head * jb->Nk * d;  /* value rows (d_v columns) */
   const long long nkeys = kept_keys(jb, head, i);
   double m = -INFINITY, l = 0.0;
   for (long long j = 0; j < nkeys; ++j) {
@@ -113,18 +113,18 @@ static void stats_row(const bjob_t* jb, long long hs, long long i, double* s, do
   jb->D[hs * Nq + i] = Di;
 }
 
-/* dP_ij = <g_i, v_j> */
+/* dP_ij = <g_i, v_j> (over the d_v columns) */
 static double dprob(const bjob_t* jb, long long head, long long i, long long j) {
-  const long long d = jb->d, qb = head * jb->Nq * d, kb = head * jb->Nk * d;
+  const long long d = jb->d_v, qb = head * jb->Nq * d, kb = head * jb->Nk * d;
   double dot = 0.0;
   for (long long c = 0; c < d; ++c)
     dot += ld(jb, jb->g, qb + i * d + c) * ld(jb, jb->v, kb + j * d + c);
   return dot;
 }
 
-/* phase 1: dq of flat query row r = head*Nq + i */
+/* phase 1: dq of flat query row r = head*Nq + i (d_qk columns) */
 static void dq_row(const bjob_t* jb, long long t) {
-  const long long Nq = jb->Nq, d = jb->d, r = jb->q_rows[t];
+  const long long Nq = jb->Nq, d = jb->d_qk, r = jb->q_rows[t];
   const long long head = r / Nq, i = r % Nq, hs = head_slot(jb, head);
   const long long kb = head * jb->Nk * d;
   const long long nkeys = kept_keys(jb, head, i);
@@ -141,22 +141,22 @@ static void dq_row(const bjob_t* jb, long long t) {
 /* phase 2: dk and dv of flat key row r = head*Nk + j, summed over the query
  * rows that keep key j */
 static void dkv_row(const bjob_t* jb, long long t) {
-  const long long Nq = jb->Nq, Nk = jb->Nk, d = jb->d, r = jb->k_rows[t];
+  const long long Nq = jb->Nq, Nk = jb->Nk, d_qk = jb->d_qk, d_v = jb->d_v, r = jb->k_rows[t];
   const long long head = r / Nk, j = r % Nk, hs = head_slot(jb, head);
-  const long long qb = head * Nq * d;
-  double* dk = jb->dk + t * d;
-  double* dv = jb->dv + t * d;
-  for (long long c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
+  const long long qb = head * Nq * d_qk;  /* query rows */
+  const long long gb = head * Nq * d_v;   /* upstream-gradient rows */
+  double* dk = jb->dk + t * d_qk;
+  double* dv = jb->dv + t * d_v;
+  for (long long c = 0; c < d_qk; ++c) dk[c] = 0.0;
+  for (long long c = 0; c < d_v; ++c) dv[c] = 0.0;
   for (long long i = 0; i < Nq; ++i) {
     if (j >= kept_keys(jb, head, i)) continue;
     const double P = exp(score(jb, head, i, j) - jb->lse[hs * Nq + i]);
     const double dS = P * (dprob(jb, head, i, j) - jb->D[hs * Nq + i]);
-    for (long long c = 0; c < d; ++c) {
-      dv[c] += P * ld(jb, jb->g, qb + i * d + c);
-      dk[c] += dS * ld(jb, jb->q, qb + i * d + c);
-    }
+    for (long long c = 0; c < d_v; ++c) dv[c] += P * ld(jb, jb->g, gb + i * d_v + c);
+    for (long long c = 0; c < d_qk; ++c) dk[c] += dS * ld(jb, jb->q, qb + i * d_qk + c);
   }
-  for (long long c = 0; c < d; ++c) dk[c] *= jb->scale;
+  for (long long c = 0; c < d_qk; ++c) dk[c] *= jb->scale;
 }
 
 static void* bworker(void* arg) {
@@ -165,7 +165,7 @@ static void* bworker(void* arg) {
   double* o = NULL;
   if (jb->phase == 0) {
     s = (double*)malloc((size_t)jb->Nk * sizeof(double));
-    o = (double*)malloc((size_t)jb->d * sizeof(double));
+    o = (double*)malloc((size_t)jb->d_v * sizeof(double));
     if (!s || !o) {
       free(s);
       free(o);
@@ -232,8 +232,19 @@ int oracle_attn_bwd_ex(const void* q, const void* k, const void* v, const void* 
                        const long long* q_rows, long long n_q,
                        const long long* k_rows, long long n_k,
                        double* dq_out, double* dk_out, double* dv_out, int threads) {
+  return oracle_attn_bwd_gen(q, k, v, dout, dtype, B, H, Nq, Nk, d, d, scale, causal, k_len,
+                             q_rows, n_q, k_rows, n_k, dq_out, dk_out, dv_out, threads);
+}
+
+int oracle_attn_bwd_gen(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                        long long B, long long H, long long Nq, long long Nk, long long d_qk,
+                        long long d_v, double scale, int causal, const long long* k_len,
+                        const long long* q_rows, long long n_q,
+                        const long long* k_rows, long long n_k,
+                        double* dq_out, double* dk_out, double* dv_out, int threads) {
   if (!q || !k || !v || !dout) return -1;
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || n_q < 0 || n_k < 0) return -1;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d_qk <= 0 || d_v <= 0 || n_q < 0 || n_k < 0)
+    return -1;
   if ((n_q > 0 && (!q_rows || !dq_out)) || (n_k > 0 && (!k_rows || !dk_out || !dv_out)))
     return -1;
   if (causal != 0 && causal != 1) return -1;
@@ -265,7 +276,8 @@ int oracle_attn_bwd_ex(const void* q, const void* k, const void* v, const void* 
   bjob_t jb;
   memset(&jb, 0, sizeof jb);
   jb.q = q; jb.k = k; jb.v = v; jb.g = dout; jb.dtype = dtype;
-  jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.d = d; jb.scale = scale; jb.causal = causal;
+  jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.d_qk = d_qk; jb.d_v = d_v;
+  jb.scale = scale; jb.causal = causal;
   jb.k_len = k_len;
   jb.heads = heads; jb.n_heads = u; jb.lse = lse; jb.D = D;
   jb.q_rows = q_rows; jb.k_rows = k_rows; jb.n_q = n_q; jb.n_k = n_k;
