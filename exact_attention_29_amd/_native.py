@@ -56,6 +56,14 @@ def library():
             ctypes.c_size_t, ctypes.c_void_p]
         L.fa_fwd_ex_workspace_size.restype = ctypes.c_size_t
         L.fa_fwd_ex_workspace_size.argtypes = [ctypes.c_int] * 7
+        L.fa_fwd_gen.restype = ctypes.c_int
+        L.fa_fwd_gen.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_size_t, ctypes.c_void_p]
+        L.fa_fwd_gen_workspace_size.restype = ctypes.c_size_t
+        L.fa_fwd_gen_workspace_size.argtypes = [ctypes.c_int] * 8
+        L.fa_fwd_gen_supported.restype = ctypes.c_int
+        L.fa_fwd_gen_supported.argtypes = [ctypes.c_int] * 4
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
@@ -126,37 +134,57 @@ def fa_fwd_ex_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, causal: i
                                                   int(causal), int(dtype)))
 
 
+def fa_fwd_gen(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
+               d_qk: int, d_v: int, scale: float, causal: int, dtype: int, k_len: int,
+               workspace: int, workspace_bytes: int, stream: int) -> int:
+    """The raw C entry point with separate query/key and value head dims."""
+    return library().fa_fwd_gen(q, k, v, o, lse, B, H, Nq, Nk, d_qk, d_v, ctypes.c_float(scale),
+                                int(causal), int(dtype), k_len, workspace,
+                                int(workspace_bytes), stream)
+
+
+def fa_fwd_gen_workspace_size(B: int, H: int, Nq: int, Nk: int, d_qk: int, d_v: int,
+                              causal: int, dtype: int) -> int:
+    return int(library().fa_fwd_gen_workspace_size(int(B), int(H), int(Nq), int(Nk), int(d_qk),
+                                                   int(d_v), int(causal), int(dtype)))
+
+
+def fa_fwd_gen_supported(d_qk: int, d_v: int, dtype: int, causal: int) -> bool:
+    return bool(library().fa_fwd_gen_supported(int(d_qk), int(d_v), int(dtype), int(causal)))
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               scale: float | None = None, out: torch.Tensor | None = None,
               lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
               split_keys: bool = True, k_len: torch.Tensor | None = None):
     """O = softmax(scale * Q K^T) V and the per-row log-sum-exp, on the GPU.
 
-    q: contiguous device tensor [B, H, Nq, d]; k, v: [B, H, Nk, d], one
-    dtype.  k_len: optional int32 device tensor [B] of valid key counts (key
-    padding).  scale defaults to 1/sqrt(d).  Returns (o [B,H,Nq,d] in q's
-    dtype, lse [B,H,Nq] fp32); rows with no kept key give o = 0, lse = -inf.
-    The launch is asynchronous on `stream` (default: torch's current
-    stream).  Equal lengths without k_len run through fa_fwd (fa_fwd_ws when
-    split_keys and the library would split fp32 keys over ranges; the
-    workspace comes from torch's allocator on `stream`); other shapes through
-    fa_fwd_ex.
+    q: contiguous device tensor [B, H, Nq, d]; k: [B, H, Nk, d]; v:
+    [B, H, Nk, dv] (dv may differ from d), one dtype.  k_len: optional int32
+    device tensor [B] of valid key counts (key padding).  scale defaults to
+    1/sqrt(d).  Returns (o [B,H,Nq,dv] in q's dtype, lse [B,H,Nq] fp32); rows
+    with no kept key give o = 0, lse = -inf.  The launch is asynchronous on
+    `stream` (default: torch's current stream).  Equal lengths and head dims
+    without k_len run through fa_fwd (fa_fwd_ws when split_keys and the
+    library would split fp32 keys over ranges; the workspace comes from
+    torch's allocator on `stream`); other shapes through fa_fwd_ex, and
+    unequal head dims through fa_fwd_gen.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [B, H, N, d]")
-    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
-            or q.shape[3] != k.shape[3]:
-        raise ValueError(f"q must be [B, H, Nq, d] and k, v [B, H, Nk, d], got "
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape[:3] != v.shape[:3] \
+            or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q must be [B, H, Nq, d], k [B, H, Nk, d] and v [B, H, Nk, dv], got "
                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtypes {q.dtype}, {k.dtype}, {v.dtype}")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
     B, H, N, d = q.shape
-    Nk = k.shape[2]
+    Nk, dv = k.shape[2], v.shape[3]
     if k_len is not None:
         if not isinstance(k_len, torch.Tensor) or k_len.dtype != torch.int32 \
                 or k_len.shape != (B,) or not k_len.is_contiguous() or k_len.device != q.device:
@@ -164,10 +192,10 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, H, N, dv) or out.dtype != q.dtype or not out.is_contiguous() \
             or out.device != q.device:
-        raise ValueError("out must be a contiguous tensor like q")
+        raise ValueError("out must be a contiguous tensor [B, H, Nq, dv] of q's dtype")
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
@@ -176,6 +204,24 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     code = _DTYPE_CODE[q.dtype]
+    if dv != d:
+        with torch.cuda.device(q.device):
+            ws_bytes = fa_fwd_gen_workspace_size(B, H, N, Nk, d, dv, int(bool(causal)), code) \
+                if split_keys else 0
+            ws = None
+            if ws_bytes:
+                with torch.cuda.stream(stream):
+                    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            st = fa_fwd_gen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, N, Nk, d, dv, float(scale), int(bool(causal)),
+                            code, None if k_len is None else k_len.data_ptr(),
+                            None if ws is None else ws.data_ptr(), ws_bytes, stream.cuda_stream)
+            if ws is not None:
+                ws.record_stream(stream)
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_gen") if st == FA_ERR_HIP else ValueError(
+                f"fa_fwd_gen: {fa_status_string(st)} (status {st})")
+        return out, lse
     if Nk != N or k_len is not None:
         with torch.cuda.device(q.device):
             ws_bytes = fa_fwd_ex_workspace_size(B, H, N, Nk, d, int(bool(causal)), code) \

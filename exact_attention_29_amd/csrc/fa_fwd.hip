@@ -120,23 +120,28 @@ __device__ __forceinline__ void leave_launch(int slot) {
 //     give lane (d = lane%32, h) the same eight keys for its column d.
 //   O^T (accumulator): block b, register r of lane (q, h) holds
 //     O[q][32b + 8*(r/4) + 4h + r%4].
-template <class TT, int D, bool CAUSAL, int NW, int NS, bool PERSIST>
+template <class TT, int DK, int DV, bool CAUSAL, int NW, int NS, bool PERSIST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Nq, int Nk, int H, const int* __restrict__ k_len, int n_qtiles, int total_items, int slot,
     float scale) {
+  // DK: head dim of Q and K (the scores); DV: head dim of V and O
   constexpr int BR = 32 * NW, BC = 64;
-  using LY = TileLayout<D>;
-  constexpr int TB = LY::BYTES, CG = LY::CG;
-  // DMA instructions one wave issues for one full stage (K and V tiles)
-  constexpr int NDMA = 2 * LY::BLOCKS / NW;
-  static_assert(2 * LY::BLOCKS % NW == 0 && NS >= 2, "stages split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * 2 * TB];  // [stage buffer][K, V]
+  using LK = TileLayout<DK>;
+  using LV = TileLayout<DV>;
+  constexpr int TBK = LK::BYTES, TBV = LV::BYTES, CGK = LK::CG, CGV = LV::CG;
+  constexpr int SB = TBK + TBV;  // bytes of one stage (K tile, then V tile)
+  // DMA instructions one wave issues for a K tile and for a V tile
+  constexpr int NDK = LK::BLOCKS / NW, NDV = LV::BLOCKS / NW;
+  static_assert(LK::BLOCKS % NW == 0 && LV::BLOCKS % NW == 0 && NS >= 2,
+                "stages split evenly over the waves");
+  static_assert(DK == DV || NS == 2, "more than two stages only with equal head dims");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SB];  // [stage buffer][K, V]
   // O staging in the epilogue: per wave 32 rows x 64 columns (bf16) at a
   // 144-byte row stride (16-byte aligned rows, writes spread over the banks)
   constexpr int kOStageRow = 144, kOStageBytes = 32 * kOStageRow;
-  static_assert(NW * kOStageBytes <= NS * 2 * TB && D % 64 == 0, "O staging fits the stage buffers");
+  static_assert(NW * kOStageBytes <= NS * SB && DV % 64 == 0, "O staging fits the stage buffers");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
@@ -159,15 +164,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // query row is aligned with the last valid key)
     const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
     const int diag = nk - Nq;
-    const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+    const size_t qhead = (size_t)bh * Nq * DK, ohead = (size_t)bh * Nq * DV;
+    const size_t khead = (size_t)bh * Nk * DK, vhead = (size_t)bh * Nk * DV;
     const int q_first = qt * BR + 32 * wave;
     const int my_q = q_first + lq;
 
-    u32x4 qf[D / 16];
+    u32x4 qf[DK / 16];
     {
-      const uint16_t* qrow = Q + head + (size_t)my_q * D + 8 * hf;
+      const uint16_t* qrow = Q + qhead + (size_t)my_q * DK + 8 * hf;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c)
+      for (int c = 0; c < DK / 16; ++c)
         qf[c] = (my_q < Nq) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
     }
 
@@ -177,32 +183,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int my_T = CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
 
     const uint16_t* const kbase = K + khead;
-    const uint16_t* const vbase = V + khead;
+    const uint16_t* const vbase = V + vhead;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
     // stage st in [-1, T-1] = (K tile st+1, V tile st) into buffer (st+1) % NS.
     // Each tile gets a descriptor starting at its first key row (scalar
     // arithmetic), so the per-lane offsets are the same for every tile; the
     // record count ends at the last valid key, so rows past it read as zero.
     auto load_stage = [&](int st) {
-      const unsigned base = lds0 + ((st + 1) % NS) * 2 * TB;
+      const unsigned base = lds0 + ((st + 1) % NS) * SB;
       if (st + 1 < T) {
         const int k0 = (st + 1) * BC;
-        dma_tile<D, false, NW>(buffer_desc(kbase + (size_t)k0 * D, (unsigned)(nk - k0) * D * 2), base, 0, wave, lane);
+        dma_tile<DK, false, NW>(buffer_desc(kbase + (size_t)k0 * DK, (unsigned)(nk - k0) * DK * 2), base, 0, wave, lane);
       }
       if (st >= 0) {
         const int k0 = st * BC;
-        dma_tile<D, true, NW>(buffer_desc(vbase + (size_t)k0 * D, (unsigned)(nk - k0) * D * 2), base + TB, 0, wave, lane);
+        dma_tile<DV, true, NW>(buffer_desc(vbase + (size_t)k0 * DV, (unsigned)(nk - k0) * DV * 2), base + TBK, 0, wave, lane);
       }
     };
     auto stage_buf = [&](int st) { return (st + 1) % NS; };
-    const int k_lane = (lq >> 4) * CG * 1024 + (hf * 16 + (lq & 15)) * 16;
+    const int k_lane = (lq >> 4) * CGK * 1024 + (hf * 16 + (lq & 15)) * 16;
     const int tr_i = lane & 15, tr_grp = lane >> 4;
     const int v_lane = (4 * (tr_grp >> 1) + (tr_i >> 2)) * 64 + (2 * (tr_grp & 1) + ((tr_i & 3) >> 1)) * 16 +
                        8 * (tr_i & 1);
 
-    f32x16 o[D / 32];
+    f32x16 o[DV / 32];
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b) o[b] = f32x16{};
+    for (int b = 0; b < DV / 32; ++b) o[b] = f32x16{};
     // running state: row max m, its scaled reference mc (exponents are taken
     // against mc), fp32 sum l and the sum lw of the bf16-rounded weights
     float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
@@ -214,8 +220,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int b = 0; b < BC / 32; ++b) {
         acc[b] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const u32x4 a = *(const u32x4*)(kt + k_lane + (2 * b * CG + (c >> 1)) * 1024 + (c & 1) * 512);
+        for (int c = 0; c < DK / 16; ++c) {
+          const u32x4 a = *(const u32x4*)(kt + k_lane + (2 * b * CGK + (c >> 1)) * 1024 + (c & 1) * 512);
           acc[b] = TT::mma(a, qf[c], acc[b]);
         }
       }
@@ -224,8 +230,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int cc = 0; cc < BC / 16; ++cc)
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const uint8_t* va = vt + v_lane + (cc * CG + b) * 1024;
+        for (int b = 0; b < DV / 32; ++b) {
+          const uint8_t* va = vt + v_lane + (cc * CGV + b) * 1024;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
@@ -293,14 +299,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // followed by the independent vector work that hides it.
     auto steady = [&](f32x16 (&cur)[BC / 32], f32x16 (&nxt)[BC / 32], const uint8_t* kt,
                       const uint8_t* vt, int t_next, bool mask_next) {
-      constexpr int NQK = BC / 32 * D / 16, NPV = BC / 16 * D / 32;
+      constexpr int NQK = BC / 32 * DK / 16, NPV = BC / 16 * DV / 32;
       constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
       const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
       float ls0 = 0.f, ls1 = 0.f, lw0 = 0.f, lw1 = 0.f;
       // ---- step A: S_{j+1} (MFMA) with exp / sums / packing of tile j (VALU)
       auto kaddr = [&](int i) {
-        const int bb = i / (D / 16), c = i % (D / 16);
-        return (const u32x4*)(kt + k_lane + (2 * bb * CG + (c >> 1)) * 1024 + (c & 1) * 512);
+        const int bb = i / (DK / 16), c = i % (DK / 16);
+        return (const u32x4*)(kt + k_lane + (2 * bb * CGK + (c >> 1)) * 1024 + (c & 1) * 512);
       };
       constexpr int KP = 4;  // K operands in flight ahead of the matrix core
       u32x4 kop[KP + 1];
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
         if (i + KP < NQK) kop[(i + KP) % (KP + 1)] = *kaddr(i + KP);
-        const int bb = i / (D / 16), c = i % (D / 16);
+        const int bb = i / (DK / 16), c = i % (DK / 16);
         nxt[bb] = TT::mma(kop[i % (KP + 1)], qf[c], c == 0 ? f32x16{} : nxt[bb]);
 #pragma unroll
         for (int e = EPM * i; e < EPM * (i + 1); ++e) {
@@ -333,8 +339,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       lw_run += lw0 + lw1;
       // ---- step B: O += P_j V_j (MFMA) with tile j+1's row max (VALU)
       auto vaddr = [&](int i) {
-        const int cc = i / (D / 32), bb = i % (D / 32);
-        return vt + v_lane + (cc * CG + bb) * 1024;
+        const int cc = i / (DV / 32), bb = i % (DV / 32);
+        return vt + v_lane + (cc * CGV + bb) * 1024;
       };
       constexpr int VP = 4;  // V operands in flight ahead of the matrix core
       u32x4 vop[VP + 1];
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         if (i + VP < NPV) vop[(i + VP) % (VP + 1)] = vload(i + VP);
-        const int cc = i / (D / 32), bb = i % (D / 32);
+        const int cc = i / (DV / 32), bb = i % (DV / 32);
         o[bb] = TT::mma(vop[i % (VP + 1)], pf[cc], o[bb]);
         if (i >= 2) {
 #pragma unroll
@@ -398,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         l_run *= alpha;
         lw_run *= alpha;
 #pragma unroll
-        for (int bb = 0; bb < D / 32; ++bb) o[bb] *= alpha;
+        for (int bb = 0; bb < DV / 32; ++bb) o[bb] *= alpha;
       }
     };
 
@@ -414,13 +420,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     auto issue_for = [&](int j) { if (j + AHEAD < T) load_stage(j + AHEAD); };
     // loads one wave issues for stage st: K tile (if st+1 < T) and V tile (if st >= 0)
     auto stage_loads = [&](int st) {
-      return st >= T ? 0 : (st + 1 < T ? NDMA / 2 : 0) + (st >= 0 ? NDMA / 2 : 0);
+      return st >= T ? 0 : (st + 1 < T ? NDK : 0) + (st >= 0 ? NDV : 0);
     };
     // s_waitcnt takes an immediate, so each reachable count (a multiple of half
     // a stage, at most NS-2 full stages) gets its own instruction
     auto wait_keep = [&](int keep) {
-      constexpr int HS = NDMA / 2;  // loads of half a stage
-      static_assert((NS - 2) * NDMA <= 63, "vmcnt is a 6-bit count");
+      constexpr int HS = NDK;  // loads of half a stage (NDK = NDV when NS > 2)
+      static_assert((NS - 2) * (NDK + NDV) <= 63, "vmcnt is a 6-bit count");
       if constexpr (NS >= 4) {
         if (keep >= 4 * HS) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * HS)); return; }
         if (keep == 3 * HS) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * HS)); return; }
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // masked, so the steady steps below see -inf instead of stale registers.
     if (0 < T) {
       bool resc;
-      qk(smem + stage_buf(-1) * 2 * TB, sA);
+      qk(smem + stage_buf(-1) * SB, sA);
       part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
     }
     __syncthreads();  // every wave is done with stage -1's buffer before it is refilled
@@ -471,14 +477,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (; j + 2 < T; j += 2) {
       issue_for(j);
       {
-        const uint8_t* kt = smem + stage_buf(j) * 2 * TB;
-        steady(sA, sB, kt, kt + TB, j + 1, tile_masked(j + 1));
+        const uint8_t* kt = smem + stage_buf(j) * SB;
+        steady(sA, sB, kt, kt + TBK, j + 1, tile_masked(j + 1));
       }
       end_iter(j);
       issue_for(j + 1);
       {
-        const uint8_t* kt = smem + stage_buf(j + 1) * 2 * TB;
-        steady(sB, sA, kt, kt + TB, j + 2, tile_masked(j + 2));
+        const uint8_t* kt = smem + stage_buf(j + 1) * SB;
+        steady(sB, sA, kt, kt + TBK, j + 2, tile_masked(j + 2));
       }
       end_iter(j + 1);
     }
@@ -488,8 +494,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // claim the next item during the last tile: claiming earlier would
       // reserve work that an idle workgroup could have started sooner
       if (PERSIST && tid == 0 && j == T - 1) next = take_item(slot, xcd, total_items);
-      const uint8_t* kt = smem + stage_buf(j) * 2 * TB;  // K_{j+1}
-      const uint8_t* vt = kt + TB;                        // V_j
+      const uint8_t* kt = smem + stage_buf(j) * SB;  // K_{j+1}
+      const uint8_t* vt = kt + TBK;                   // V_j
       if (j < my_T) {
         part2(sA);
         pv(vt);
@@ -499,7 +505,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           const float alpha = part1(sB, j + 1, tile_masked(j + 1), resc);
           if (resc) {
 #pragma unroll
-            for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+            for (int b = 0; b < DV / 32; ++b) o[b] *= alpha;
           }
 #pragma unroll
           for (int b = 0; b < BC / 32; ++b) sA[b] = sB[b];
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const float inv = lw_tot > 0.f ? __builtin_amdgcn_rcpf(lw_tot) : 0.f;
       uint8_t* stg = smem + wave * kOStageBytes;
 #pragma unroll
-      for (int r = 0; r < D / 64; ++r) {
+      for (int r = 0; r < DV / 64; ++r) {
 #pragma unroll
         for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           const int row = 8 * i + (lane >> 3);
           const u32x4 v = *(const u32x4*)(stg + row * kOStageRow + 16 * (lane & 7));
           if (q_first + row < Nq)
-            *(u32x4*)(O + head + (size_t)(q_first + row) * D + 64 * r + 8 * (lane & 7)) = v;
+            *(u32x4*)(O + ohead + (size_t)(q_first + row) * DV + 64 * r + 8 * (lane & 7)) = v;
         }
       }
       // a row without kept keys: -inf + ln 0 = -inf, the log of the empty sum
@@ -567,13 +573,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // log-sum-exp over those keys to Opart[s] / LSEpart[s] (rows*D and rows
 // floats per split); attn_combine_f32 merges the splits.  A split that holds
 // no kept key of a row writes 0 and -inf for it.
-template <int DSL, int DS, bool CAUSAL, bool SPLIT>
+template <int DSL, int DSLV, int DS, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int H,
     const int* __restrict__ k_len, int n_qtiles, int total_wg, float scale, int n_split, int tps,
     float* __restrict__ Opart, float* __restrict__ LSEpart) {
-  constexpr int D = DSL * DS, NB = DSL / 32, BC = 32;
+  // D: head dim of Q and K (DSL columns per wave); DV: of V and O (DSLV per wave)
+  constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSLV / 32, BC = 32;
   __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -587,9 +594,10 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernel
   const int diag = nk - Nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const size_t vhead = (size_t)bh * Nk * DV, ohead = (size_t)bh * Nq * DV;
   const int q_first = qt * 32;
   const int my_q = q_first + lq;
-  const int col0 = wave * DSL;
+  const int col0 = wave * DSL, colv0 = wave * DSLV;
 
   f32x4 qf[DSL / 8];
   {
@@ -663,7 +671,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float* vrow = V + khead + (size_t)key * D + col0 + NB * lq;
+      const float* vrow = V + vhead + (size_t)key * DV + colv0 + NB * lq;
       float vv[NB];
       if (key < nk) {
         if constexpr (NB == 4) {
@@ -689,8 +697,8 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   if (my_q < Nq) {
     // a split may hold no kept key of this row: weight 0, lse -inf
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* orow = (SPLIT ? Opart + (size_t)split * ((size_t)Nq * D * (total_wg / (n_qtiles * n_split))) : O) +
-                  head + (size_t)my_q * D + col0;
+    float* orow = (SPLIT ? Opart + (size_t)split * ((size_t)Nq * DV * (total_wg / (n_qtiles * n_split))) : O) +
+                  ohead + (size_t)my_q * DV + colv0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -758,15 +766,17 @@ struct Shape {
   const int* k_len;
 };
 
-template <class TT, int D>
+template <class TT, int DK, int DV>
 hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse,
                      const Shape& sh, float scale, bool causal, hipStream_t st) {
   // d = 128: 8 waves (256 query rows) per workgroup halve the K/V tile
   // loads per FLOP, and one persistent workgroup per CU claims work items
   // (no gap between items, no idle XCD at the end).  d = 64: 4 waves, two
-  // workgroups per CU, one workgroup per item.
-  constexpr int NW = D == 128 ? 8 : 4, NS = 2;
-  constexpr bool PERSIST = D == 128;
+  // workgroups per CU, one workgroup per item.  Unequal head dims take the
+  // d = 128 arrangement.
+  constexpr bool WIDE = DK == 128 || DV == 128;
+  constexpr int NW = WIDE ? 8 : 4, NS = 2;
+  constexpr bool PERSIST = WIDE;
   static std::atomic<unsigned> launches{0};
   const int nq = (sh.Nq + 32 * NW - 1) / (32 * NW);
   const int total = nq * sh.BH;
@@ -779,11 +789,11 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   }
   const dim3 grid(grid_wg), block(64 * NW);
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_sp<TT, D, true, NW, NS, PERSIST>), grid, block, 0, st,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, PERSIST>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                        sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale);
   else
-    hipLaunchKernelGGL((attn_fwd_sp<TT, D, false, NW, NS, PERSIST>), grid, block, 0, st,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, PERSIST>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                        sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale);
   return hipGetLastError();
@@ -793,9 +803,10 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
 // one workgroup per CU, at least 4 key tiles per split.  n_split = 1: none.
 struct SplitPlan {
   int n_split = 1, tps = 0;
-  size_t bytes = 0;  // workspace: n_split*rows*d floats of partial O, then n_split*rows of lse
+  size_t bytes = 0;  // workspace: n_split*rows*dv floats of partial O, then n_split*rows of lse
 };
 
+// d: the value head dim (the width of O)
 SplitPlan plan_split(long long BH, int Nq, int Nk, int d, int dtype) {
   SplitPlan p;
   if (dtype != FA_DTYPE_FP32) return p;
@@ -813,11 +824,11 @@ SplitPlan plan_split(long long BH, int Nq, int Nk, int d, int dtype) {
   return p;
 }
 
-template <int DSL, int DS>
+template <int DSL, int DSLV, int DS>
 hipError_t launch32(const void* q, const void* k, const void* v, void* o, float* lse,
                     const Shape& sh, float scale, bool causal, hipStream_t st,
                     const SplitPlan& plan, void* ws) {
-  constexpr int D = DSL * DS;
+  constexpr int D = DSLV * DS;  // the width of O
   const int nq = (sh.Nq + 31) / 32;
   if (plan.n_split > 1) {
     const int total = nq * sh.BH * plan.n_split;
@@ -825,11 +836,11 @@ hipError_t launch32(const void* q, const void* k, const void* v, void* o, float*
     float* lpart = opart + (size_t)plan.n_split * sh.BH * sh.Nq * D;
     const dim3 grid(total), block(DS * 64);
     if (causal)
-      hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true, true>), grid, block, 0, st, (const float*)q,
+      hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, true, true>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
                          sh.k_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
     else
-      hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false, true>), grid, block, 0, st, (const float*)q,
+      hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, false, true>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
                          sh.k_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -843,11 +854,11 @@ hipError_t launch32(const void* q, const void* k, const void* v, void* o, float*
   const int total = nq * sh.BH;
   const dim3 grid(total), block(DS * 64);
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, true, false>), grid, block, 0, st, (const float*)q,
+    hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, true, false>), grid, block, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
                        sh.k_len, nq, total, scale, 1, 0, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((attn_fwd_f32<DSL, DS, false, false>), grid, block, 0, st, (const float*)q,
+    hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, false, false>), grid, block, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
                        sh.k_len, nq, total, scale, 1, 0, nullptr, nullptr);
   return hipGetLastError();
@@ -866,15 +877,23 @@ int fa_fwd_supported(int d, int dtype, int causal) {
   return 0;
 }
 
+int fa_fwd_gen_supported(int d_qk, int d_v, int dtype, int causal) {
+  if (d_qk == d_v) return fa_fwd_supported(d_qk, dtype, causal);
+  if (causal != 0 && causal != 1) return 0;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_FP32) return 0;
+  return (d_qk == 64 || d_qk == 128) && (d_v == 64 || d_v == 128);
+}
+
 }  // extern "C"
 
 namespace {
 
 // Argument checks shared by the entry points (no HIP call).
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
-               int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype) {
+               int B, int H, int Nq, int Nk, int dk, int dv, float scale, int causal,
+               int dtype) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || dk <= 0 || dv <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   const long long BH = (long long)B * H;
@@ -884,34 +903,46 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   if (BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return FA_ERR_INVALID_ARG;  // row ids
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
     return FA_ERR_UNSUPPORTED;
-  if (!fa_fwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
+  if (!fa_fwd_gen_supported(dk, dv, dtype, causal)) return FA_ERR_UNSUPPORTED;
   // per-head byte offsets (plus one tile of slack) must fit the 32-bit
   // offsets of the buffer loads
   const long long elem = dtype == FA_DTYPE_FP32 ? 4 : 2;
-  if (((long long)std::max(Nq, Nk) + 128) * d * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (((long long)std::max(Nq, Nk) + 128) * std::max(dk, dv) * elem > 0x7fffffffLL)
+    return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
+template <class TT>
+hipError_t launch_sp_dims(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const Shape& sh, int dk, int dv, float scale, bool c, hipStream_t st) {
+  if (dk == 64) return dv == 64 ? launch_sp<TT, 64, 64>(q, k, v, o, lse, sh, scale, c, st)
+                                : launch_sp<TT, 64, 128>(q, k, v, o, lse, sh, scale, c, st);
+  return dv == 64 ? launch_sp<TT, 128, 64>(q, k, v, o, lse, sh, scale, c, st)
+                  : launch_sp<TT, 128, 128>(q, k, v, o, lse, sh, scale, c, st);
+}
+
+// dk, dv: head dims of Q/K and of V/O (a supported pair)
 int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, const Shape& sh,
-             int d, float scale, int causal, int dtype, const SplitPlan& plan, void* ws,
+             int dk, int dv, float scale, int causal, int dtype, const SplitPlan& plan, void* ws,
              void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool c = causal != 0;
   hipError_t e = hipSuccess;
   if (dtype == FA_DTYPE_BF16) {
-    e = d == 64 ? launch_sp<Bf16, 64>(q, k, v, o, lse, sh, scale, c, st)
-                : launch_sp<Bf16, 128>(q, k, v, o, lse, sh, scale, c, st);
+    e = launch_sp_dims<Bf16>(q, k, v, o, lse, sh, dk, dv, scale, c, st);
   } else if (dtype == FA_DTYPE_FP16) {
-    e = d == 64 ? launch_sp<F16, 64>(q, k, v, o, lse, sh, scale, c, st)
-                : launch_sp<F16, 128>(q, k, v, o, lse, sh, scale, c, st);
+    e = launch_sp_dims<F16>(q, k, v, o, lse, sh, dk, dv, scale, c, st);
+  } else if (dk != dv) {
+    e = dk == 64 ? launch32<64, 128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws)
+                 : launch32<128, 64, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws);
   } else {
-    switch (d) {
-      case 64: e = launch32<64, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
-      case 128: e = launch32<128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
-      case 256: e = launch32<128, 2>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
-      case 512: e = launch32<128, 4>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
-      default: e = launch32<128, 8>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+    switch (dk) {
+      case 64: e = launch32<64, 64, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 128: e = launch32<128, 128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 256: e = launch32<128, 128, 2>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 512: e = launch32<128, 128, 4>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      default: e = launch32<128, 128, 8>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
     }
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -921,27 +952,41 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, c
 
 extern "C" {
 
-size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
+size_t fa_fwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v, int causal,
+                                 int dtype) {
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (causal != 0 && causal != 1)) return 0;
-  if (!fa_fwd_supported(d, dtype, causal)) return 0;
+  if (!fa_fwd_gen_supported(d_qk, d_v, dtype, causal)) return 0;
   const long long BH = (long long)B * H;
   if (BH > (1LL << 24) || BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return 0;
-  return plan_split(BH, Nq, Nk, d, dtype).bytes;
+  return plan_split(BH, Nq, Nk, d_v, dtype).bytes;
+}
+
+size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
+  return fa_fwd_gen_workspace_size(B, H, Nq, Nk, d, d, causal, dtype);
+}
+
+int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Nq, int Nk, int d_qk, int d_v, float scale, int causal, int dtype,
+               const int* k_len, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int err = check_args(q, k, v, o, lse, B, H, Nq, Nk, d_qk, d_v, scale, causal, dtype);
+      err != FA_OK)
+    return err;
+  if (((uintptr_t)k_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  const Shape sh{B * H, H, Nq, Nk, k_len};
+  if (workspace == nullptr || workspace_bytes == 0)
+    return dispatch(q, k, v, o, lse, sh, d_qk, d_v, scale, causal, dtype, SplitPlan{}, nullptr,
+                    stream);
+  const SplitPlan plan = plan_split((long long)B * H, Nq, Nk, d_v, dtype);
+  if (workspace_bytes < plan.bytes) return FA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return FA_ERR_UNSUPPORTED;
+  return dispatch(q, k, v, o, lse, sh, d_qk, d_v, scale, causal, dtype, plan, workspace, stream);
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int Nq, int Nk, int d, float scale, int causal, int dtype, const int* k_len,
               void* workspace, size_t workspace_bytes, void* stream) {
-  if (int err = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype); err != FA_OK)
-    return err;
-  if (((uintptr_t)k_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
-  const Shape sh{B * H, H, Nq, Nk, k_len};
-  if (workspace == nullptr || workspace_bytes == 0)
-    return dispatch(q, k, v, o, lse, sh, d, scale, causal, dtype, SplitPlan{}, nullptr, stream);
-  const SplitPlan plan = plan_split((long long)B * H, Nq, Nk, d, dtype);
-  if (workspace_bytes < plan.bytes) return FA_ERR_INVALID_ARG;
-  if (!aligned16(workspace)) return FA_ERR_UNSUPPORTED;
-  return dispatch(q, k, v, o, lse, sh, d, scale, causal, dtype, plan, workspace, stream);
+  return fa_fwd_gen(q, k, v, o, lse, B, H, Nq, Nk, d, d, scale, causal, dtype, k_len, workspace,
+                    workspace_bytes, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

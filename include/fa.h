@@ -157,6 +157,31 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype);
 
 /*
+ * fa_fwd_gen -- fa_fwd_ex with the value head dim apart from the query/key
+ * one: Q of shape (n, d_k), K (m, d_k) and V (m, d_v), as the scaled
+ * dot-product attention of "Transformer Attention: A Mathematical Deep Dive"
+ * is defined.  The scores contract the d_qk columns; O has the d_v columns.
+ *   q : [B][H][Nq][d_qk];  k : [B][H][Nk][d_qk];  v : [B][H][Nk][d_v];
+ *   o : [B][H][Nq][d_v];   lse : [B][H][Nq] fp32.
+ * Supported pairs: fa_fwd_gen_supported (d_qk = d_v as for fa_fwd; otherwise
+ * d_qk, d_v in {64, 128} for bf16, fp16 and fp32).  The workspace is sized by
+ * fa_fwd_gen_workspace_size.  Everything else is as for fa_fwd_ex, which is
+ * fa_fwd_gen with d_qk = d_v = d.  scale is the caller's (1/sqrt(d_qk) is the
+ * usual choice).
+ */
+int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Nq, int Nk, int d_qk, int d_v, float scale, int causal,
+               int dtype, const int* k_len, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* fa_fwd_ex_workspace_size for fa_fwd_gen's shapes (0: none needed, or invalid). */
+size_t fa_fwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v, int causal,
+                                 int dtype);
+
+/* 1 when fa_fwd_gen has a kernel for (d_qk, d_v, dtype, causal), else 0. */
+int fa_fwd_gen_supported(int d_qk, int d_v, int dtype, int causal);
+
+/*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for this
  * problem: two fp32 row statistics per (batch, head, row), rows padded to a
  * multiple of 32; for fp32 problems with fewer query or key blocks (32 rows)

@@ -205,3 +205,45 @@ def test_bwd_ex_checks_arguments_first():
     assert fa.fa_bwd_ex_workspace_size(2, 3, 100, 7, 64, 1, fa.FA_DTYPE_BF16) == 2 * 6 * 128 * 4
     assert fa.fa_bwd_ex_workspace_size(2, 3, 100, 100, 64, 1, fa.FA_DTYPE_BF16) == \
         fa.fa_bwd_workspace_size(2, 3, 100, 64, 1, fa.FA_DTYPE_BF16)
+
+
+# ------------------------------------------------------------------ value head dim of its own
+def call_gen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=16, Nk=40, d_qk=64, d_v=128,
+             scale=0.125, causal=0, dtype=fa.FA_DTYPE_BF16, k_len=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return fa.fa_fwd_gen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                         a["Nk"], a["d_qk"], a["d_v"], a["scale"], a["causal"], a["dtype"],
+                         a["k_len"], a["ws"], a["ws_bytes"], None)
+
+
+def test_gen_supported_table():
+    for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16, fa.FA_DTYPE_FP32):
+        for dk, dv in ((64, 128), (128, 64), (64, 64), (128, 128)):
+            assert fa.fa_fwd_gen_supported(dk, dv, dt, 0) and fa.fa_fwd_gen_supported(dk, dv, dt, 1)
+        for dk, dv in ((64, 256), (256, 128), (96, 64), (128, 32)):
+            assert not fa.fa_fwd_gen_supported(dk, dv, dt, 0)
+        for d in (64, 128, 256, 512, 1024):  # equal dims: as fa_fwd
+            assert fa.fa_fwd_gen_supported(d, d, dt, 0) == fa.fa_fwd_supported(d, dt, 0)
+    assert not fa.fa_fwd_gen_supported(64, 128, 9, 0)
+    assert not fa.fa_fwd_gen_supported(64, 128, fa.FA_DTYPE_BF16, 2)
+
+
+@pytest.mark.parametrize("kw", [dict(d_v=0), dict(d_qk=-1), dict(Nq=0), dict(v=None), dict(causal=3),
+                                dict(scale=0.0)])
+def test_gen_invalid_arguments(kw):
+    assert call_gen(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d_v=256), dict(d_qk=96), dict(dtype=7), dict(v=FAKE + 8),
+                                dict(k_len=FAKE + 2)])
+def test_gen_unsupported_configurations(kw):
+    assert call_gen(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_gen_workspace_size_matches_equal_dims():
+    for dt, d in ((fa.FA_DTYPE_FP32, 64), (fa.FA_DTYPE_FP32, 1024), (fa.FA_DTYPE_BF16, 128)):
+        for N in (64, 300, 1024):
+            assert fa.fa_fwd_gen_workspace_size(1, 1, N, N, d, d, 0, dt) == \
+                fa.fa_fwd_ex_workspace_size(1, 1, N, N, d, 0, dt)
+    assert fa.fa_fwd_gen_workspace_size(1, 1, 16, 16, 64, 256, 0, fa.FA_DTYPE_BF16) == 0

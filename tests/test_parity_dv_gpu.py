@@ -1,0 +1,108 @@
+"""GPU parity for a value head dim apart from the query/key one: fa_fwd_gen
+(through the C ABI, via attention()) against the fp64 oracle
+(oracle_attn_rows_gen), element by element, and bitwise against the
+equal-dim kernels on zero-padded inputs.
+
+Zero columns change nothing exactly: zero columns of Q and K add exact zero
+products to every score, and zero columns of V give zero columns of O while
+the other columns see the same weights.  So fa_fwd_gen(d_qk=64, d_v=128) must
+equal fa_fwd(d=128) on Q and K padded to 128 columns bit for bit, and
+fa_fwd_gen(128, 64) must equal the first 64 columns of fa_fwd(d=128) on V
+padded to 128 columns.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_29_amd as fa
+import oracle
+from exact_attention_29_amd.inputs import make_qkv
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU; run with -m 'not gpu' on a CPU host"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def inputs(B, H, Nq, Nk, dk, dv, dt, seed):
+    """Q [B,H,Nq,dk], K [B,H,Nk,dk], V [B,H,Nk,dv]: the seeded N(0,1) recipe,
+    V taken from a draw of its own width."""
+    q, k, _ = make_qkv(B, H, max(Nq, Nk), dk, dt, seed)
+    _, _, v = make_qkv(B, H, Nk, dv, dt, seed + 1)
+    return q[:, :, :Nq].contiguous(), k[:, :, :Nk].contiguous(), v
+
+
+def pad(x, width):
+    out = torch.zeros(*x.shape[:3], width, dtype=x.dtype, device=x.device)
+    out[..., : x.shape[3]] = x
+    return out
+
+
+PAIRS = [(64, 128), (128, 64)]
+SHAPES = [(200, 200, None), (77, 300, None), (300, 77, None), (129, 1, None),
+          (190, 333, [333, 150, 0]), (64, 64, [40, 64, 1])]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("dk,dv", PAIRS)
+@pytest.mark.parametrize("Nq,Nk,k_len", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_unequal_head_dims_match_oracle(dt, dk, dv, Nq, Nk, k_len, causal):
+    B, H = 3, 2
+    q, k, v = inputs(B, H, Nq, Nk, dk, dv, dt, 7000 + Nq + 3 * Nk + dk + int(causal))
+    scale = 1 / math.sqrt(dk)
+    kl = None if k_len is None else torch.tensor(k_len, dtype=torch.int32, device="cuda")
+    o, lse = fa.attention(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, k_len=kl)
+    torch.cuda.synchronize()
+    assert o.shape == (B, H, Nq, dv)
+    o_ref, l_ref = oracle.attn_rows_ex(q, k, v, scale, causal, None, k_len)
+    og = o.double().cpu().reshape(-1, dv).numpy()
+    lg = lse.double().cpu().reshape(-1).numpy()
+    empty = np.isneginf(l_ref)
+    assert np.all(og[empty] == 0) and np.all(np.isneginf(lg[empty])), "empty rows"
+    full = ~empty
+    assert np.isfinite(og).all() and np.isfinite(lg[full]).all()
+    if full.any():
+        do = np.abs(og[full] - o_ref[full])
+        parity.check(dict(max_o=float(do.max()), mean_o=float(do.mean()),
+                          max_lse=float(np.abs(lg[full] - l_ref[full]).max()), finite=True,
+                          rows=int(full.sum())), DT[dt])
+
+
+@pytest.mark.parametrize("dt,B,H,Nq,Nk", [("bf16", 2, 8, 2048, 2048), ("fp16", 1, 4, 1000, 3000),
+                                          ("fp32", 1, 2, 700, 700), ("fp32", 1, 1, 1024, 1024)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_equals_equal_dim_kernel_on_zero_padded_inputs(dt, B, H, Nq, Nk, causal):
+    q, k, v = inputs(B, H, Nq, Nk, 128, 128, dt, 7100 + Nq + Nk)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    scale = 0.11
+    # d_qk = 64, d_v = 128  vs  d = 128 with Q, K zero beyond column 64
+    q64, k64 = q[..., :64].contiguous(), k[..., :64].contiguous()
+    o1, l1 = fa.attention(q64, k64, v, causal=causal, scale=scale)
+    o2, l2 = fa.attention(pad(q64, 128), pad(k64, 128), v, causal=causal, scale=scale)
+    # d_qk = 128, d_v = 64  vs  d = 128 with V zero beyond column 64
+    v64 = v[..., :64].contiguous()
+    o3, l3 = fa.attention(q, k, v64, causal=causal, scale=scale)
+    o4, l4 = fa.attention(q, k, pad(v64, 128), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4[..., :64]) and torch.equal(l3, l4)
+    assert torch.all(o4[..., 64:] == 0)
+
+
+def test_unsupported_pairs_are_rejected():
+    q = torch.zeros(1, 1, 16, 64, device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros(1, 1, 16, 256, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, v)
+    with pytest.raises(ValueError):  # v of another key count
+        fa.attention(q, q, torch.zeros(1, 1, 8, 128, device="cuda", dtype=torch.bfloat16))
