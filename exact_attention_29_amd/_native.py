@@ -76,6 +76,14 @@ def library():
             ctypes.c_size_t, ctypes.c_void_p]
         L.fa_bwd_ex_workspace_size.restype = ctypes.c_size_t
         L.fa_bwd_ex_workspace_size.argtypes = [ctypes.c_int] * 7
+        L.fa_bwd_gen.restype = ctypes.c_int
+        L.fa_bwd_gen.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_size_t, ctypes.c_void_p]
+        L.fa_bwd_gen_workspace_size.restype = ctypes.c_size_t
+        L.fa_bwd_gen_workspace_size.argtypes = [ctypes.c_int] * 8
+        L.fa_bwd_gen_supported.restype = ctypes.c_int
+        L.fa_bwd_gen_supported.argtypes = [ctypes.c_int] * 4
         L.fa_bwd_supported.restype = ctypes.c_int
         L.fa_bwd_supported.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.fa_status_string.restype = ctypes.c_char_p
@@ -291,6 +299,25 @@ def fa_bwd_ex_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, causal: i
                                                   int(causal), int(dtype)))
 
 
+def fa_bwd_gen(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+               B: int, H: int, Nq: int, Nk: int, d_qk: int, d_v: int, scale: float, causal: int,
+               dtype: int, k_len: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    """The raw C entry point with separate query/key and value head dims."""
+    return library().fa_bwd_gen(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d_qk, d_v,
+                                ctypes.c_float(scale), int(causal), int(dtype), k_len, workspace,
+                                int(workspace_bytes), stream)
+
+
+def fa_bwd_gen_workspace_size(B: int, H: int, Nq: int, Nk: int, d_qk: int, d_v: int,
+                              causal: int, dtype: int) -> int:
+    return int(library().fa_bwd_gen_workspace_size(int(B), int(H), int(Nq), int(Nk), int(d_qk),
+                                                   int(d_v), int(causal), int(dtype)))
+
+
+def fa_bwd_gen_supported(d_qk: int, d_v: int, dtype: int, causal: int) -> bool:
+    return bool(library().fa_bwd_gen_supported(int(d_qk), int(d_v), int(dtype), int(causal)))
+
+
 def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                   lse: torch.Tensor, dout: torch.Tensor, causal: bool = False,
                   scale: float | None = None, dq: torch.Tensor | None = None,
@@ -298,24 +325,28 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
                   stream: torch.cuda.Stream | None = None, k_len: torch.Tensor | None = None):
     """Gradients (dq, dk, dv) of the attention `attention()` computes.
 
-    q, o, dout: contiguous device tensors [B, H, Nq, d]; k, v: [B, H, Nk, d];
-    one dtype (bf16, fp16, or fp32); o and lse as returned by attention() for the same
-    arguments (k_len included).  The workspace comes from torch's allocator on
-    `stream`.  Asynchronous on `stream` (default: torch's current stream).
-    Equal lengths without k_len run through fa_bwd, other shapes fa_bwd_ex.
+    q: contiguous device tensor [B, H, Nq, d]; k: [B, H, Nk, d]; v: [B, H,
+    Nk, dv]; o, dout: [B, H, Nq, dv]; one dtype (bf16, fp16, or fp32); o and
+    lse as returned by attention() for the same arguments (k_len included).
+    The workspace comes from torch's allocator on `stream`.  Asynchronous on
+    `stream` (default: torch's current stream).  Equal lengths and head dims
+    without k_len run through fa_bwd, other shapes fa_bwd_ex, unequal head dims
+    fa_bwd_gen.  Returns (dq like q, dk like k, dv like v).
     """
-    for name, t, like in (("q", q, q), ("o", o, q), ("dout", dout, q), ("k", k, k), ("v", v, k)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
             raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous() or t.shape != like.shape or t.dtype != q.dtype \
-                or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous tensor like {'q' if like is q else 'k'}")
-    if q.dim() != 4 or q.dtype not in _DTYPE_CODE or q.shape[:2] != k.shape[:2] \
-            or q.shape[3] != k.shape[3]:
-        raise ValueError(f"q must be [B, H, Nq, d] and k [B, H, Nk, d] of a supported dtype, "
-                         f"got {tuple(q.shape)}, {tuple(k.shape)} {q.dtype}")
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor of q's dtype and device")
+    if q.dtype not in _DTYPE_CODE or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3] \
+            or v.shape[:3] != k.shape[:3] or o.shape != q.shape[:3] + v.shape[3:] \
+            or dout.shape != o.shape:
+        raise ValueError(f"q must be [B, H, Nq, d], k [B, H, Nk, d], v [B, H, Nk, dv] and o, "
+                         f"dout [B, H, Nq, dv] of a supported dtype, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}, {tuple(o.shape)}, "
+                         f"{tuple(dout.shape)} {q.dtype}")
     B, H, N, d = q.shape
-    Nk = k.shape[2]
+    Nk, d_v = k.shape[2], v.shape[3]
     if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32 \
             or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
@@ -326,36 +357,41 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     outs = []
-    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t is None:
             t = torch.empty_like(like)
         elif t.shape != like.shape or t.dtype != q.dtype or not t.is_contiguous() \
                 or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous tensor like {'q' if like is q else 'k'}")
+            raise ValueError(f"{name} must be a contiguous tensor like {name[1]}")
         outs.append(t)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     code = _DTYPE_CODE[q.dtype]
-    square = Nk == N and k_len is None
+    square = Nk == N and k_len is None and d_v == d
     with torch.cuda.device(q.device):
-        ws_bytes = fa_bwd_ex_workspace_size(B, H, N, Nk, d, int(bool(causal)), code)
+        ws_bytes = fa_bwd_gen_workspace_size(B, H, N, Nk, d, d_v, int(bool(causal)), code)
         if ws_bytes == 0:
             raise ValueError(f"fa_bwd: {fa_status_string(FA_ERR_UNSUPPORTED)} "
-                             f"(d={d}, dtype={q.dtype})")
+                             f"(d={d}, dv={d_v}, dtype={q.dtype})")
         with torch.cuda.stream(stream):
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
         ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr())
+        kl = None if k_len is None else k_len.data_ptr()
         if square:
+            where = "fa_bwd"
             st = fa_bwd(*ptrs, B, H, N, d, float(scale), int(bool(causal)), code, ws.data_ptr(),
                         ws_bytes, stream.cuda_stream)
+        elif d_v == d:
+            where = "fa_bwd_ex"
+            st = fa_bwd_ex(*ptrs, B, H, N, Nk, d, float(scale), int(bool(causal)), code, kl,
+                           ws.data_ptr(), ws_bytes, stream.cuda_stream)
         else:
-            st = fa_bwd_ex(*ptrs, B, H, N, Nk, d, float(scale), int(bool(causal)), code,
-                           None if k_len is None else k_len.data_ptr(), ws.data_ptr(), ws_bytes,
-                           stream.cuda_stream)
+            where = "fa_bwd_gen"
+            st = fa_bwd_gen(*ptrs, B, H, N, Nk, d, d_v, float(scale), int(bool(causal)), code, kl,
+                            ws.data_ptr(), ws_bytes, stream.cuda_stream)
         ws.record_stream(stream)
     if st != FA_OK:
-        where = "fa_bwd" if square else "fa_bwd_ex"
         raise FaError(st, where) if st == FA_ERR_HIP else ValueError(
             f"{where}: {fa_status_string(st)} (status {st})")
     return tuple(outs)

@@ -158,24 +158,27 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // dK, dV.  NW = 4 waves x 32 keys; query tiles of 32 rows.
 //
-// Register layouts (D = head dim; lane (x = lane % 32, h = lane / 32)):
+// Register layouts (DK = head dim of Q and K, DV = of V, O and dO; lane
+// (x = lane % 32, h = lane / 32)):
 //   K and V rows (whole kernel): lane holds row[key0 + x][16c + 8h .. +7]
-//     for c = 0..D/16-1, the B operand of S = Q K^T and dP = dO V^T.
+//     for c = 0..DK/16-1 (K) or DV/16-1 (V), the B operand of S = Q K^T and
+//     dP = dO V^T.
 //   S, dP (accumulators, 32 queries x 32 keys): register r of lane (x, h) is
 //     query 8(r/4) + 4h + r%4 of the tile and key key0 + x.
 //   dK^T, dV^T (accumulators): block b, register r of lane (x, h) is
 //     d-column 32b + 8(r/4) + 4h + r%4 of key key0 + x.
-template <class TT, int D, bool CAUSAL, int NW>
+template <class TT, int DK, int DV, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int H,
     const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale) {
-  constexpr int BQ = 32, CG = D / 32;
-  constexpr int TBLK = 2 * CG, TB = TBLK * 1024;  // 1 KB blocks and bytes of one 32-row tile
+  constexpr int BQ = 32, CGK = DK / 32, CGV = DV / 32;
+  // 1 KB blocks and bytes of one 32-row Q tile and one dO tile
+  constexpr int TBLKQ = 2 * CGK, TBQ = TBLKQ * 1024, TBLKD = 2 * CGV, TBD = TBLKD * 1024;
   // [buffer][Q tile, dO tile, nl of its rows (1 KB), nd of its rows (1 KB)];
   // the epilogue reuses it as the waves' output staging
-  constexpr int BUF = 2 * TB + 2048;
+  constexpr int BUF = TBQ + TBD + 2048;
   constexpr int SMEM = 2 * BUF > NW * 32 * 144 ? 2 * BUF : NW * 32 * 144;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
@@ -188,24 +191,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // j <= i + diag
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
   const int diag = nk - Nq;
-  const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const size_t head = (size_t)bh * Nq * DK, ohead = (size_t)bh * Nq * DV;
+  const size_t khead = (size_t)bh * Nk * DK, vhead = (size_t)bh * Nk * DV;
   const int k0 = kb * 32 * NW;              // the block's first key
   const int kw = k0 + 32 * wave;            // this wave's first key
   const int my_k = kw + x;
 
-  u32x4 kf[D / 16], vf[D / 16];
+  u32x4 kf[DK / 16], vf[DV / 16];
   {
-    const uint16_t* kr = K + khead + (size_t)my_k * D + 8 * h;
-    const uint16_t* vr = V + khead + (size_t)my_k * D + 8 * h;
+    const uint16_t* kr = K + khead + (size_t)my_k * DK + 8 * h;
+    const uint16_t* vr = V + vhead + (size_t)my_k * DV + 8 * h;
+    if constexpr (DK == DV) {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      kf[c] = my_k < nk ? *(const u32x4*)(kr + 16 * c) : u32x4{0, 0, 0, 0};
-      vf[c] = my_k < nk ? *(const u32x4*)(vr + 16 * c) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < DK / 16; ++c) {
+        kf[c] = my_k < nk ? *(const u32x4*)(kr + 16 * c) : u32x4{0, 0, 0, 0};
+        vf[c] = my_k < nk ? *(const u32x4*)(vr + 16 * c) : u32x4{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < DK / 16; ++c)
+        kf[c] = my_k < nk ? *(const u32x4*)(kr + 16 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < DV / 16; ++c)
+        vf[c] = my_k < nk ? *(const u32x4*)(vr + 16 * c) : u32x4{0, 0, 0, 0};
     }
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 dk[DK / 32], dv[DV / 32];
 #pragma unroll
-  for (int b = 0; b < D / 32; ++b) dk[b] = dv[b] = f32x16{};
+  for (int b = 0; b < DK / 32; ++b) dk[b] = f32x16{};
+#pragma unroll
+  for (int b = 0; b < DV / 32; ++b) dv[b] = f32x16{};
   const float c2 = scale * kLog2e;
   const float* nl_row = NL + (size_t)bh * n_pad;
   const float* nd_row = ND + (size_t)bh * n_pad;
@@ -222,17 +237,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // rest of the 1 KB reads past the descriptor's end and lands as zeros)
     if (wave < 2) {
       const float* src = (wave == 0 ? nl_row : nd_row) + r0;
-      dma16(buffer_desc(src, BQ * 4), base + 2 * TB + 1024 * wave, lane * 16);
+      dma16(buffer_desc(src, BQ * 4), base + TBQ + TBD + 1024 * wave, lane * 16);
     }
-    const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * D, (unsigned)(Nq - r0) * D * 2);
-    const u32x4 dd = buffer_desc(dO + head + (size_t)r0 * D, (unsigned)(Nq - r0) * D * 2);
+    const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * DK, (unsigned)(Nq - r0) * DK * 2);
+    const u32x4 dd = buffer_desc(dO + ohead + (size_t)r0 * DV, (unsigned)(Nq - r0) * DV * 2);
+    if constexpr (DK == DV) {  // the same block pattern in both tiles
 #pragma unroll
-    for (int i = 0; i < (TBLK + NW - 1) / NW; ++i) {
-      const int blk = wave + i * NW;
-      if (blk < TBLK) {  // with more waves than blocks, some waves load none
-        const int el = TileLayout<D>::v_src(blk, lane);
-        dma16(dq, base + blk * 1024, el * 2);
-        dma16(dd, base + TB + blk * 1024, el * 2);
+      for (int i = 0; i < (TBLKQ + NW - 1) / NW; ++i) {
+        const int blk = wave + i * NW;
+        if (blk < TBLKQ) {  // with more waves than blocks, some waves load none
+          const int el = TileLayout<DK>::v_src(blk, lane);
+          dma16(dq, base + blk * 1024, el * 2);
+          dma16(dd, base + TBQ + blk * 1024, el * 2);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < (TBLKQ + NW - 1) / NW; ++i) {
+        const int blk = wave + i * NW;
+        if (blk < TBLKQ) dma16(dq, base + blk * 1024, TileLayout<DK>::v_src(blk, lane) * 2);
+      }
+#pragma unroll
+      for (int i = 0; i < (TBLKD + NW - 1) / NW; ++i) {
+        const int blk = wave + i * NW;
+        if (blk < TBLKD) dma16(dd, base + TBQ + blk * 1024, TileLayout<DV>::v_src(blk, lane) * 2);
       }
     }
   };
@@ -249,23 +277,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // last query row of the tile
     if (kw < nk && (!CAUSAL || q0 + BQ - 1 + diag >= kw)) {
       const uint8_t* qt = smem + buf * BUF;
-      const uint8_t* dt = qt + TB;
+      const uint8_t* dt = qt + TBQ;
       f32x16 s, dp;
       // initial accumulators: -lse/scale and -delta of the tile's rows
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 a = *(const f32x4*)(qt + 2 * TB + 4 * (8 * g + 4 * h));
-        const f32x4 b = *(const f32x4*)(qt + 2 * TB + 1024 + 4 * (8 * g + 4 * h));
+        const f32x4 a = *(const f32x4*)(qt + TBQ + TBD + 4 * (8 * g + 4 * h));
+        const f32x4 b = *(const f32x4*)(qt + TBQ + TBD + 1024 + 4 * (8 * g + 4 * h));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           s[4 * g + e] = a[e];
           dp[4 * g + e] = b[e];
         }
       }
+      if constexpr (DK == DV) {
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s = TT::mma(*(const u32x4*)(qt + rowmajor_a<D>(x, h, c)), kf[c], s);
-        dp = TT::mma(*(const u32x4*)(dt + rowmajor_a<D>(x, h, c)), vf[c], dp);
+        for (int c = 0; c < DK / 16; ++c) {
+          s = TT::mma(*(const u32x4*)(qt + rowmajor_a<DK>(x, h, c)), kf[c], s);
+          dp = TT::mma(*(const u32x4*)(dt + rowmajor_a<DV>(x, h, c)), vf[c], dp);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DK / 16; ++c) s = TT::mma(*(const u32x4*)(qt + rowmajor_a<DK>(x, h, c)), kf[c], s);
+#pragma unroll
+        for (int c = 0; c < DV / 16; ++c) dp = TT::mma(*(const u32x4*)(dt + rowmajor_a<DV>(x, h, c)), vf[c], dp);
       }
       // P = exp(scale s - lse); dS = P (dP - delta); a tile across the
       // diagonal or the end of the valid keys keeps key <= query + diag and
@@ -289,14 +324,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                        TT::pack(dp[r0 + 4], dp[r0 + 5]), TT::pack(dp[r0 + 6], dp[r0 + 7])};
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries
+      if constexpr (DK == DV) {
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const int off = (kc * CG + b) * 1024 + trl;
-          dv[b] = TT::mma(tr_read(dt + off), pf[kc], dv[b]);
-          dk[b] = TT::mma(tr_read(qt + off), df[kc], dk[b]);
+          for (int b = 0; b < DV / 32; ++b) {
+            const int off = (kc * CGV + b) * 1024 + trl;
+            dv[b] = TT::mma(tr_read(dt + off), pf[kc], dv[b]);
+            dk[b] = TT::mma(tr_read(qt + off), df[kc], dk[b]);
+          }
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+          for (int b = 0; b < DV / 32; ++b)
+            dv[b] = TT::mma(tr_read(dt + (kc * CGV + b) * 1024 + trl), pf[kc], dv[b]);
+#pragma unroll
+          for (int b = 0; b < DK / 32; ++b)
+            dk[b] = TT::mma(tr_read(qt + (kc * CGK + b) * 1024 + trl), df[kc], dk[b]);
         }
+      }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -304,8 +351,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // the tile buffers are free after the last barrier
   // every key row is written, those past the valid keys as zeros
   uint8_t* stg = smem + wave * 32 * 144;
-  store_rows<TT, D>(dv, 1.f, stg, dV + khead, kw, Nk, lane);
-  store_rows<TT, D>(dk, scale, stg, dK + khead, kw, Nk, lane);
+  store_rows<TT, DV>(dv, 1.f, stg, dV + vhead, kw, Nk, lane);
+  store_rows<TT, DK>(dk, scale, stg, dK + khead, kw, Nk, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -318,18 +365,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 //   S^T, dP^T (accumulators, per 32-key block): register r of lane (x, h) is
 //     key 8(r/4) + 4h + r%4 of the block and query q_first + x.
 //   dQ^T (accumulator): block b, register r is d-column 32b + 8(r/4) + 4h + r%4.
-template <class TT, int D, bool CAUSAL, int NW>
+template <class TT, int DK, int DV, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     uint16_t* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
     int n_qblocks, int total, float scale) {
-  constexpr int BR = 32 * NW, BC = 64, CG = D / 32;
-  using LY = TileLayout<D>;
-  constexpr int TB = LY::BYTES;
-  static_assert(LY::BLOCKS % NW == 0, "tile blocks split evenly over the waves");
+  // DK: head dim of Q, K and dQ; DV: of V and dO
+  constexpr int BR = 32 * NW, BC = 64, CGK = DK / 32, CGV = DV / 32;
+  using LK = TileLayout<DK>;
+  using LV = TileLayout<DV>;
+  constexpr int TBK = LK::BYTES, TBV = LV::BYTES, SB = TBK + TBV;
+  static_assert(LK::BLOCKS % NW == 0 && LV::BLOCKS % NW == 0, "tile blocks split evenly over the waves");
   // [buffer][K, V]; the epilogue reuses it as the waves' output staging
-  constexpr int SMEM = 2 * 2 * TB > NW * 32 * 144 ? 2 * 2 * TB : NW * 32 * 144;
+  constexpr int SMEM = 2 * SB > NW * 32 * 144 ? 2 * SB : NW * 32 * 144;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -340,27 +389,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the dK/dV kernel
   const int diag = nk - Nq;
-  const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const size_t head = (size_t)bh * Nq * DK, ohead = (size_t)bh * Nq * DV;
+  const size_t khead = (size_t)bh * Nk * DK, vhead = (size_t)bh * Nk * DV;
   const int q_first = qb * BR + 32 * wave;
   const int my_q = q_first + x;
 
-  u32x4 qf[D / 16], of[D / 16];
+  u32x4 qf[DK / 16], of[DV / 16];
   {
-    const uint16_t* qr = Q + head + (size_t)my_q * D + 8 * h;
-    const uint16_t* dr = dO + head + (size_t)my_q * D + 8 * h;
+    const uint16_t* qr = Q + head + (size_t)my_q * DK + 8 * h;
+    const uint16_t* dr = dO + ohead + (size_t)my_q * DV + 8 * h;
+    if constexpr (DK == DV) {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      qf[c] = my_q < Nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
-      of[c] = my_q < Nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < DK / 16; ++c) {
+        qf[c] = my_q < Nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
+        of[c] = my_q < Nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < DK / 16; ++c)
+        qf[c] = my_q < Nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < DV / 16; ++c)
+        of[c] = my_q < Nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
     }
   }
   const float c2 = scale * kLog2e;
   // (rows past N are never stored; the block's last rows may lie past the padding)
   const float nl2 = my_q < Nq ? NL[(size_t)bh * n_pad + my_q] * c2 : 0.f;
   const float nd = my_q < Nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
-  f32x16 dq[D / 32];
+  f32x16 dq[DK / 32];
 #pragma unroll
-  for (int b = 0; b < D / 32; ++b) dq[b] = f32x16{};
+  for (int b = 0; b < DK / 32; ++b) dq[b] = f32x16{};
 
   const int kv_end = CAUSAL ? min(nk, (qb + 1) * BR + diag) : nk;
   const int T = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
@@ -369,14 +428,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto load = [&](int j, int buf) {
     const int k0 = j * BC;
-    const unsigned base = lds0 + buf * 2 * TB;
-    const unsigned bytes = (unsigned)(nk - k0) * D * 2;
-    dma_tile<D, true, NW>(buffer_desc(K + khead + (size_t)k0 * D, bytes), base, 0, wave, lane);
-    dma_tile<D, false, NW>(buffer_desc(V + khead + (size_t)k0 * D, bytes), base + TB, 0, wave, lane);
+    const unsigned base = lds0 + buf * SB;
+    const unsigned rows = (unsigned)(nk - k0);
+    dma_tile<DK, true, NW>(buffer_desc(K + khead + (size_t)k0 * DK, rows * DK * 2), base, 0, wave, lane);
+    dma_tile<DV, false, NW>(buffer_desc(V + vhead + (size_t)k0 * DV, rows * DV * 2), base + TBK, 0,
+                            wave, lane);
   };
   const int trl = tr_lane(lane);
   // A operand of V (chunk-major block layout), as in the forward kernel
-  const int v_lane = (x >> 4) * CG * 1024 + (h * 16 + (x & 15)) * 16;
+  const int v_lane = (x >> 4) * CGV * 1024 + (h * 16 + (x & 15)) * 16;
 
   if (T > 0) load(0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -385,8 +445,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int buf = j & 1;
     if (j + 1 < T) load(j + 1, buf ^ 1);
     if (j < my_T) {
-      const uint8_t* kt = smem + buf * 2 * TB;
-      const uint8_t* vt = kt + TB;
+      const uint8_t* kt = smem + buf * SB;
+      const uint8_t* vt = kt + TBK;
       const int k0 = j * BC;
       // keys past the row (causal) or past the valid keys get no weight: such
       // a key has zero K and V rows, but its weight exp(-lse) need not be finite
@@ -395,11 +455,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
         f32x16 st = f32x16{}, dpt = f32x16{};
+        auto vop = [&](int c) {
+          return *(const u32x4*)(vt + v_lane + (2 * kb2 * CGV + (c >> 1)) * 1024 + (c & 1) * 512);
+        };
+        if constexpr (DK == DV) {
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          st = TT::mma(*(const u32x4*)(kt + rowmajor_a<D>(32 * kb2 + x, h, c)), qf[c], st);
-          dpt = TT::mma(*(const u32x4*)(vt + v_lane + (2 * kb2 * CG + (c >> 1)) * 1024 + (c & 1) * 512),
-                        of[c], dpt);
+          for (int c = 0; c < DK / 16; ++c) {
+            st = TT::mma(*(const u32x4*)(kt + rowmajor_a<DK>(32 * kb2 + x, h, c)), qf[c], st);
+            dpt = TT::mma(vop(c), of[c], dpt);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < DK / 16; ++c)
+            st = TT::mma(*(const u32x4*)(kt + rowmajor_a<DK>(32 * kb2 + x, h, c)), qf[c], st);
+#pragma unroll
+          for (int c = 0; c < DV / 16; ++c) dpt = TT::mma(vop(c), of[c], dpt);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -417,15 +487,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-          for (int b = 0; b < D / 32; ++b)
-            dq[b] = TT::mma(tr_read(kt + ((2 * kb2 + kc) * CG + b) * 1024 + trl), df[kc], dq[b]);
+          for (int b = 0; b < DK / 32; ++b)
+            dq[b] = TT::mma(tr_read(kt + ((2 * kb2 + kc) * CGK + b) * 1024 + trl), df[kc], dq[b]);
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
   uint8_t* stg = smem + wave * 32 * 144;
-  store_rows<TT, D>(dq, scale, stg, dQ + head, q_first, Nq, lane);
+  store_rows<TT, DK>(dq, scale, stg, dQ + head, q_first, Nq, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -521,14 +591,15 @@ __device__ __forceinline__ void sum_waves(f32x16* red, f32x16& s, f32x16& dp, in
 
 // dK, dV of 32 keys per workgroup.  S and dP in (query x key) orientation:
 // register r of lane (x, h) is query q0 + 8(r/4) + 4h + r%4, key k0 + x.
-template <int DSL, int DS, bool CAUSAL>
+// DSL, DSLV: a wave's columns of Q/K and of V/dO (DS waves each).
+template <int DSL, int DSLV, int DS, bool CAUSAL>
 __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int H,
     const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale, int n_split,
-    float* __restrict__ part, long long part_stride) {
-  constexpr int D = DSL * DS, NB = DSL / 32;
+    float* __restrict__ part, long long kstride, long long vstride) {
+  constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSL / 32, NBV = DSLV / 32;
   __shared__ f32x16 red[DS > 1 ? 2 * DS * 64 : 1];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = lane & 31, h = lane >> 5;
@@ -538,27 +609,42 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernels
   const int diag = nk - Nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
-  const int k0 = kb * 32, my_k = k0 + x, col0 = wave * DSL;
+  const size_t ohead = (size_t)bh * Nq * DV, vhead = (size_t)bh * Nk * DV;
+  const int k0 = kb * 32, my_k = k0 + x, col0 = wave * DSL, colv0 = wave * DSLV;
 
   // The block's K and V rows are held in registers for the whole kernel when
   // a wave's share is 128 columns or fewer; with 256 columns each 16-byte
   // piece is read from L2 where a product uses it, to stay within the wave's
   // 512 registers.
-  constexpr bool HOLD = DSL <= 128;
-  constexpr int NF = HOLD ? DSL / 8 : 1;
+  constexpr bool HOLD = DSL <= 128 && DSLV <= 128;
+  constexpr int NF = HOLD ? DSL / 8 : 1, NFV = HOLD ? DSLV / 8 : 1;
   const float* kr = K + khead + (size_t)my_k * D + col0 + 4 * h;
-  const float* vr = V + khead + (size_t)my_k * D + col0 + 4 * h;
-  f32x4 kf[NF], vf[NF];
+  const float* vr = V + vhead + (size_t)my_k * DV + colv0 + 4 * h;
+  f32x4 kf[NF], vf[NFV];
   if (HOLD) {
+    if constexpr (DSL == DSLV) {
 #pragma unroll
-    for (int u = 0; u < NF; ++u) {
-      kf[u] = my_k < nk ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
-      vf[u] = my_k < nk ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
+      for (int u = 0; u < NF; ++u) {
+        kf[u] = my_k < nk ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
+        vf[u] = my_k < nk ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NF; ++u) kf[u] = my_k < nk ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < NFV; ++u) vf[u] = my_k < nk ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
     }
   }
-  f32x16 dk[NB], dv[NB];
+  f32x16 dk[NB], dv[NBV];
+  if constexpr (DSL == DSLV) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) dk[b] = dv[b] = f32x16{};
+    for (int b = 0; b < NB; ++b) dk[b] = dv[b] = f32x16{};
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dk[b] = f32x16{};
+#pragma unroll
+    for (int b = 0; b < NBV; ++b) dv[b] = f32x16{};
+  }
   const float c2 = scale * kLog2e;
   const float* nl_row = NL + (size_t)bh * n_pad;
   const float* nd_row = ND + (size_t)bh * n_pad;
@@ -577,19 +663,34 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
     {
       const bool ok = q0 + x < Nq;
       const float* qr = Q + head + (size_t)(q0 + x) * D + col0 + 4 * h;
-      const float* gr = dO + head + (size_t)(q0 + x) * D + col0 + 4 * h;
+      const float* gr = dO + ohead + (size_t)(q0 + x) * DV + colv0 + 4 * h;
+      if constexpr (DSL == DSLV) {
 #pragma unroll
-      for (int u = 0; u < DSL / 8; ++u) {
-        const f32x4 qa = ok ? *(const f32x4*)(qr + 8 * u) : f32x4{0, 0, 0, 0};
-        const f32x4 ga = ok ? *(const f32x4*)(gr + 8 * u) : f32x4{0, 0, 0, 0};
-        const f32x4 ka = HOLD ? kf[HOLD ? u : 0]
-                              : (my_k < nk ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0});
-        const f32x4 va = HOLD ? vf[HOLD ? u : 0]
-                              : (my_k < nk ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0});
+        for (int u = 0; u < DSL / 8; ++u) {
+          const f32x4 qa = ok ? *(const f32x4*)(qr + 8 * u) : f32x4{0, 0, 0, 0};
+          const f32x4 ga = ok ? *(const f32x4*)(gr + 8 * u) : f32x4{0, 0, 0, 0};
+          const f32x4 ka = HOLD ? kf[HOLD ? u : 0]
+                                : (my_k < nk ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0});
+          const f32x4 va = HOLD ? vf[HOLD ? u : 0]
+                                : (my_k < nk ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0});
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[v], ka[v], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[v], va[v], dp, 0, 0, 0);
+          for (int v = 0; v < 4; ++v) {
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[v], ka[v], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[v], va[v], dp, 0, 0, 0);
+          }
+        }
+      } else {  // unequal widths: both fit in registers (at most 128 columns)
+#pragma unroll
+        for (int u = 0; u < DSL / 8; ++u) {
+          const f32x4 qa = ok ? *(const f32x4*)(qr + 8 * u) : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[v], kf[u][v], s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < DSLV / 8; ++u) {
+          const f32x4 ga = ok ? *(const f32x4*)(gr + 8 * u) : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[v], vf[u][v], dp, 0, 0, 0);
         }
       }
     }
@@ -614,29 +715,47 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      float gv[NB], qv[NB];
-      load_nb<NB>(dO + head + (size_t)q * D + col0 + NB * x, q < Nq, gv);
+      float gv[NBV], qv[NB];
+      load_nb<NBV>(dO + ohead + (size_t)q * DV + colv0 + NBV * x, q < Nq, gv);
       load_nb<NB>(Q + head + (size_t)q * D + col0 + NB * x, q < Nq, qv);
+      if constexpr (DSL == DSLV) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        dv[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(gv[b], s[r], dv[b], 0, 0, 0);
-        dk[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[b], dp[r], dk[b], 0, 0, 0);
+        for (int b = 0; b < NB; ++b) {
+          dv[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(gv[b], s[r], dv[b], 0, 0, 0);
+          dk[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[b], dp[r], dk[b], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NBV; ++b) dv[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(gv[b], s[r], dv[b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) dk[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[b], dp[r], dk[b], 0, 0, 0);
       }
     }
   }
   if (my_k < Nk) {  // every key row, those past the valid keys as zeros
-    // split: partial sums to the workspace, dK parts then dV parts
-    float* kout = part ? part + (size_t)split * part_stride : dK;
-    float* vout = part ? part + (size_t)(n_split + split) * part_stride : dV;
+    // split: partial sums to the workspace, the dK parts then the dV parts
+    float* kout = part ? part + (size_t)split * kstride : dK;
+    float* vout = part ? part + (size_t)n_split * kstride + (size_t)split * vstride : dV;
     float* kr = kout + khead + (size_t)my_k * D + col0;
-    float* vr = vout + khead + (size_t)my_k * D + col0;
+    float* vr = vout + vhead + (size_t)my_k * DV + colv0;
+    if constexpr (DSL == DSLV) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * h + (r & 3);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        kr[NB * i + b] = dk[b][r] * scale;
-        vr[NB * i + b] = dv[b][r];
+        for (int b = 0; b < NB; ++b) {
+          kr[NB * i + b] = dk[b][r] * scale;
+          vr[NB * i + b] = dv[b][r];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) kr[NB * i + b] = dk[b][r] * scale;
+#pragma unroll
+        for (int b = 0; b < NBV; ++b) vr[NBV * i + b] = dv[b][r];
       }
     }
   }
@@ -644,14 +763,14 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
 
 // dQ of 32 query rows per workgroup.  S^T and dP^T: register r of lane (x, h)
 // is key k0 + 8(r/4) + 4h + r%4, query q0 + x.
-template <int DSL, int DS, bool CAUSAL>
+template <int DSL, int DSLV, int DS, bool CAUSAL>
 __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     float* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
     int n_qblocks, int total, float scale, int n_split, float* __restrict__ part,
     long long part_stride) {
-  constexpr int D = DSL * DS, NB = DSL / 32;
+  constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSL / 32;
   __shared__ f32x16 red[DS > 1 ? 2 * DS * 64 : 1];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = lane & 31, h = lane >> 5;
@@ -663,20 +782,28 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
   const int diag = nk - Nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
-  const int q0 = qb * 32, my_q = q0 + x, col0 = wave * DSL;
+  const size_t ohead = (size_t)bh * Nq * DV, vhead = (size_t)bh * Nk * DV;
+  const int q0 = qb * 32, my_q = q0 + x, col0 = wave * DSL, colv0 = wave * DSLV;
 
   // Q and dO rows in registers, or read where used with 256 columns per wave
   // (as K and V in the dK/dV kernel)
-  constexpr bool HOLD = DSL <= 128;
-  constexpr int NF = HOLD ? DSL / 8 : 1;
+  constexpr bool HOLD = DSL <= 128 && DSLV <= 128;
+  constexpr int NF = HOLD ? DSL / 8 : 1, NFV = HOLD ? DSLV / 8 : 1;
   const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * h;
-  const float* grow = dO + head + (size_t)my_q * D + col0 + 4 * h;
-  f32x4 qf[NF], gf[NF];
+  const float* grow = dO + ohead + (size_t)my_q * DV + colv0 + 4 * h;
+  f32x4 qf[NF], gf[NFV];
   if (HOLD) {
+    if constexpr (DSL == DSLV) {
 #pragma unroll
-    for (int u = 0; u < NF; ++u) {
-      qf[u] = my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
-      gf[u] = my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
+      for (int u = 0; u < NF; ++u) {
+        qf[u] = my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+        gf[u] = my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NF; ++u) qf[u] = my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < NFV; ++u) gf[u] = my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
     }
   }
   const float c2 = scale * kLog2e;
@@ -696,19 +823,34 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
     {
       const bool ok = k0 + x < nk;
       const float* kr = K + khead + (size_t)(k0 + x) * D + col0 + 4 * h;
-      const float* vr = V + khead + (size_t)(k0 + x) * D + col0 + 4 * h;
+      const float* vr = V + vhead + (size_t)(k0 + x) * DV + colv0 + 4 * h;
+      if constexpr (DSL == DSLV) {
 #pragma unroll
-      for (int u = 0; u < DSL / 8; ++u) {
-        const f32x4 ka = ok ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
-        const f32x4 va = ok ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
-        const f32x4 qa = HOLD ? qf[HOLD ? u : 0]
-                              : (my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0});
-        const f32x4 ga = HOLD ? gf[HOLD ? u : 0]
-                              : (my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0});
+        for (int u = 0; u < DSL / 8; ++u) {
+          const f32x4 ka = ok ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
+          const f32x4 va = ok ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
+          const f32x4 qa = HOLD ? qf[HOLD ? u : 0]
+                                : (my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0});
+          const f32x4 ga = HOLD ? gf[HOLD ? u : 0]
+                                : (my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0});
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          st = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[v], qa[v], st, 0, 0, 0);
-          dpt = __builtin_amdgcn_mfma_f32_32x32x2f32(va[v], ga[v], dpt, 0, 0, 0);
+          for (int v = 0; v < 4; ++v) {
+            st = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[v], qa[v], st, 0, 0, 0);
+            dpt = __builtin_amdgcn_mfma_f32_32x32x2f32(va[v], ga[v], dpt, 0, 0, 0);
+          }
+        }
+      } else {  // unequal widths: both fit in registers (at most 128 columns)
+#pragma unroll
+        for (int u = 0; u < DSL / 8; ++u) {
+          const f32x4 ka = ok ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) st = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[v], qf[u][v], st, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < DSLV / 8; ++u) {
+          const f32x4 va = ok ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dpt = __builtin_amdgcn_mfma_f32_32x32x2f32(va[v], gf[u][v], dpt, 0, 0, 0);
         }
       }
     }
@@ -746,7 +888,7 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
 // host side
 size_t padded_rows(long long BH, int N) { return (size_t)BH * (size_t)((N + kRowPad - 1) / kRowPad * kRowPad); }
 
-template <class TT, int D>
+template <class TT, int DK, int DV>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, int BH, int H, int Nq, int Nk,
                       const int* k_len, float scale, bool causal, float* ws, hipStream_t st) {
@@ -755,8 +897,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   float* nl = ws;
   float* nd = ws + prow;
   {
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((attn_bwd_prep<TT, D>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256), 0,
+    constexpr int RPB = 256 / (DV / 8);  // delta = <dO, O> over the value dim
+    hipLaunchKernelGGL((attn_bwd_prep<TT, DV>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256), 0,
                        st, (const uint16_t*)o, (const uint16_t*)dout, lse, nl, nd, Nq, n_pad, prow,
                        1.f / scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -768,19 +910,19 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   const int tk = nkb * BH, tq = nqb * BH;
   const dim3 bk(64 * NWK), bq(64 * NWQ);
   if (causal) {
-    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, true, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dkdv<TT, DK, DV, true, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq<TT, D, true, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dq<TT, DK, DV, true, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv<TT, D, false, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dkdv<TT, DK, DV, false, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq<TT, D, false, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((attn_bwd_dq<TT, DK, DV, false, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
                        (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
   }
@@ -810,7 +952,8 @@ struct BwdSplit {
   size_t bytes = 0;  // partial sums
 };
 
-BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int d, int dtype) {
+// dk, dv: head dims of Q/K and of V/dO
+BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype) {
   BwdSplit p;
   if (dtype != FA_DTYPE_FP32) return p;
   int cus = 0;
@@ -823,48 +966,49 @@ BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int d, int dtype) {
   };
   p.kv = pick(nkb * BH, nqb);
   p.q = pick(nqb * BH, nkb);
-  if (p.kv > 1) p.bytes += (size_t)p.kv * 2 * BH * Nk * d * sizeof(float);
-  if (p.q > 1) p.bytes += (size_t)p.q * BH * Nq * d * sizeof(float);
+  if (p.kv > 1) p.bytes += (size_t)p.kv * BH * Nk * (size_t)(dk + dv) * sizeof(float);
+  if (p.q > 1) p.bytes += (size_t)p.q * BH * Nq * (size_t)dk * sizeof(float);
   return p;
 }
 
-template <int DSL, int DS>
+template <int DSL, int DSLV, int DS>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int BH,
                           int H, int Nq, int Nk, const int* k_len, float scale, bool causal,
                           float* ws, const BwdSplit& sp, hipStream_t st) {
-  constexpr int D = DSL * DS;
+  constexpr int D = DSL * DS, DV = DSLV * DS;
   const int n_pad = (Nq + kRowPad - 1) / kRowPad * kRowPad;
   const long long prow = (long long)BH * n_pad;
   float* nl = ws;
   float* nd = ws + prow;
   {
-    constexpr int TPR = D / 4 < 64 ? D / 4 : 64, RPB = 256 / TPR;
-    hipLaunchKernelGGL((attn_bwd_prep_f32<D>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256),
+    constexpr int TPR = DV / 4 < 64 ? DV / 4 : 64, RPB = 256 / TPR;  // delta over the value dim
+    hipLaunchKernelGGL((attn_bwd_prep_f32<DV>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256),
                        0, st, (const float*)o, (const float*)dout, lse, nl, nd, Nq, n_pad, prow,
                        1.f / scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int nkb = (Nk + 31) / 32, nqb = (Nq + 31) / 32;
   const int tk = nkb * BH * sp.kv, tq = nqb * BH * sp.q;
-  const long long kstride = (long long)BH * Nk * D, qstride = (long long)BH * Nq * D;
+  const long long kstride = (long long)BH * Nk * D, vstride = (long long)BH * Nk * DV;
+  const long long qstride = (long long)BH * Nq * D;
   float* kvpart = sp.kv > 1 ? ws + 2 * prow : nullptr;
-  float* qpart = sp.q > 1 ? ws + 2 * prow + (sp.kv > 1 ? 2 * sp.kv * kstride : 0) : nullptr;
+  float* qpart = sp.q > 1 ? ws + 2 * prow + (sp.kv > 1 ? sp.kv * (kstride + vstride) : 0) : nullptr;
   const dim3 blk(64 * DS);
   if (causal) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DS, true>), dim3(tk), blk, 0, st, (const float*)q,
+    hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DSLV, DS, true>), dim3(tk), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
-                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride);
+                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DS, true>), dim3(tq), blk, 0, st, (const float*)q,
+    hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DSLV, DS, true>), dim3(tq), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
                        Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DS, false>), dim3(tk), blk, 0, st, (const float*)q,
+    hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DSLV, DS, false>), dim3(tk), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
-                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride);
+                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DS, false>), dim3(tq), blk, 0, st, (const float*)q,
+    hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DSLV, DS, false>), dim3(tq), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
                        Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
   }
@@ -877,7 +1021,7 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
   };
   if (sp.kv > 1) {
     if (hipError_t e = sum(kvpart, dk, kstride, sp.kv); e != hipSuccess) return e;
-    if (hipError_t e = sum(kvpart + sp.kv * kstride, dv, kstride, sp.kv); e != hipSuccess) return e;
+    if (hipError_t e = sum(kvpart + sp.kv * kstride, dv, vstride, sp.kv); e != hipSuccess) return e;
   }
   if (sp.q > 1)
     if (hipError_t e = sum(qpart, dq, qstride, sp.q); e != hipSuccess) return e;
@@ -885,6 +1029,22 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+namespace {
+
+template <class TT>
+hipError_t launch_bwd_dims(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int bh, int H, int Nq, int Nk, const int* k_len, float scale,
+                           bool causal, int d_qk, int d_v, float* ws, hipStream_t st) {
+  if (d_qk == 64)
+    return d_v == 64 ? launch_bwd<TT, 64, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
+                     : launch_bwd<TT, 64, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+  return d_v == 64 ? launch_bwd<TT, 128, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
+                   : launch_bwd<TT, 128, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+}
 
 }  // namespace
 
@@ -897,23 +1057,37 @@ int fa_bwd_supported(int d, int dtype, int causal) {
   return 0;
 }
 
-size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !fa_bwd_supported(d, dtype, causal)) return 0;
+int fa_bwd_gen_supported(int d_qk, int d_v, int dtype, int causal) {
+  if (d_qk == d_v) return fa_bwd_supported(d_qk, dtype, causal);
+  if (causal != 0 && causal != 1) return 0;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_FP32) return 0;
+  return (d_qk == 64 || d_qk == 128) && (d_v == 64 || d_v == 128);
+}
+
+size_t fa_bwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v, int causal,
+                                 int dtype) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !fa_bwd_gen_supported(d_qk, d_v, dtype, causal))
+    return 0;
   const long long BH = (long long)B * H;
   if (BH > (1LL << 24) || BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return 0;
-  return 2 * padded_rows(BH, Nq) * sizeof(float) + plan_bwd_split(BH, Nq, Nk, d, dtype).bytes;
+  return 2 * padded_rows(BH, Nq) * sizeof(float) +
+         plan_bwd_split(BH, Nq, Nk, d_qk, d_v, dtype).bytes;
+}
+
+size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
+  return fa_bwd_gen_workspace_size(B, H, Nq, Nk, d, d, causal, dtype);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) {
   return fa_bwd_ex_workspace_size(B, H, N, N, d, causal, dtype);
 }
 
-int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
-              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
-              float scale, int causal, int dtype, const int* k_len, void* workspace,
-              size_t workspace_bytes, void* stream) {
+int fa_bwd_gen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+               int d_qk, int d_v, float scale, int causal, int dtype, const int* k_len,
+               void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d_qk <= 0 || d_v <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   const long long BH = (long long)B * H;
@@ -922,11 +1096,13 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
     return FA_ERR_INVALID_ARG;
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
     return FA_ERR_UNSUPPORTED;
-  if (!fa_bwd_supported(d, dtype, causal)) return FA_ERR_UNSUPPORTED;
+  if (!fa_bwd_gen_supported(d_qk, d_v, dtype, causal)) return FA_ERR_UNSUPPORTED;
   // per-head byte offsets (plus one tile of slack) fit the 32-bit buffer offsets
   const long long elem = dtype == FA_DTYPE_FP32 ? 4 : 2;
-  if (((long long)(Nq > Nk ? Nq : Nk) + 128) * d * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
-  if (!workspace || workspace_bytes < fa_bwd_ex_workspace_size(B, H, Nq, Nk, d, causal, dtype))
+  const long long dmax = d_qk > d_v ? d_qk : d_v;
+  if (((long long)(Nq > Nk ? Nq : Nk) + 128) * dmax * elem > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (!workspace ||
+      workspace_bytes < fa_bwd_gen_workspace_size(B, H, Nq, Nk, d_qk, d_v, causal, dtype))
     return FA_ERR_INVALID_ARG;
   for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv,
                         (const void*)workspace})
@@ -935,24 +1111,33 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   hipStream_t st = (hipStream_t)stream;
   const int bh = (int)BH;
   float* ws = (float*)workspace;
-  const BwdSplit sp = plan_bwd_split(BH, Nq, Nk, d, dtype);
+  const BwdSplit sp = plan_bwd_split(BH, Nq, Nk, d_qk, d_v, dtype);
   hipError_t e;
   if (dtype == FA_DTYPE_BF16) {
-    e = d == 64 ? launch_bwd<Bf16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
-                : launch_bwd<Bf16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+    e = launch_bwd_dims<Bf16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, st);
   } else if (dtype == FA_DTYPE_FP16) {
-    e = d == 64 ? launch_bwd<F16, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
-                : launch_bwd<F16, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+    e = launch_bwd_dims<F16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, st);
+  } else if (d_qk != d_v) {
+    e = d_qk == 64 ? launch_bwd_f32<64, 128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st)
+                   : launch_bwd_f32<128, 64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st);
   } else {
-    switch (d) {
-      case 64: e = launch_bwd_f32<64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      case 128: e = launch_bwd_f32<128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      case 256: e = launch_bwd_f32<128, 2>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      case 512: e = launch_bwd_f32<128, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      default: e = launch_bwd_f32<256, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+    switch (d_qk) {
+      case 64: e = launch_bwd_f32<64, 64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      case 128: e = launch_bwd_f32<128, 128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      case 256: e = launch_bwd_f32<128, 128, 2>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      case 512: e = launch_bwd_f32<128, 128, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      default: e = launch_bwd_f32<256, 256, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
     }
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+              float scale, int causal, int dtype, const int* k_len, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return fa_bwd_gen(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, d, scale, causal, dtype,
+                    k_len, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -259,6 +259,29 @@ size_t fa_bwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal,
 /* 1 when fa_bwd has kernels for (d, dtype, causal), else 0. */
 int fa_bwd_supported(int d, int dtype, int causal);
 
+/*
+ * fa_bwd_gen -- the gradients of fa_fwd_gen's attention (value head dim
+ * apart from the query/key one): q, dq [B][H][Nq][d_qk]; k, dk
+ * [B][H][Nk][d_qk]; v, dv [B][H][Nk][d_v]; o, dout [B][H][Nq][d_v]; lse
+ * [B][H][Nq].  dP_ij = dout_i . v_j and delta_i = dout_i . o_i contract the
+ * d_v columns; the scores, dq and dk the d_qk columns.  Supported pairs:
+ * fa_bwd_gen_supported (d_qk = d_v as for fa_bwd; otherwise d_qk, d_v in
+ * {64, 128} for bf16, fp16 and fp32).  The workspace must hold
+ * fa_bwd_gen_workspace_size(...) bytes.  Everything else is as for fa_bwd_ex,
+ * which is fa_bwd_gen with d_qk = d_v = d.
+ */
+int fa_bwd_gen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+               int d_qk, int d_v, float scale, int causal, int dtype, const int* k_len,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of fa_bwd_gen (as fa_bwd_ex_workspace_size, for both head dims). */
+size_t fa_bwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v, int causal,
+                                 int dtype);
+
+/* 1 when fa_bwd_gen has kernels for (d_qk, d_v, dtype, causal), else 0. */
+int fa_bwd_gen_supported(int d_qk, int d_v, int dtype, int causal);
+
 /* 1 when fa_fwd has a kernel for (d, dtype, causal), else 0. */
 int fa_fwd_supported(int d, int dtype, int causal);
 

@@ -247,3 +247,31 @@ def test_gen_workspace_size_matches_equal_dims():
             assert fa.fa_fwd_gen_workspace_size(1, 1, N, N, d, d, 0, dt) == \
                 fa.fa_fwd_ex_workspace_size(1, 1, N, N, d, 0, dt)
     assert fa.fa_fwd_gen_workspace_size(1, 1, 16, 16, 64, 256, 0, fa.FA_DTYPE_BF16) == 0
+
+
+def test_bwd_gen_table_and_workspace():
+    for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16, fa.FA_DTYPE_FP32):
+        for dk, dv in ((64, 128), (128, 64)):
+            assert fa.fa_bwd_gen_supported(dk, dv, dt, 0) and fa.fa_bwd_gen_supported(dk, dv, dt, 1)
+        assert not fa.fa_bwd_gen_supported(64, 256, dt, 0)
+        for d in (64, 128, 256, 1024):
+            assert fa.fa_bwd_gen_supported(d, d, dt, 1) == fa.fa_bwd_supported(d, dt, 1)
+            assert fa.fa_bwd_gen_workspace_size(2, 3, 100, 50, d, d, 1, dt) == \
+                fa.fa_bwd_ex_workspace_size(2, 3, 100, 50, d, 1, dt)
+    # two fp32 statistics per query row (no split on a CPU-only host)
+    assert fa.fa_bwd_gen_workspace_size(2, 3, 100, 50, 64, 128, 1, fa.FA_DTYPE_BF16) == 2 * 6 * 128 * 4
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                B=1, H=1, Nq=16, Nk=40, d_qk=64, d_v=128, scale=0.125, causal=0,
+                dtype=fa.FA_DTYPE_BF16, k_len=None, ws=FAKE, ws_bytes=1 << 20)
+
+    def run(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_bwd_gen(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"],
+                             a["dk"], a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["d_qk"],
+                             a["d_v"], a["scale"], a["causal"], a["dtype"], a["k_len"], a["ws"],
+                             a["ws_bytes"], None)
+    for kw in (dict(d_v=0), dict(Nk=0), dict(dv=None), dict(ws=None), dict(ws_bytes=4)):
+        assert run(**kw) == fa.FA_ERR_INVALID_ARG, kw
+    for kw in (dict(d_v=256), dict(d_qk=32), dict(dtype=4), dict(v=FAKE + 4)):
+        assert run(**kw) == fa.FA_ERR_UNSUPPORTED, kw

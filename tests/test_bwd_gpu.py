@@ -206,3 +206,50 @@ def test_unequal_lengths_and_padding_match_gradient_oracle(dt, d, Nq, Nk, k_len,
         assert torch.all(dk[b, :, L:] == 0) and torch.all(dv[b, :, L:] == 0)
         empty = [i for i in range(Nq) if L == 0 or (causal and i + L - Nq < 0)]
         assert torch.all(dq[b, :, empty] == 0)
+
+
+# ------------------------------------------------------------------ value head dim of its own
+def dv_inputs(B, H, Nq, Nk, dk, dv, dt, seed):
+    q, k, _ = make_qkv(B, H, max(Nq, Nk), dk, dt, seed)
+    _, _, v = make_qkv(B, H, Nk, dv, dt, seed + 1)
+    g = make_dout(B, H, Nq, dv, dt, seed + 2)
+    return q[:, :, :Nq].contiguous(), k[:, :, :Nk].contiguous(), v, g
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("Nq,Nk,k_len", [(200, 200, None), (77, 300, None), (300, 77, None),
+                                         (190, 333, [333, 150, 0])])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unequal_head_dims_match_gradient_oracle(dt, dk, dv, Nq, Nk, k_len, causal):
+    B, H = 3, 2
+    q, k, v, g = dv_inputs(B, H, Nq, Nk, dk, dv, dt, 8000 + Nq + 3 * Nk + dk + int(causal))
+    scale = 1 / math.sqrt(dk)
+    kl = None if k_len is None else torch.tensor(k_len, dtype=torch.int32, device="cuda")
+    qc, kc, vc, gc = (t.cuda() for t in (q, k, v, g))
+    o, lse = fa.attention(qc, kc, vc, causal=causal, scale=scale, k_len=kl)
+    dq, dk_, dv_ = fa.attention_bwd(qc, kc, vc, o, lse, gc, causal=causal, scale=scale, k_len=kl)
+    torch.cuda.synchronize()
+    assert dq.shape == q.shape and dk_.shape == k.shape and dv_.shape == v.shape
+    rq, rk, rv = oracle.attention_bwd_ex(q, k, v, g, scale, causal, k_len)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk_, rk), ("dv", dv_, rv)):
+        check(errors(got, ref), DT[dt], name)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_narrow_qk_gradients_equal_the_zero_padded_equal_dim_call(dt, causal):
+    """d_qk = 64, d_v = 128 against d = 128 with Q and K zero beyond column 64
+    (same o, lse, dO): the extra score columns add exact zeros, so dq and dk
+    are the first 64 columns of the padded call's, bit for bit, the rest zero,
+    and dv is equal."""
+    B, H, N = 2, 4, 700
+    q, k, v, g = (t.cuda() for t in dv_inputs(B, H, N, N, 64, 128, dt, 8100 + int(causal)))
+    o, lse = fa.attention(q, k, v, causal=causal, scale=0.1)
+    a = fa.attention_bwd(q, k, v, o, lse, g, causal=causal, scale=0.1)
+    pad = lambda x: torch.cat([x, torch.zeros_like(x)], dim=3).contiguous()
+    b = fa.attention_bwd(pad(q), pad(k), v, o, lse, g, causal=causal, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0][..., :64]) and torch.all(b[0][..., 64:] == 0)
+    assert torch.equal(a[1], b[1][..., :64]) and torch.all(b[1][..., 64:] == 0)
+    assert torch.equal(a[2], b[2])
