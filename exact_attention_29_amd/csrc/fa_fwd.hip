@@ -1016,6 +1016,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"

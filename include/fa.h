@@ -288,7 +288,7 @@ int fa_fwd_supported(int d, int dtype, int causal);
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* fa_status_string(int status);
 
-/* Library version, major*10000 + minor*100 + patch (200: 0.2.0). */
+/* Library version, major*10000 + minor*100 + patch (300: 0.3.0). */
 int fa_version(void);
 
 #ifdef __cplusplus
