@@ -134,3 +134,16 @@ def make_dout(B: int, H: int, N: int, d: int, dtype: str, seed: int):
     x = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
     td = _DTYPES[dtype]
     return x.to(td) if td != torch.float32 else x
+
+
+def make_normal_device(shape, dtype: str, seed: int, device="cuda"):
+    """A seeded i.i.d. N(0, 1) tensor drawn on the device (torch's device
+    generator), cast to `dtype` (round to nearest even): for inputs too large
+    to draw on the host in reasonable time, e.g. key sequences of millions of
+    rows.  The tests hand the same cast tensor (copied to the host) to the
+    oracle."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(*shape, dtype=torch.float32, generator=g, device=device)
+    td = _DTYPES[dtype]
+    return x.to(td) if td != torch.float32 else x

@@ -275,3 +275,12 @@ def test_bwd_gen_table_and_workspace():
         assert run(**kw) == fa.FA_ERR_INVALID_ARG, kw
     for kw in (dict(d_v=256), dict(d_qk=32), dict(dtype=4), dict(v=FAKE + 4)):
         assert run(**kw) == fa.FA_ERR_UNSUPPORTED, kw
+
+
+def test_largest_key_count_is_the_offset_limit():
+    """(N + 128) * d * element bytes must fit the 31-bit buffer offsets: the
+    last accepted and the first rejected key counts."""
+    for dt, elem in ((fa.FA_DTYPE_BF16, 2), (fa.FA_DTYPE_FP32, 4)):
+        n_max = 0x7fffffff // (128 * elem) - 128
+        over = call_ex(Nq=16, Nk=n_max + 1, d=128, dtype=dt)
+        assert over == fa.FA_ERR_UNSUPPORTED
