@@ -17,7 +17,11 @@ Extra objects on the line:
                   the stream the kernel runs on) against the bf16 dense MFMA
                   peak; `traffic` is the HBM bytes per launch measured with
                   rocprofv3 counters, read from the profile summary of the
-                  same kernel source (null if the source changed since).
+                  same kernel source (null if the source changed since);
+                  `counters` likewise gives the matrix-core busy fraction,
+                  the shader clock and the LDS bank-conflict rate from the
+                  committed counter summary; `kernel_ms_median` is the median
+                  launch beside the mean.
   cpu_baseline -- the fp64 oracle timed on the host cores on a bounded,
                   seeded sample of rows of the same workload, in the same
                   unit; the GPU output on those rows is compared too.
@@ -82,6 +86,25 @@ def read_traffic(w, pass_: str = "fwd"):
     if not h or not b or h.group(1) != kernel_source_hash(pass_):
         return None
     return float(b.group(1))
+
+
+def read_counters(w, pass_: str = "fwd"):
+    """Matrix-core busy fraction, shader clock and LDS bank-conflict rate from
+    profiles/<kernel tag>.counters.md, if taken from the current kernel
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag(w, pass_)}.counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    if not h or h.group(1) != kernel_source_hash(pass_):
+        return None
+    out = {}
+    for key, label in (("mfma_busy_frac", "MFMA busy fraction"), ("shader_clock_ghz", "Shader clock GHz"),
+                       ("lds_bank_conflict_per_active", "LDS bank-conflict cycles per LDS-active cycle")):
+        m = re.search(re.escape(label) + r"[^`]*`([0-9.eE+-]+)`", text)
+        out[key] = float(m.group(1)) if m else None
+    return out
 
 
 def copy_calibration(mib: int) -> None:
@@ -239,7 +262,8 @@ def main() -> int:
         b.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    per_launch = [a.elapsed_time(b) for a, b in ev]
+    kernel_ms = float(np.mean(per_launch))
 
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -262,6 +286,8 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 4),
+                     "kernel_ms_median": round(float(np.median(per_launch)), 4),
+                     "counters": read_counters(w, args.pass_),
                      "algorithmic_bytes": algo_bytes,
                      "kernel_source_sha256_16": kernel_source_hash(args.pass_)},
     }

@@ -22,8 +22,10 @@
 //    through double-buffered LDS.  S = Q K^T and dP = dO V^T are computed in
 //    (query x key) orientation, so each lane owns one key column and its P and
 //    dS values are already the B operand of dV^T += dO^T P and
-//    dK^T += Q^T dS; dO^T and Q^T are read out of the row-major LDS tiles with
-//    ds_read_b64_tr_b16 (the V^T reads of the forward kernel).
+//    dK^T += Q^T dS; dO^T and Q^T are read out of the same LDS tiles with
+//    ds_read_b64_tr_b16 (the V^T reads of the forward kernel).  Tiles read
+//    both ways are row-major with a chunk swizzle that keeps both kinds of
+//    read free of bank conflicts.
 //  * attn_bwd_dq: a workgroup owns 128 query rows (32 per wave) with Q and dO
 //    in registers and streams 64-key tiles of K and V, like the forward pass:
 //    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read by the
@@ -59,30 +61,40 @@ __device__ __forceinline__ float widen<F16>(uint16_t x) {
 
 constexpr int kRowPad = 32;  // statistic rows are padded to this multiple
 
-// Byte offset, inside a row-major LDS tile (1 KB blocks of 16 rows x 4
-// sixteen-byte chunks; block (rg, cg) at (rg * D/32 + cg) KB, row ri chunk ci
-// at (ri * 4 + ci) * 16), of the 16 bytes lane (row, hf) supplies as the A
-// operand of a 32x32x16 product over head-dim chunk c: elements
-// [16c + 8hf, 16c + 8hf + 8) of row `row`.
+// The streamed tiles that are read both as rows and transposed (Q and dO in
+// the dK/dV kernel, K in the dQ kernel) use the swizzled row-major layout of
+// TileLayout::s_src: 1 KB blocks of 16 rows x 4 sixteen-byte chunks, block
+// (rg, cg) at (rg * D/32 + cg) KB, row ri chunk ci in slot 4ri + (ci ^ ri/4).
+__device__ __forceinline__ int swz_slot(int ri, int ci) { return 4 * ri + (ci ^ (ri >> 2)); }
+
+// Byte offset, inside such a tile, of the 16 bytes lane (row, hf) supplies as
+// the A operand of a 32x32x16 product over head-dim chunk c: elements
+// [16c + 8hf, 16c + 8hf + 8) of row `row`.  A 16-lane group reads 16 rows of
+// one chunk: 16 distinct slots modulo 16, so no bank conflicts.
 template <int D>
 __device__ __forceinline__ int rowmajor_a(int row, int hf, int c) {
   const int t = 2 * c + hf;  // 16-byte chunk of the row
-  return ((row >> 4) * (D / 32) + (t >> 2)) * 1024 + ((row & 15) * 4 + (t & 3)) * 16;
+  return ((row >> 4) * (D / 32) + (t >> 2)) * 1024 + swz_slot(row & 15, t & 3) * 16;
 }
 
-// Lane part of the transpose read (ds_read_b64_tr_b16) of a row-major block:
-// two reads, at this offset and 512 bytes on, give lane (x = lane % 32,
-// h = lane / 32) rows {4h .. 4h+3} and {8 + 4h .. 8 + 4h + 3} of column x of
-// the block's 32 columns -- the A-operand order that matches a B operand
-// packed from accumulator registers 0..7 (rows 8(r/4) + 4h + r%4).
-__device__ __forceinline__ int tr_lane(int lane) {
+// Lane parts of the transpose read (ds_read_b64_tr_b16) of one such block:
+// the reads at offsets lo and hi give lane (x = lane % 32, h = lane / 32)
+// rows {4h .. 4h+3} and {8 + 4h .. 8 + 4h + 3} of column x of the block's
+// 32 columns -- the A-operand order that matches a B operand packed from
+// accumulator registers 0..7 (rows 8(r/4) + 4h + r%4).  Each lane reads 8
+// bytes of row r (first read: r in 0..7, second: r + 8), chunk ch.
+struct TrLane {
+  int lo, hi;
+};
+__device__ __forceinline__ TrLane tr_lane(int lane) {
   const int i = lane & 15, grp = lane >> 4;
-  return (4 * (grp >> 1) + (i >> 2)) * 64 + (2 * (grp & 1) + ((i & 3) >> 1)) * 16 + 8 * (i & 1);
+  const int r = 4 * (grp >> 1) + (i >> 2), ch = 2 * (grp & 1) + ((i & 3) >> 1), half = 8 * (i & 1);
+  return TrLane{swz_slot(r, ch) * 16 + half, swz_slot(r + 8, ch) * 16 + half};
 }
 
-__device__ __forceinline__ u32x4 tr_read(const uint8_t* p) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 512));
+__device__ __forceinline__ u32x4 tr_read(const uint8_t* blk, TrLane t) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(blk + t.lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(blk + t.hi));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
 }
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int i = 0; i < (TBLKQ + NW - 1) / NW; ++i) {
         const int blk = wave + i * NW;
         if (blk < TBLKQ) {  // with more waves than blocks, some waves load none
-          const int el = TileLayout<DK>::v_src(blk, lane);
+          const int el = TileLayout<DK>::s_src(blk, lane);
           dma16(dq, base + blk * 1024, el * 2);
           dma16(dd, base + TBQ + blk * 1024, el * 2);
         }
@@ -255,16 +267,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int i = 0; i < (TBLKQ + NW - 1) / NW; ++i) {
         const int blk = wave + i * NW;
-        if (blk < TBLKQ) dma16(dq, base + blk * 1024, TileLayout<DK>::v_src(blk, lane) * 2);
+        if (blk < TBLKQ) dma16(dq, base + blk * 1024, TileLayout<DK>::s_src(blk, lane) * 2);
       }
 #pragma unroll
       for (int i = 0; i < (TBLKD + NW - 1) / NW; ++i) {
         const int blk = wave + i * NW;
-        if (blk < TBLKD) dma16(dd, base + TBQ + blk * 1024, TileLayout<DV>::v_src(blk, lane) * 2);
+        if (blk < TBLKD) dma16(dd, base + TBQ + blk * 1024, TileLayout<DV>::s_src(blk, lane) * 2);
       }
     }
   };
-  const int trl = tr_lane(lane);
+  const TrLane trl = tr_lane(lane);
 
   if (qt0 < nqt) load(qt0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -329,19 +341,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
           for (int b = 0; b < DV / 32; ++b) {
-            const int off = (kc * CGV + b) * 1024 + trl;
-            dv[b] = TT::mma(tr_read(dt + off), pf[kc], dv[b]);
-            dk[b] = TT::mma(tr_read(qt + off), df[kc], dk[b]);
+            const int off = (kc * CGV + b) * 1024;
+            dv[b] = TT::mma(tr_read(dt + off, trl), pf[kc], dv[b]);
+            dk[b] = TT::mma(tr_read(qt + off, trl), df[kc], dk[b]);
           }
       } else {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
           for (int b = 0; b < DV / 32; ++b)
-            dv[b] = TT::mma(tr_read(dt + (kc * CGV + b) * 1024 + trl), pf[kc], dv[b]);
+            dv[b] = TT::mma(tr_read(dt + (kc * CGV + b) * 1024, trl), pf[kc], dv[b]);
 #pragma unroll
           for (int b = 0; b < DK / 32; ++b)
-            dk[b] = TT::mma(tr_read(qt + (kc * CGK + b) * 1024 + trl), df[kc], dk[b]);
+            dk[b] = TT::mma(tr_read(qt + (kc * CGK + b) * 1024, trl), df[kc], dk[b]);
         }
       }
     }
@@ -356,8 +368,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  NW = 4 waves x 32 queries; key tiles of 64 keys: K row-major (read as
-// rows and, transposed, as K^T), V chunk-major (read as rows).
+// dQ.  NW = 4 waves x 32 queries; key tiles of 64 keys: K swizzled row-major
+// (read as rows and, transposed, as K^T), V chunk-major (read as rows).
 //
 // Register layouts (lane (x, h)):
 //   Q and dO rows (whole kernel): row[q_first + x][16c + 8h .. +7], the B
@@ -430,11 +442,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int k0 = j * BC;
     const unsigned base = lds0 + buf * SB;
     const unsigned rows = (unsigned)(nk - k0);
-    dma_tile<DK, true, NW>(buffer_desc(K + khead + (size_t)k0 * DK, rows * DK * 2), base, 0, wave, lane);
+    dma_tile_swz<DK, NW>(buffer_desc(K + khead + (size_t)k0 * DK, rows * DK * 2), base, wave, lane);
     dma_tile<DV, false, NW>(buffer_desc(V + vhead + (size_t)k0 * DV, rows * DV * 2), base + TBK, 0,
                             wave, lane);
   };
-  const int trl = tr_lane(lane);
+  const TrLane trl = tr_lane(lane);
   // A operand of V (chunk-major block layout), as in the forward kernel
   const int v_lane = (x >> 4) * CGV * 1024 + (h * 16 + (x & 15)) * 16;
 
@@ -488,7 +500,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
           for (int b = 0; b < DK / 32; ++b)
-            dq[b] = TT::mma(tr_read(kt + ((2 * kb2 + kc) * CGK + b) * 1024 + trl), df[kc], dq[b]);
+            dq[b] = TT::mma(tr_read(kt + ((2 * kb2 + kc) * CGK + b) * 1024, trl), df[kc], dq[b]);
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

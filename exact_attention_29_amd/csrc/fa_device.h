@@ -132,6 +132,16 @@ struct TileLayout {
     const int rg = blk / CG, cg = blk % CG;
     return (16 * rg + (L >> 2)) * D + 8 * (4 * cg + (L & 3));
   }
+  // Swizzled row-major block (for a tile read both as rows and transposed):
+  // row ri keeps its four chunks in slots 4ri .. 4ri+3, chunk ci in slot
+  // 4ri + (ci ^ (ri / 4)).  Sixteen rows of one chunk (an A-operand read)
+  // then fall in sixteen distinct 16-byte bank groups, while each row's 64
+  // bytes stay together for the transposing reads.
+  static __device__ __forceinline__ int s_src(int blk, int L) {
+    const int rg = blk / CG, cg = blk % CG;
+    const int ri = L >> 2, ci = (L & 3) ^ (ri >> 2);
+    return (16 * rg + ri) * D + 8 * (4 * cg + ci);
+  }
 };
 
 // A raw buffer descriptor as four SGPRs: 48-bit base, no stride,
@@ -167,6 +177,18 @@ __device__ __forceinline__ void dma_tile(u32x4 desc, unsigned lds_tile, int key0
     const int blk = wave + i * NW;
     const int el = key0 * D + (IS_V ? L::v_src(blk, lane) : L::k_src(blk, lane));
     dma16(desc, lds_tile + blk * 1024, el * 2);
+  }
+}
+
+// The same for a tile in the swizzled row-major layout (TileLayout::s_src).
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile_swz(u32x4 desc, unsigned lds_tile, int wave, int lane) {
+  using L = TileLayout<D>;
+  static_assert(L::BLOCKS % NW == 0, "tile blocks split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < L::BLOCKS / NW; ++i) {
+    const int blk = wave + i * NW;
+    dma16(desc, lds_tile + blk * 1024, L::s_src(blk, lane) * 2);
   }
 }
 
