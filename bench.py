@@ -29,6 +29,9 @@ Extra objects on the line:
 Other modes (used to take the profiles):
   --no-cpu-baseline        skip the oracle leg
   --copy-calibration MiB   run only a plain device copy of that size
+  --gemm-reference N       run only a sustained bf16 N x N x N torch.matmul (the
+                           vendor GEMM library) and print its TFLOP/s: a
+                           practical matrix-core reference on the same box
 """
 from __future__ import annotations
 
@@ -119,6 +122,30 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
 
 
+def gemm_reference(n: int, steps: int = 20) -> None:
+    """Sustained throughput of a plain bf16 GEMM through torch (hipBLASLt):
+    what the vendor library reaches on dense matrix products on this machine."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16).t().contiguous()
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        torch.matmul(a, b, out=c)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    tf = 2.0 * n ** 3 / ms / 1e9
+    print(json.dumps({"gemm_reference": f"bf16 {n}x{n}x{n} torch.matmul", "ms": round(ms, 4),
+                      "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "steps": steps}))
+
+
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s: float, seed: int = 0):
     """Time the oracle on a seeded uniform sample of rows sized to ~target_s."""
     import oracle
@@ -201,6 +228,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    ap.add_argument("--gemm-reference", type=int, default=0, metavar="N")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -213,6 +241,9 @@ def main() -> int:
         return 1
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return 0
+    if args.gemm_reference:
+        gemm_reference(args.gemm_reference, args.steps)
         return 0
 
     import exact_attention_29_amd as fa
