@@ -121,12 +121,20 @@ __device__ __forceinline__ void leave_launch(int slot) {
 //   O^T (accumulator): block b, register r of lane (q, h) holds
 //     O[q][32b + 8*(r/4) + 4h + r%4].
 // Occupancy: two waves per SIMD (256 registers each), three at d = 64.
-template <class TT, int DK, int DV, bool CAUSAL, int NW, int NS, bool PERSIST>
+//
+// Key split (SPLIT, for grids smaller than the GPU; never persistent): item
+// (query block, split s) covers the s-th of n_split equal shares of the
+// block's key tiles and writes, per row, its output normalised by its own
+// rounded-weight sum (fp32, Opart[s]) and the two log2 weights of the share,
+// mc + log2(lw) and mc + log2(l) (Lpart[s]); attn_combine_sp merges them.
+// A share with no kept key of a row writes 0 and -inf.
+template <class TT, int DK, int DV, bool CAUSAL, int NW, int NS, bool PERSIST, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV == 128 ? 3 : 2, DK + DV == 128 ? 3 : 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Nq, int Nk, int H, const int* __restrict__ k_len, int n_qtiles, int total_items, int slot,
-    float scale) {
+    float scale, int n_split, float* __restrict__ Opart, float2* __restrict__ Lpart) {
+  static_assert(!(SPLIT && PERSIST), "a split launch has one workgroup per item");
   // DK: head dim of Q and K (the scores); DV: head dim of V and O
   constexpr int BR = 32 * NW, BC = 64;
   using LK = TileLayout<DK>;
@@ -158,8 +166,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   int work = __builtin_amdgcn_readfirstlane(s_item);
   while (work >= 0) {
     int next = -1;
-    const int bh = work / n_qtiles;
-    int qt = work % n_qtiles;
+    const int split = SPLIT ? work % n_split : 0;  // the shares of a block are neighbours
+    const int wq = SPLIT ? work / n_split : work;
+    const int bh = wq / n_qtiles;
+    int qt = wq % n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
     // keys kept for query i: j < nk and, when causal, j <= i + diag (the last
     // query row is aligned with the last valid key)
@@ -179,9 +189,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     }
 
     const int kv_end = CAUSAL ? min(nk, (qt + 1) * BR + diag) : nk;
-    const int T = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+    const int T_all = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+    // this workgroup's tiles: [tile0, tile0 + T) of the block's T_all (all of
+    // them unsplit); tile t below is key tile tile0 + t
+    const int tile0 = SPLIT ? (int)((long long)T_all * split / n_split) : 0;
+    const int T = SPLIT ? (int)((long long)T_all * (split + 1) / n_split) - tile0 : T_all;
     const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
-    const int my_T = CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
+    const int my_T_all = CAUSAL ? (last_key < 0 ? 0 : min(T_all, last_key / BC + 1)) : T_all;
+    const int my_T = SPLIT ? min(T, max(0, my_T_all - tile0)) : my_T_all;
 
     const uint16_t* const kbase = K + khead;
     const uint16_t* const vbase = V + vhead;
@@ -193,11 +208,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     auto load_stage = [&](int st) {
       const unsigned base = lds0 + ((st + 1) % NS) * SB;
       if (st + 1 < T) {
-        const int k0 = (st + 1) * BC;
+        const int k0 = (tile0 + st + 1) * BC;
         dma_tile<DK, false, NW>(buffer_desc(kbase + (size_t)k0 * DK, (unsigned)(nk - k0) * DK * 2), base, 0, wave, lane);
       }
       if (st >= 0) {
-        const int k0 = st * BC;
+        const int k0 = (tile0 + st) * BC;
         dma_tile<DV, true, NW>(buffer_desc(vbase + (size_t)k0 * DV, (unsigned)(nk - k0) * DV * 2), base + TBK, 0, wave, lane);
       }
     };
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     // l and lw are rescaled here.  `resc` tells whether any row moved.
     auto part1 = [&](f32x16 (&sv)[BC / 32], int t, bool masked, bool& resc) -> float {
       if (masked) {
-        const int k0 = t * BC;
+        const int k0 = (tile0 + t) * BC;
 #pragma unroll
         for (int b = 0; b < BC / 32; ++b)
 #pragma unroll
@@ -293,7 +308,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       l_run += ls[0] + ls[1];
       lw_run += lws[0] + lws[1];
     };
-    auto tile_masked = [&](int t) { return (CAUSAL && t * BC + BC - 1 > q_first + diag) || (t * BC + BC > nk); };
+    auto tile_masked = [&](int t) {
+      const int k0 = (tile0 + t) * BC;
+      return (CAUSAL && k0 + BC - 1 > q_first + diag) || (k0 + BC > nk);
+    };
 
     // One steady-state step (tile j's softmax and product, tile j+1's scores
     // and statistics), written in issue order and fenced so that every MFMA is
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       if (mask_next) {
         // keys past the row (causal) or past the valid keys score -inf: lane
         // (q, h) keeps key offsets 32b + 8(r/4) + r%4 <= lim within tile t_next
-        const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1) - (t_next * BC + 4 * hf);
+        const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1) - ((tile0 + t_next) * BC + 4 * hf);
 #pragma unroll
         for (int b = 0; b < BC / 32; ++b)
 #pragma unroll
@@ -522,7 +540,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     // barrier) and stores whole 128-byte row segments, 8 lanes per segment.
     const float l_tot = half_sum(l_run);
     const float lw_tot = half_sum(lw_run);
-    {
+    if constexpr (SPLIT) {
+      // this share's output and weights, fp32, straight from the registers
+      // (block b, register 4g+e of lane (q, h) is column 32b + 8g + 4h + e)
+      const float inv = lw_tot > 0.f ? __builtin_amdgcn_rcpf(lw_tot) : 0.f;
+      if (my_q < Nq) {
+        const size_t rows = (size_t)(total_items / (n_qtiles * n_split)) * Nq;
+        const size_t row = (size_t)split * rows + (size_t)bh * Nq + my_q;
+        float* orow = Opart + row * DV + 4 * hf;
+#pragma unroll
+        for (int b = 0; b < DV / 32; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(orow + 32 * b + 8 * g) = f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv,
+                                                     o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
+        if (hf == 0)
+          Lpart[row] = float2{lw_tot > 0.f ? mc_run + __builtin_amdgcn_logf(lw_tot) : -INFINITY,
+                              l_tot > 0.f ? mc_run + __builtin_amdgcn_logf(l_tot) : -INFINITY};
+      }
+    } else {
       // a row without kept keys has lw = 0 and O = 0 (rows past Nq: not stored)
       const float inv = lw_tot > 0.f ? __builtin_amdgcn_rcpf(lw_tot) : 0.f;
       uint8_t* stg = smem + wave * kOStageBytes;
@@ -553,6 +589,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     work = __builtin_amdgcn_readfirstlane(s_item);
   }
   if (PERSIST && tid == 0) leave_launch(slot);
+}
+
+// Merge of the 16-bit kernel's key shares, per row: with a_s = mc_s +
+// log2(lw_s) (the share's rounded-weight mass) and b_s = mc_s + log2(l_s),
+// O = sum_s 2^(a_s) O_s / sum_s 2^(a_s) -- the normalisation by the rounded
+// weights that the unsplit kernel applies -- and lse = ln sum_s 2^(b_s), the
+// rule by which partial softmax results over disjoint key sets combine
+// ("FlashAttention Engine", "Core FlashAttention Mechanics", item 3).  DV/8
+// threads per row, 8 columns each; shares are added in order.
+template <class TT, int DV>
+__global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__ Opart,
+                                                       const float2* __restrict__ Lpart,
+                                                       uint16_t* __restrict__ O,
+                                                       float* __restrict__ LSE, long long rows,
+                                                       int n_split) {
+  constexpr int TPR = DV / 8, RPB = 256 / TPR;  // threads per row, rows per block
+  const int t = threadIdx.x % TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= rows) return;
+  float amax = -INFINITY, bmax = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float2 w = Lpart[(size_t)sp * rows + row];
+    amax = fmaxf(amax, w.x);
+    bmax = fmaxf(bmax, w.y);
+  }
+  uint16_t* orow = O + (size_t)row * DV + 8 * t;
+  if (amax == -INFINITY) {  // no share kept a key of this row: the empty sum
+    *(u32x4*)orow = u32x4{0, 0, 0, 0};
+    if (t == 0) LSE[row] = -INFINITY;
+    return;
+  }
+  float wsum = 0.f, lsum = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float2 w = Lpart[(size_t)sp * rows + row];
+    const float e = fast_exp2(w.x - amax);  // 0 for a share without kept keys
+    wsum += e;
+    lsum += fast_exp2(w.y - bmax);
+    const f32x4* op = (const f32x4*)(Opart + ((size_t)sp * rows + row) * DV + 8 * t);
+    acc0 += e * op[0];
+    acc1 += e * op[1];
+  }
+  const float inv = 1.f / wsum;
+  *(u32x4*)orow = u32x4{TT::pack(acc0[0] * inv, acc0[1] * inv), TT::pack(acc0[2] * inv, acc0[3] * inv),
+                        TT::pack(acc1[0] * inv, acc1[1] * inv), TT::pack(acc1[2] * inv, acc1[3] * inv)};
+  if (t == 0) LSE[row] = (bmax + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -767,9 +849,48 @@ struct Shape {
   const int* k_len;
 };
 
+// Key-split plan for grids too small to fill the GPU.  fp32: about one
+// workgroup per CU, at least 4 key tiles (of 32) per split, `tps` tiles each.
+// 16-bit: about as many workgroups as the CUs hold at once (one at d = 128,
+// three at d = 64), at least 4 key tiles (of 64) per share, each query
+// block's tiles cut into n_split equal shares.  n_split = 1: none.
+struct SplitPlan {
+  int n_split = 1, tps = 0;
+  size_t bytes = 0;  // workspace: partial O (n_split*rows*dv floats), then the rows' weights
+};
+
+SplitPlan plan_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype) {
+  SplitPlan p;
+  int cus = 0;
+  if (compute_units(&cus) != hipSuccess) return p;
+  const size_t rows = (size_t)BH * Nq;
+  if (dtype == FA_DTYPE_FP32) {
+    const long long items = (long long)((Nq + 31) / 32) * BH, ntiles = (Nk + 31) / 32;
+    if (items >= cus) return p;
+    long long sp = std::min<long long>((cus + items - 1) / items, ntiles / 4);
+    if (sp < 2) return p;
+    p.tps = (int)((ntiles + sp - 1) / sp);
+    p.n_split = (int)((ntiles + p.tps - 1) / p.tps);
+    if (p.n_split < 2) return SplitPlan{};
+    p.bytes = (size_t)p.n_split * rows * (size_t)(dv + 1) * sizeof(float);
+    return p;
+  }
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return p;
+  const bool wide = dk == 128 || dv == 128;
+  const long long br = wide ? 256 : 128, slots = (long long)cus * (wide ? 1 : 3);
+  const long long items = (Nq + br - 1) / br * BH, ntiles = (Nk + 63) / 64;
+  if (items >= slots) return p;
+  const long long sp = std::min<long long>((slots + items - 1) / items, ntiles / 4);
+  if (sp < 2) return p;
+  p.n_split = (int)sp;
+  p.bytes = (size_t)p.n_split * rows * (size_t)(dv + 2) * sizeof(float);
+  return p;
+}
+
 template <class TT, int DK, int DV>
 hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse,
-                     const Shape& sh, float scale, bool causal, hipStream_t st) {
+                     const Shape& sh, float scale, bool causal, hipStream_t st,
+                     const SplitPlan& plan, void* ws) {
   // d = 128: 8 waves (256 query rows) per workgroup halve the K/V tile
   // loads per FLOP, and one persistent workgroup per CU claims work items
   // (no gap between items, no idle XCD at the end).  d = 64: 4 waves, three
@@ -781,6 +902,29 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   constexpr bool PERSIST = WIDE;
   static std::atomic<unsigned> launches{0};
   const int nq = (sh.Nq + 32 * NW - 1) / (32 * NW);
+  if (plan.n_split > 1) {
+    const int total = nq * sh.BH * plan.n_split;
+    const long long rows = (long long)sh.BH * sh.Nq;
+    float* opart = (float*)ws;
+    float2* lpart = (float2*)(opart + (size_t)plan.n_split * rows * DV);
+    const dim3 grid(total), block(64 * NW);
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, false, true>), grid, block, 0, st,
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o,
+                         lse, sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, 0, scale, plan.n_split,
+                         opart, lpart);
+    else
+      hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, false, true>), grid, block, 0, st,
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o,
+                         lse, sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, 0, scale, plan.n_split,
+                         opart, lpart);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    constexpr int RPB = 256 / (DV / 8);
+    hipLaunchKernelGGL((attn_combine_sp<TT, DV>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                       0, st, (const float*)opart, (const float2*)lpart, (uint16_t*)o, lse, rows,
+                       plan.n_split);
+    return hipGetLastError();
+  }
   const int total = nq * sh.BH;
   int grid_wg = total, slot = 0;
   if (PERSIST) {
@@ -791,39 +935,14 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   }
   const dim3 grid(grid_wg), block(64 * NW);
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, PERSIST>), grid, block, 0, st,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, PERSIST, false>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale);
+                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale, 1, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, PERSIST>), grid, block, 0, st,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, PERSIST, false>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale);
+                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale, 1, nullptr, nullptr);
   return hipGetLastError();
-}
-
-// Key-split plan of the fp32 path for grids too small to fill the GPU: about
-// one workgroup per CU, at least 4 key tiles per split.  n_split = 1: none.
-struct SplitPlan {
-  int n_split = 1, tps = 0;
-  size_t bytes = 0;  // workspace: n_split*rows*dv floats of partial O, then n_split*rows of lse
-};
-
-// d: the value head dim (the width of O)
-SplitPlan plan_split(long long BH, int Nq, int Nk, int d, int dtype) {
-  SplitPlan p;
-  if (dtype != FA_DTYPE_FP32) return p;
-  int cus = 0;
-  if (compute_units(&cus) != hipSuccess) return p;
-  const long long items = (long long)((Nq + 31) / 32) * BH, ntiles = (Nk + 31) / 32;
-  if (items >= cus) return p;
-  long long sp = std::min<long long>((cus + items - 1) / items, ntiles / 4);
-  if (sp < 2) return p;
-  p.tps = (int)((ntiles + sp - 1) / sp);
-  p.n_split = (int)((ntiles + p.tps - 1) / p.tps);
-  if (p.n_split < 2) return SplitPlan{};
-  const size_t rows = (size_t)BH * Nq;
-  p.bytes = (size_t)p.n_split * rows * (size_t)(d + 1) * sizeof(float);
-  return p;
 }
 
 template <int DSL, int DSLV, int DS>
@@ -917,11 +1036,12 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
 
 template <class TT>
 hipError_t launch_sp_dims(const void* q, const void* k, const void* v, void* o, float* lse,
-                          const Shape& sh, int dk, int dv, float scale, bool c, hipStream_t st) {
-  if (dk == 64) return dv == 64 ? launch_sp<TT, 64, 64>(q, k, v, o, lse, sh, scale, c, st)
-                                : launch_sp<TT, 64, 128>(q, k, v, o, lse, sh, scale, c, st);
-  return dv == 64 ? launch_sp<TT, 128, 64>(q, k, v, o, lse, sh, scale, c, st)
-                  : launch_sp<TT, 128, 128>(q, k, v, o, lse, sh, scale, c, st);
+                          const Shape& sh, int dk, int dv, float scale, bool c, hipStream_t st,
+                          const SplitPlan& plan, void* ws) {
+  if (dk == 64) return dv == 64 ? launch_sp<TT, 64, 64>(q, k, v, o, lse, sh, scale, c, st, plan, ws)
+                                : launch_sp<TT, 64, 128>(q, k, v, o, lse, sh, scale, c, st, plan, ws);
+  return dv == 64 ? launch_sp<TT, 128, 64>(q, k, v, o, lse, sh, scale, c, st, plan, ws)
+                  : launch_sp<TT, 128, 128>(q, k, v, o, lse, sh, scale, c, st, plan, ws);
 }
 
 // dk, dv: head dims of Q/K and of V/O (a supported pair)
@@ -932,9 +1052,9 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, c
   const bool c = causal != 0;
   hipError_t e = hipSuccess;
   if (dtype == FA_DTYPE_BF16) {
-    e = launch_sp_dims<Bf16>(q, k, v, o, lse, sh, dk, dv, scale, c, st);
+    e = launch_sp_dims<Bf16>(q, k, v, o, lse, sh, dk, dv, scale, c, st, plan, ws);
   } else if (dtype == FA_DTYPE_FP16) {
-    e = launch_sp_dims<F16>(q, k, v, o, lse, sh, dk, dv, scale, c, st);
+    e = launch_sp_dims<F16>(q, k, v, o, lse, sh, dk, dv, scale, c, st, plan, ws);
   } else if (dk != dv) {
     e = dk == 64 ? launch32<64, 128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws)
                  : launch32<128, 64, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws);
@@ -960,7 +1080,7 @@ size_t fa_fwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v
   if (!fa_fwd_gen_supported(d_qk, d_v, dtype, causal)) return 0;
   const long long BH = (long long)B * H;
   if (BH > (1LL << 24) || BH * Nq > 0x7fffffffLL || BH * Nk > 0x7fffffffLL) return 0;
-  return plan_split(BH, Nq, Nk, d_v, dtype).bytes;
+  return plan_split(BH, Nq, Nk, d_qk, d_v, dtype).bytes;
 }
 
 size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal, int dtype) {
@@ -978,7 +1098,7 @@ int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse,
   if (workspace == nullptr || workspace_bytes == 0)
     return dispatch(q, k, v, o, lse, sh, d_qk, d_v, scale, causal, dtype, SplitPlan{}, nullptr,
                     stream);
-  const SplitPlan plan = plan_split((long long)B * H, Nq, Nk, d_v, dtype);
+  const SplitPlan plan = plan_split((long long)B * H, Nq, Nk, d_qk, d_v, dtype);
   if (workspace_bytes < plan.bytes) return FA_ERR_INVALID_ARG;
   if (!aligned16(workspace)) return FA_ERR_UNSUPPORTED;
   return dispatch(q, k, v, o, lse, sh, d_qk, d_v, scale, causal, dtype, plan, workspace, stream);

@@ -84,9 +84,11 @@ def test_key_split_matches_oracle_and_unsplit_path(d, causal):
 
 
 def test_workspace_size_and_rejection():
-    """No workspace for 16-bit inputs or grids that fill the GPU; a workspace
-    smaller than the reported size is rejected before anything is written."""
-    assert fa.fa_fwd_workspace_size(1, 1, 4096, 128, 0, fa.FA_DTYPE_BF16) == 0
+    """No workspace for grids that fill the GPU; a workspace smaller than the
+    reported size is rejected before anything is written."""
+    assert fa.fa_fwd_workspace_size(2, 32, 8192, 128, 1, fa.FA_DTYPE_BF16) == 0
+    assert fa.fa_fwd_workspace_size(4, 32, 2048, 64, 0, fa.FA_DTYPE_BF16) == 0
+    assert fa.fa_fwd_workspace_size(1, 1, 4096, 128, 0, fa.FA_DTYPE_BF16) > 0
     assert fa.fa_fwd_workspace_size(4, 64, 1024, 64, 0, fa.FA_DTYPE_FP32) == 0
     need = fa.fa_fwd_workspace_size(1, 1, 1024, 1024, 0, fa.FA_DTYPE_FP32)
     assert need > 0
