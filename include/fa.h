@@ -98,8 +98,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * fa_fwd_workspace_size -- device workspace, in bytes, that fa_fwd_ws can use
  * for this problem on the current device; 0 when it would run exactly as
- * fa_fwd does.  Nonzero only for fp32 problems whose (query block, head,
- * batch) items are fewer than the device's compute units: fa_fwd_ws then
+ * fa_fwd does.  Nonzero only for problems whose (query block, head, batch)
+ * items are fewer than the device holds at once (fp32: 32-row blocks against
+ * the compute units; 16-bit: 256-row blocks at d = 128, one per compute
+ * unit, 128-row blocks at d = 64, three per compute unit): fa_fwd_ws then
  * splits each query block's keys into ranges, computes the softmax-weighted
  * output and log-sum-exp of every range in its own workgroup, and merges the
  * ranges with lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s ("The
@@ -121,8 +123,9 @@ size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
  *                     it must be >= fa_fwd_workspace_size(...) for the same
  *                     problem on the same device, else FA_ERR_INVALID_ARG
  *                     (a misaligned workspace gives FA_ERR_UNSUPPORTED).
- * The key-split result equals fa_fwd's up to fp32 rounding (the merge adds
- * one rounding per range); it is bitwise reproducible run to run.
+ * The key-split result equals fa_fwd's up to rounding (fp32: the merge adds
+ * one rounding per range; 16-bit: each range normalises by its own rounded
+ * weights before the merge); it is bitwise reproducible run to run.
  */
 int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype,
