@@ -157,9 +157,14 @@ __device__ __forceinline__ u32x4 buffer_desc(const void* base, unsigned bytes) {
 // bytes land at LDS byte address lds_addr + 16 L.  Written as inline asm so
 // that the compiler does not wait for it at every LDS read and barrier: the
 // caller waits (vmcnt) before the barrier that precedes the first read of
-// the data.
+// the data.  The statement sets M0, the LDS base the load reads, and keeps
+// one wait state between that SALU write of M0 and the load that reads it
+// (the ISA asks for it before an LDS-writing memory instruction).  M0 is
+// named as clobbered so that the compiler's hazard checks see the write, and
+// keep a wait state before whatever follows (the compiler reserves M0 and
+// warns about the clobber; nothing else in these kernels touches M0).
 __device__ __forceinline__ void dma16(u32x4 desc, unsigned lds_addr, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_addr), "v"(voffset), "s"(desc)
                : "memory", "m0");
