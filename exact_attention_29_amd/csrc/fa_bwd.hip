@@ -129,6 +129,24 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mu
   }
 }
 
+// Store a wave's 32 x D transposed accumulator (block b, register 4g+e of
+// lane (x, h) = element [row x][32b + 8g + 4h + e]) times `mul`, in fp32, to
+// rows row0 .. row0+31 of `out` (rows >= n_valid are skipped): the partial
+// sums of a split, one 16-byte store per register group.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(const f32x16 (&acc)[D / 32], float mul, float* out,
+                                               int row0, int n_valid, int lane) {
+  const int x = lane & 31, h = lane >> 5;
+  if (row0 + x >= n_valid) return;
+  float* row = out + (size_t)(row0 + x) * D + 4 * h;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(row + 32 * b + 8 * g) = f32x4{acc[b][4 * g] * mul, acc[b][4 * g + 1] * mul,
+                                               acc[b][4 * g + 2] * mul, acc[b][4 * g + 3] * mul};
+}
+
 // ---------------------------------------------------------------------------
 // Row statistics.  TPR = D/8 threads per row, 8 elements each.
 template <class TT, int D>
@@ -186,7 +204,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int H,
-    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale) {
+    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale, int n_split,
+    float* __restrict__ part, long long kstride, long long vstride) {
   constexpr int BQ = 32, CGK = DK / 32, CGV = DV / 32;
   // 1 KB blocks and bytes of one 32-row Q tile and one dO tile
   constexpr int TBLKQ = 2 * CGK, TBQ = TBLKQ * 1024, TBLKD = 2 * CGV, TBD = TBLKD * 1024;
@@ -199,8 +218,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = lane & 31, h = lane >> 5;
   const int item = xcd_remap(blockIdx.x, total);
-  const int bh = item / n_kblocks;
-  const int kb = item % n_kblocks;  // ascending: causal key blocks near 0 see the most queries
+  // split (small grids): this workgroup takes one of n_split shares of the
+  // block's query tiles and writes fp32 partial sums to `part`
+  const int split = item % n_split, work = item / n_split;
+  const int bh = work / n_kblocks;
+  const int kb = work % n_kblocks;  // ascending: causal key blocks near 0 see the most queries
   // as in the forward: key j is kept for query i iff j < nk and, when causal,
   // j <= i + diag
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
@@ -280,12 +302,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   };
   const TrLane trl = tr_lane(lane);
 
-  if (qt0 < nqt) load(qt0, 0);
+  const int qs = qt0 + (int)((long long)(nqt - qt0) * split / n_split);
+  const int qe = qt0 + (int)((long long)(nqt - qt0) * (split + 1) / n_split);
+  if (qs < qe) load(qs, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  for (int t = qt0; t < nqt; ++t) {
-    const int buf = (t - qt0) & 1;
-    if (t + 1 < nqt) load(t + 1, buf ^ 1);
+  for (int t = qs; t < qe; ++t) {
+    const int buf = (t - qs) & 1;
+    if (t + 1 < qe) load(t + 1, buf ^ 1);
     const int q0 = t * BQ;
     // nothing kept when this wave's keys are all padding, or all above the
     // last query row of the tile
@@ -364,6 +388,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   }
   // the tile buffers are free after the last barrier
   // every key row is written, those past the valid keys as zeros
+  if (part) {  // split: the dK parts, then the dV parts
+    store_rows_f32<DK>(dk, scale, part + (size_t)split * kstride + khead, kw, Nk, lane);
+    store_rows_f32<DV>(dv, 1.f, part + (size_t)n_split * kstride + (size_t)split * vstride + vhead, kw,
+                       Nk, lane);
+    return;
+  }
   uint8_t* stg = smem + wave * 32 * 144;
   store_rows<TT, DV>(dv, 1.f, stg, dV + vhead, kw, Nk, lane);
   store_rows<TT, DK>(dk, scale, stg, dK + khead, kw, Nk, lane);
@@ -384,7 +414,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     uint16_t* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
-    int n_qblocks, int total, float scale) {
+    int n_qblocks, int total, float scale, int n_split, float* __restrict__ part,
+    long long qstride) {
   // DK: head dim of Q, K and dQ; DV: of V and dO
   constexpr int BR = 32 * NW, BC = 64, CGK = DK / 32, CGV = DV / 32;
   using LK = TileLayout<DK>;
@@ -398,8 +429,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = lane & 31, h = lane >> 5;
   const int item = xcd_remap(blockIdx.x, total);
-  const int bh = item / n_qblocks;
-  int qb = item % n_qblocks;
+  // split (small grids): one of n_split shares of the block's key tiles,
+  // fp32 partial sums to `part`
+  const int split = item % n_split, work = item / n_split;
+  const int bh = work / n_qblocks;
+  int qb = work % n_qblocks;
   if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the dK/dV kernel
   const int diag = nk - Nq;
@@ -452,12 +486,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   // A operand of V (chunk-major block layout), as in the forward kernel
   const int v_lane = (x >> 4) * CGV * 1024 + (h * 16 + (x & 15)) * 16;
 
-  if (T > 0) load(0, 0);
+  const int js = (int)((long long)T * split / n_split), je = (int)((long long)T * (split + 1) / n_split);
+  if (js < je) load(js, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  for (int j = 0; j < T; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < T) load(j + 1, buf ^ 1);
+  for (int j = js; j < je; ++j) {
+    const int buf = (j - js) & 1;
+    if (j + 1 < je) load(j + 1, buf ^ 1);
     if (j < my_T) {
       const uint8_t* kt = smem + buf * SB;
       const uint8_t* vt = kt + TBK;
@@ -507,6 +542,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+  }
+  if (part) {
+    store_rows_f32<DK>(dq, scale, part + (size_t)split * qstride + head, q_first, Nq, lane);
+    return;
   }
   uint8_t* stg = smem + wave * 32 * 144;
   store_rows<TT, DK>(dq, scale, stg, dQ + head, q_first, Nq, lane);
@@ -902,10 +941,82 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
 // host side
 size_t padded_rows(long long BH, int N) { return (size_t)BH * (size_t)((N + kRowPad - 1) / kRowPad * kRowPad); }
 
+// out = sum of n_split partial tensors of n floats each (stride apart), added
+// in split order so the result does not depend on timing.
+__global__ __launch_bounds__(256) void attn_bwd_sum_f32(const float* __restrict__ part,
+                                                        float* __restrict__ out, long long n,
+                                                        long long stride, int n_split) {
+  const long long n4 = n / 4;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * 256) {
+    f32x4 acc = ((const f32x4*)part)[i];
+    for (int sp = 1; sp < n_split; ++sp) acc += ((const f32x4*)(part + sp * stride))[i];
+    ((f32x4*)out)[i] = acc;
+  }
+}
+
+// The same for 16-bit outputs: the fp32 partial sums added in split order,
+// then rounded once to the element type (8 elements per thread).
+template <class TT>
+__global__ __launch_bounds__(256) void attn_bwd_sum_sp(const float* __restrict__ part,
+                                                       uint16_t* __restrict__ out, long long n,
+                                                       long long stride, int n_split) {
+  const long long n8 = n / 8;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8;
+       i += (long long)gridDim.x * 256) {
+    f32x4 a = ((const f32x4*)part)[2 * i], b = ((const f32x4*)part)[2 * i + 1];
+    for (int sp = 1; sp < n_split; ++sp) {
+      a += ((const f32x4*)(part + sp * stride))[2 * i];
+      b += ((const f32x4*)(part + sp * stride))[2 * i + 1];
+    }
+    ((u32x4*)out)[i] = u32x4{TT::pack(a[0], a[1]), TT::pack(a[2], a[3]), TT::pack(b[0], b[1]),
+                             TT::pack(b[2], b[3])};
+  }
+}
+
+// Problems with fewer key (query) blocks than the GPU holds at once split
+// each block's query (key) tiles over `kv` (`q`) workgroups; their partial dK
+// and dV (dQ) go to the workspace after the row statistics, in fp32, and are
+// summed by attn_bwd_sum_f32 / attn_bwd_sum_sp.  Each split keeps at least
+// two tiles.
+struct BwdSplit {
+  int kv = 1, q = 1;
+  size_t bytes = 0;  // partial sums
+};
+
+// dk, dv: head dims of Q/K and of V/dO
+BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype) {
+  BwdSplit p;
+  int cus = 0;
+  if (compute_units(&cus) != hipSuccess) return p;
+  auto pick = [&](long long blocks, long long tiles, long long slots) {
+    if (blocks >= slots) return 1;
+    const long long sp = std::min<long long>((slots + blocks - 1) / blocks, tiles / 2);
+    return sp < 2 ? 1 : (int)sp;
+  };
+  if (dtype == FA_DTYPE_FP32) {  // 32-row blocks of keys and of queries, one workgroup per CU
+    const long long nkb = (Nk + 31) / 32, nqb = (Nq + 31) / 32;
+    p.kv = pick(nkb * BH, nqb, cus);
+    p.q = pick(nqb * BH, nkb, cus);
+  } else if (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16) {
+    // 128-row blocks; a CU holds two workgroups (three at d = 64); the dK/dV
+    // kernel streams 32-row query tiles, the dQ kernel 64-key tiles
+    const long long slots = (long long)cus * (dk + dv == 128 ? 3 : 2);
+    p.kv = pick((Nk + 127) / 128 * BH, (Nq + 31) / 32, slots);
+    p.q = pick((Nq + 127) / 128 * BH, (Nk + 63) / 64, slots);
+  } else {
+    return p;
+  }
+  if (p.kv > 1) p.bytes += (size_t)p.kv * BH * Nk * (size_t)(dk + dv) * sizeof(float);
+  if (p.q > 1) p.bytes += (size_t)p.q * BH * Nq * (size_t)dk * sizeof(float);
+  return p;
+}
+
 template <class TT, int DK, int DV>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, int BH, int H, int Nq, int Nk,
-                      const int* k_len, float scale, bool causal, float* ws, hipStream_t st) {
+                      const int* k_len, float scale, bool causal, float* ws, const BwdSplit& sp,
+                      hipStream_t st) {
   const int n_pad = (Nq + kRowPad - 1) / kRowPad * kRowPad;
   const long long prow = (long long)BH * n_pad;
   float* nl = ws;
@@ -921,68 +1032,47 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   // on every workload shape, though they halve the re-streamed tiles
   constexpr int NWK = 4, NWQ = 4;
   const int nkb = (Nk + 32 * NWK - 1) / (32 * NWK), nqb = (Nq + 32 * NWQ - 1) / (32 * NWQ);
-  const int tk = nkb * BH, tq = nqb * BH;
+  const int tk = nkb * BH * sp.kv, tq = nqb * BH * sp.q;
+  const long long kstride = (long long)BH * Nk * DK, vstride = (long long)BH * Nk * DV;
+  const long long qstride = (long long)BH * Nq * DK;
+  float* kvpart = sp.kv > 1 ? ws + 2 * prow : nullptr;
+  float* qpart = sp.q > 1 ? ws + 2 * prow + (sp.kv > 1 ? sp.kv * (kstride + vstride) : 0) : nullptr;
   const dim3 bk(64 * NWK), bq(64 * NWQ);
   if (causal) {
     hipLaunchKernelGGL((attn_bwd_dkdv<TT, DK, DV, true, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
+                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale,
+                       sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq<TT, DK, DV, true, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
+                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart,
+                       qstride);
   } else {
     hipLaunchKernelGGL((attn_bwd_dkdv<TT, DK, DV, false, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale);
+                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale,
+                       sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq<TT, DK, DV, false, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale);
+                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart,
+                       qstride);
   }
-  return hipGetLastError();
-}
-
-// out = sum of n_split partial tensors of n floats each (stride apart), added
-// in split order so the result does not depend on timing.
-__global__ __launch_bounds__(256) void attn_bwd_sum_f32(const float* __restrict__ part,
-                                                        float* __restrict__ out, long long n,
-                                                        long long stride, int n_split) {
-  const long long n4 = n / 4;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4;
-       i += (long long)gridDim.x * 256) {
-    f32x4 acc = ((const f32x4*)part)[i];
-    for (int sp = 1; sp < n_split; ++sp) acc += ((const f32x4*)(part + sp * stride))[i];
-    ((f32x4*)out)[i] = acc;
-  }
-}
-
-// fp32 problems with fewer key (query) blocks than compute units split each
-// block's query (key) tiles over `kv` (`q`) workgroups; their partial dK and
-// dV (dQ) go to the workspace after the row statistics and are summed by
-// attn_bwd_sum_f32.  Each split keeps at least two tiles.
-struct BwdSplit {
-  int kv = 1, q = 1;
-  size_t bytes = 0;  // partial sums
-};
-
-// dk, dv: head dims of Q/K and of V/dO
-BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype) {
-  BwdSplit p;
-  if (dtype != FA_DTYPE_FP32) return p;
-  int cus = 0;
-  if (compute_units(&cus) != hipSuccess) return p;
-  const long long nkb = (Nk + 31) / 32, nqb = (Nq + 31) / 32;
-  auto pick = [&](long long blocks, long long tiles) {
-    if (blocks >= cus) return 1;
-    const long long sp = std::min<long long>((cus + blocks - 1) / blocks, tiles / 2);
-    return sp < 2 ? 1 : (int)sp;
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  auto sum = [&](const float* part, void* out, long long n, int n_split) {
+    const long long blocks = std::min<long long>((n / 8 + 255) / 256, 8192);
+    hipLaunchKernelGGL((attn_bwd_sum_sp<TT>), dim3((unsigned)blocks), dim3(256), 0, st, part,
+                       (uint16_t*)out, n, n, n_split);
+    return hipGetLastError();
   };
-  p.kv = pick(nkb * BH, nqb);
-  p.q = pick(nqb * BH, nkb);
-  if (p.kv > 1) p.bytes += (size_t)p.kv * BH * Nk * (size_t)(dk + dv) * sizeof(float);
-  if (p.q > 1) p.bytes += (size_t)p.q * BH * Nq * (size_t)dk * sizeof(float);
-  return p;
+  if (sp.kv > 1) {
+    if (hipError_t e = sum(kvpart, dk, kstride, sp.kv); e != hipSuccess) return e;
+    if (hipError_t e = sum(kvpart + sp.kv * kstride, dv, vstride, sp.kv); e != hipSuccess) return e;
+  }
+  if (sp.q > 1)
+    if (hipError_t e = sum(qpart, dq, qstride, sp.q); e != hipSuccess) return e;
+  return hipSuccess;
 }
 
 template <int DSL, int DSLV, int DS>
@@ -1052,12 +1142,13 @@ template <class TT>
 hipError_t launch_bwd_dims(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            int bh, int H, int Nq, int Nk, const int* k_len, float scale,
-                           bool causal, int d_qk, int d_v, float* ws, hipStream_t st) {
+                           bool causal, int d_qk, int d_v, float* ws, const BwdSplit& sp,
+                           hipStream_t st) {
   if (d_qk == 64)
-    return d_v == 64 ? launch_bwd<TT, 64, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
-                     : launch_bwd<TT, 64, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
-  return d_v == 64 ? launch_bwd<TT, 128, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st)
-                   : launch_bwd<TT, 128, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, st);
+    return d_v == 64 ? launch_bwd<TT, 64, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st)
+                     : launch_bwd<TT, 64, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st);
+  return d_v == 64 ? launch_bwd<TT, 128, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st)
+                   : launch_bwd<TT, 128, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st);
 }
 
 }  // namespace
@@ -1128,9 +1219,9 @@ int fa_bwd_gen(const void* q, const void* k, const void* v, const void* o, const
   const BwdSplit sp = plan_bwd_split(BH, Nq, Nk, d_qk, d_v, dtype);
   hipError_t e;
   if (dtype == FA_DTYPE_BF16) {
-    e = launch_bwd_dims<Bf16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, st);
+    e = launch_bwd_dims<Bf16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, sp, st);
   } else if (dtype == FA_DTYPE_FP16) {
-    e = launch_bwd_dims<F16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, st);
+    e = launch_bwd_dims<F16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, sp, st);
   } else if (d_qk != d_v) {
     e = d_qk == 64 ? launch_bwd_f32<64, 128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st)
                    : launch_bwd_f32<128, 64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st);
