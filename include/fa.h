@@ -187,10 +187,12 @@ int fa_fwd_gen_supported(int d_qk, int d_v, int dtype, int causal);
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for this
  * problem: two fp32 row statistics per (batch, head, row), rows padded to a
- * multiple of 32; for fp32 problems with fewer query or key blocks (32 rows)
- * than the current device has compute units, also the fp32 partial sums of
- * the split that spreads each block's work over several workgroups.  Depends
- * on the current device.  0 for invalid or unsupported arguments.
+ * multiple of 32; for problems with fewer query or key blocks than the
+ * current device holds at once (fp32: 32-row blocks against its compute
+ * units; 16-bit: 128-row blocks against two workgroups per compute unit,
+ * three at d = 64), also the fp32 partial sums of the split that spreads
+ * each block's work over several workgroups.  Depends on the current device.
+ * 0 for invalid or unsupported arguments.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
 
