@@ -196,7 +196,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     const int T = SPLIT ? (int)((long long)T_all * (split + 1) / n_split) - tile0 : T_all;
     const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
     const int my_T_all = CAUSAL ? (last_key < 0 ? 0 : min(T_all, last_key / BC + 1)) : T_all;
-    const int my_T = SPLIT ? min(T, max(0, my_T_all - tile0)) : my_T_all;
+    // A wave whose rows all lie past Nq (the ragged last block; a single
+    // decoding query leaves seven of eight waves so) only helps load the tiles
+    // and meets the barriers.  Not at d = 64, whose three-wave occupancy
+    // leaves no registers for the extra control flow.
+    const bool idle = DK + DV > 128 && q_first >= Nq;
+    const int my_T = idle ? 0 : SPLIT ? min(T, max(0, my_T_all - tile0)) : my_T_all;
 
     const uint16_t* const kbase = K + khead;
     const uint16_t* const vbase = V + vhead;
@@ -478,10 +483,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       wait_keep(keep);
     }
     __syncthreads();
-    // Every wave scores tile 0 when the block has one, even a wave whose rows
-    // keep no key (causal, more queries than keys): its scores are then all
-    // masked, so the steady steps below see -inf instead of stale registers.
-    if (0 < T) {
+    // Every wave with rows below Nq scores tile 0 when the block has one, even
+    // a wave whose rows keep no key (causal, more queries than keys): its
+    // scores are then all masked, so the steady steps below see -inf instead
+    // of stale registers.  An idle wave runs no steady step at all.
+    if (0 < T && !idle) {
       bool resc;
       qk(smem + stage_buf(-1) * SB, sA);
       part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
@@ -497,13 +503,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       issue_for(j);
       {
         const uint8_t* kt = smem + stage_buf(j) * SB;
-        steady(sA, sB, kt, kt + TBK, j + 1, tile_masked(j + 1));
+        if (!idle) steady(sA, sB, kt, kt + TBK, j + 1, tile_masked(j + 1));
       }
       end_iter(j);
       issue_for(j + 1);
       {
         const uint8_t* kt = smem + stage_buf(j + 1) * SB;
-        steady(sB, sA, kt, kt + TBK, j + 2, tile_masked(j + 2));
+        if (!idle) steady(sB, sA, kt, kt + TBK, j + 2, tile_masked(j + 2));
       }
       end_iter(j + 1);
     }
