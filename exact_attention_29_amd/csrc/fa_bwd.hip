@@ -472,7 +472,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   const int kv_end = CAUSAL ? min(nk, (qb + 1) * BR + diag) : nk;
   const int T = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
   const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
-  const int my_T = CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
+  // a wave whose rows all lie past Nq only helps load the tiles
+  const int my_T = q_first >= Nq ? 0 : CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto load = [&](int j, int buf) {
     const int k0 = j * BC;

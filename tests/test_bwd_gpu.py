@@ -253,3 +253,20 @@ def test_narrow_qk_gradients_equal_the_zero_padded_equal_dim_call(dt, causal):
     assert torch.equal(a[0], b[0][..., :64]) and torch.all(b[0][..., 64:] == 0)
     assert torch.equal(a[1], b[1][..., :64]) and torch.all(b[1][..., 64:] == 0)
     assert torch.equal(a[2], b[2])
+
+
+def test_small_grids_take_the_split_and_match_the_oracle():
+    """Few heads and long rows: fewer key (query) blocks than the GPU holds,
+    so each block's tiles are shared out and the fp32 partial sums added; the
+    workspace then holds more than the two row statistics."""
+    B, H, N, d = 1, 2, 1500, 128
+    stats = 2 * B * H * ((N + 31) // 32 * 32) * 4
+    assert fa.fa_bwd_workspace_size(B, H, N, d, 1, fa.FA_DTYPE_BF16) > stats
+    q, k, v = make_qkv(B, H, N, d, "bf16", 4321)
+    g = make_dout(B, H, N, d, "bf16", 4322)
+    dq, dk, dv = run(q, k, v, g, True, d ** -0.5)
+    rows = parity.sample_rows(B, H, N, seed=5, per_head_random=40, tile=128)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, g, d ** -0.5, True, rows, rows)
+    flat = lambda t: t.detach().to("cpu").double().reshape(-1, d).numpy()[rows]
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        check(errors(torch.from_numpy(flat(got)), ref), torch.bfloat16, name)
