@@ -12,7 +12,8 @@
 // backward pass"); delta_i = sum_j P_ij dP_ij reduces to <dO_i, O_i> because
 // O_i = sum_j P_ij v_j.
 //
-// Three kernels, no atomics, so the result is bitwise reproducible:
+// Three kernels per call (plus a summing kernel when split), no atomics, so
+// the result is bitwise reproducible:
 //  * attn_bwd_prep: per row, nl = -lse/scale and nd = -delta (fp32) into the
 //    caller's workspace (rows padded to a multiple of 32 with zeros).  These
 //    are the initial accumulators of the score and dP products below, so
@@ -31,7 +32,10 @@
 //    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read by the
 //    transpose instruction.
 // All products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulators;
-// P and dS are rounded to the input type before their products.
+// P and dS are rounded to the input type before their products.  fp32 inputs
+// take their own kernels (attn_bwd_*_f32, on v_mfma_f32_32x32x2_f32), and
+// grids too small to fill the GPU share each block's tiles over several
+// workgroups whose fp32 partial sums attn_bwd_sum_* adds in a fixed order.
 #include <hip/hip_runtime.h>
 
 #include <math.h>

@@ -10,9 +10,10 @@
 // and streams every key/value tile through it (the query-block worker of "An
 // Example", step 7).  The N x N score matrix never leaves registers.
 //
-// Two kernels:
-//  * attn_fwd_sp<T>: bf16 / fp16 inputs, head dim 64 or 128.  4 (d = 64) or
-//    8 (d = 128) waves x 32 query rows per workgroup; K and V tiles of 64
+// Kernels:
+//  * attn_fwd_sp<T>: bf16 / fp16 inputs, head dims 64 or 128 (Q/K and V/O
+//    each).  4 (d = 64) or 8 (d = 128) waves x 32 query rows per workgroup,
+//    persistent at d = 128; K and V tiles of 64
 //    keys double-buffered in LDS and filled by buffer loads that write
 //    straight to LDS; both products on v_mfma_f32_32x32x16_{bf16,f16} with
 //    fp32 accumulators.  The score tile is computed transposed (S^T = K Q^T)
@@ -27,6 +28,9 @@
 //    Head dims above 128 are split across the waves of a workgroup (128
 //    columns each); the partial scores are summed through LDS in a fixed wave
 //    order, so every wave sees bitwise the same scores and the same softmax.
+//  * attn_combine_sp / attn_combine_f32: grids too small to fill the GPU
+//    split each query block's keys over several workgroups; these merge the
+//    partial results of the key ranges in a fixed order.
 //
 // Exponentials are exp2 of scores pre-multiplied by scale*log2(e) (v_exp_f32);
 // the log-sum-exp is converted back to natural-log units at the end.
