@@ -72,14 +72,14 @@ def lib():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
             ctypes.c_longlong, ctypes.c_longlong, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
-            ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.oracle_attn_bwd_gen.restype = ctypes.c_int
         L.oracle_attn_bwd_gen.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
             ctypes.c_longlong, ctypes.c_longlong, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
-            ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.oracle_thread_count.restype = ctypes.c_int
         L.oracle_thread_count.argtypes = [ctypes.c_int]
@@ -136,15 +136,29 @@ def attention(q, k, v, scale: float, causal: bool, threads: int = 0):
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
 
 
-def attn_rows_ex(q, k, v, scale: float, causal: bool, rows=None, k_len=None, threads: int = 0):
+def _counts(x, B, name):
+    """Per-batch counts as a contiguous int64 array of B entries (or None)."""
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        x = x.cpu().numpy()
+    c = np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+    if c.shape != (B,):
+        raise ValueError(f"{name} must hold one count per batch")
+    return c
+
+
+def attn_rows_ex(q, k, v, scale: float, causal: bool, rows=None, k_len=None, threads: int = 0,
+                 q_len=None):
     """Oracle attention for query and key sequences of different lengths,
     with optional per-batch valid key counts and a value head dim of its own
     (oracle.h, oracle_attn_rows_gen).
 
     q: host [B, H, Nq, dk]; k: [B, H, Nk, dk]; v: [B, H, Nk, dv], one dtype.
-    rows: flat query-row ids (b*H + h)*Nq + i (None: all).  k_len: B valid
-    key counts or None.  Returns (o [n_rows, dv], lse [n_rows]) float64 numpy
-    arrays; rows with no kept key give o = 0, lse = -inf.
+    rows: flat query-row ids (b*H + h)*Nq + i (None: all).  k_len / q_len: B
+    valid key / query counts or None (a query row at or past its batch's count
+    is padding and keeps no key).  Returns (o [n_rows, dv], lse [n_rows])
+    float64 numpy arrays; rows with no kept key give o = 0, lse = -inf.
     """
     q, k, v = _as_cpu(q), _as_cpu(k), _as_cpu(v)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape[:3] != v.shape[:3] \
@@ -157,27 +171,24 @@ def attn_rows_ex(q, k, v, scale: float, causal: bool, rows=None, k_len=None, thr
     if rows is None:
         rows = np.arange(B * H * Nq, dtype=np.int64)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
-    kl = None
-    if k_len is not None:
-        kl = np.ascontiguousarray(np.asarray(k_len, dtype=np.int64))
-        if kl.shape != (B,):
-            raise ValueError("k_len must hold one count per batch")
+    kl, ql = _counts(k_len, B, "k_len"), _counts(q_len, B, "q_len")
     n = rows.shape[0]
     o = np.empty((n, d), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
     rc = lib().oracle_attn_rows_gen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), _CODES[q.dtype], B, H, Nq, Nk, dk, d,
         float(scale), int(bool(causal)), None if kl is None else kl.ctypes.data,
+        None if ql is None else ql.ctypes.data,
         rows.ctypes.data, n, o.ctypes.data, lse.ctypes.data, int(threads))
     if rc != 0:
         raise ValueError(f"oracle_attn_rows_gen failed with code {rc}")
     return o, lse
 
 
-def attention_ex(q, k, v, scale: float, causal: bool, k_len=None, threads: int = 0):
+def attention_ex(q, k, v, scale: float, causal: bool, k_len=None, threads: int = 0, q_len=None):
     """All rows of attn_rows_ex; returns (o [B,H,Nq,dv], lse [B,H,Nq])."""
     B, H, Nq, d = q.shape[:3] + v.shape[3:]
-    o, lse = attn_rows_ex(q, k, v, scale, causal, None, k_len, threads)
+    o, lse = attn_rows_ex(q, k, v, scale, causal, None, k_len, threads, q_len)
     return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
 
 
@@ -220,13 +231,14 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0):
 
 
 def attn_bwd_ex(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=None,
-                k_len=None, threads: int = 0):
+                k_len=None, threads: int = 0, q_len=None):
     """Oracle gradients for unequal lengths, key padding and a value head dim
     of its own (oracle_attn_bwd_gen).
 
     q: host [B, H, Nq, dk]; k: [B, H, Nk, dk]; v: [B, H, Nk, dv]; dout:
     [B, H, Nq, dv], one dtype.  q_rows: flat ids (b*H + h)*Nq + i; k_rows:
-    flat ids (b*H + h)*Nk + j (None: all).  k_len: B valid key counts or None.
+    flat ids (b*H + h)*Nk + j (None: all).  k_len / q_len: B valid key / query
+    counts or None.
     Returns (dq [n_q, dk], dk [n_k, dk], dv [n_k, dv]) float64 numpy arrays.
     """
     q, k, v, dout = _as_cpu(q), _as_cpu(k), _as_cpu(v), _as_cpu(dout)
@@ -243,18 +255,14 @@ def attn_bwd_ex(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=N
     kr = np.arange(B * H * Nk, dtype=np.int64) if k_rows is None else k_rows
     qr = np.ascontiguousarray(np.asarray(qr, dtype=np.int64))
     kr = np.ascontiguousarray(np.asarray(kr, dtype=np.int64))
-    kl = None
-    if k_len is not None:
-        kl = np.ascontiguousarray(np.asarray(k_len, dtype=np.int64))
-        if kl.shape != (B,):
-            raise ValueError("k_len must hold one count per batch")
+    kl, ql = _counts(k_len, B, "k_len"), _counts(q_len, B, "q_len")
     dq = np.empty((qr.shape[0], d), dtype=np.float64)
     dk = np.empty((kr.shape[0], d), dtype=np.float64)
     dv = np.empty((kr.shape[0], d_v), dtype=np.float64)
     rc = lib().oracle_attn_bwd_gen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), _CODES[q.dtype],
         B, H, Nq, Nk, d, d_v, float(scale), int(bool(causal)),
-        None if kl is None else kl.ctypes.data,
+        None if kl is None else kl.ctypes.data, None if ql is None else ql.ctypes.data,
         qr.ctypes.data, qr.shape[0], kr.ctypes.data, kr.shape[0],
         dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(threads))
     if rc != 0:
@@ -262,12 +270,13 @@ def attn_bwd_ex(q, k, v, dout, scale: float, causal: bool, q_rows=None, k_rows=N
     return dq, dk, dv
 
 
-def attention_bwd_ex(q, k, v, dout, scale: float, causal: bool, k_len=None, threads: int = 0):
+def attention_bwd_ex(q, k, v, dout, scale: float, causal: bool, k_len=None, threads: int = 0,
+                     q_len=None):
     """All rows of attn_bwd_ex; returns (dq [B,H,Nq,dk], dk [B,H,Nk,dk],
     dv [B,H,Nk,dv])."""
     B, H, Nq, d = q.shape
     Nk, d_v = k.shape[2], v.shape[3]
-    dq, dk, dv = attn_bwd_ex(q, k, v, dout, scale, causal, None, None, k_len, threads)
+    dq, dk, dv = attn_bwd_ex(q, k, v, dout, scale, causal, None, None, k_len, threads, q_len)
     return dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d_v)
 
 

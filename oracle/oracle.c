@@ -62,6 +62,7 @@ typedef struct {
   double scale;
   int causal;
   const long long* k_len; /* per-batch valid keys, or NULL (all Nk) */
+  const long long* q_len; /* per-batch valid queries, or NULL (all Nq) */
   const long long* rows;
   long long n_rows;
   double *o_out, *lse_out;
@@ -73,7 +74,8 @@ typedef struct {
  * so passes 2 and 3 reuse the dot products of the score step.  The scores
  * contract the dk columns of q and k; the output has the dv columns of v.
  * The kept keys J_i are a prefix 0 .. nkeys-1 of the head's keys: keys below
- * the batch's valid length L, and, when causal, at most i + (L - Nq). */
+ * the batch's valid length L, and, when causal, at most i + (L - Lq), where Lq
+ * is the batch's valid query count; a query row at or past Lq keeps none. */
 static void one_row(const job_t* jb, long long r, double* qrow, double* s,
                     double* o, double* lse) {
   const long long Nq = jb->Nq, Nk = jb->Nk, dk = jb->dk, dv = jb->dv;
@@ -86,8 +88,11 @@ static void one_row(const job_t* jb, long long r, double* qrow, double* s,
   long long L = jb->k_len ? jb->k_len[b] : Nk;   /* valid keys of this batch */
   if (L < 0) L = 0;
   if (L > Nk) L = Nk;
-  long long nkeys = L;                           /* |J_i| */
-  if (jb->causal && i + (L - Nq) + 1 < nkeys) nkeys = i + (L - Nq) + 1;
+  long long Lq = jb->q_len ? jb->q_len[b] : Nq;  /* valid queries of this batch */
+  if (Lq < 0) Lq = 0;
+  if (Lq > Nq) Lq = Nq;
+  long long nkeys = i < Lq ? L : 0;              /* |J_i| */
+  if (jb->causal && i + (L - Lq) + 1 < nkeys) nkeys = i + (L - Lq) + 1;
   if (nkeys < 0) nkeys = 0;
 
   for (long long c = 0; c < dv; ++c) o[c] = 0.0;
@@ -157,14 +162,14 @@ int oracle_attn_rows_ex(const void* q, const void* k, const void* v, int dtype,
                         double scale, int causal, const long long* k_len,
                         const long long* rows, long long n_rows,
                         double* o_out, double* lse_out, int threads) {
-  return oracle_attn_rows_gen(q, k, v, dtype, B, H, Nq, Nk, d, d, scale, causal, k_len, rows,
-                              n_rows, o_out, lse_out, threads);
+  return oracle_attn_rows_gen(q, k, v, dtype, B, H, Nq, Nk, d, d, scale, causal, k_len, NULL,
+                              rows, n_rows, o_out, lse_out, threads);
 }
 
 int oracle_attn_rows_gen(const void* q, const void* k, const void* v, int dtype,
                          long long B, long long H, long long Nq, long long Nk, long long dk,
                          long long dv, double scale, int causal, const long long* k_len,
-                         const long long* rows, long long n_rows,
+                         const long long* q_len, const long long* rows, long long n_rows,
                          double* o_out, double* lse_out, int threads) {
   if (!q || !k || !v || !o_out || !lse_out || (n_rows > 0 && !rows)) return -1;
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || dk <= 0 || dv <= 0 || n_rows < 0) return -1;
@@ -175,7 +180,7 @@ int oracle_attn_rows_gen(const void* q, const void* k, const void* v, int dtype,
     if (rows[t] < 0 || rows[t] >= total) return -1;
   if (n_rows == 0) return 0;
 
-  job_t jb = {q, k, v, dtype, H, Nq, Nk, dk, dv, scale, causal, k_len, rows, n_rows,
+  job_t jb = {q, k, v, dtype, H, Nq, Nk, dk, dv, scale, causal, k_len, q_len, rows, n_rows,
               o_out, lse_out, 0};
   int nt = oracle_thread_count(threads);
   if (nt > n_rows) nt = (int)n_rows;

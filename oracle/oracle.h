@@ -92,14 +92,21 @@ int oracle_attn_rows_ex(const void* q, const void* k, const void* v, int dtype,
  * oracle_attn_rows_gen -- oracle_attn_rows_ex with the value head dim apart
  * from the query/key one (Q of shape (n, d_k), K (m, d_k), V (m, d_v):
  * "Transformer Attention: A Mathematical Deep Dive", the scaled dot-product
- * attention definition): q [B][H][Nq][dk], k [B][H][Nk][dk], v [B][H][Nk][dv];
- * the scores contract the dk columns, o_out is [n_rows][dv].
- * oracle_attn_rows_ex is this with dk = dv = d.
+ * attention definition) and per-batch padding of the queries too:
+ * q [B][H][Nq][dk], k [B][H][Nk][dk], v [B][H][Nk][dv]; the scores contract
+ * the dk columns, o_out is [n_rows][dv].
+ *   q_len : host array of B valid query counts (each clamped to [0, Nq]), or
+ *           NULL for Nq.  With Lq the batch's query count and L its key count,
+ *           J_i = {}                            (i >= Lq: a padding row)
+ *               = {j < L}                       (non-causal)
+ *               = {j < L, j <= i + (L - Lq)}    (causal: the last valid query
+ *                                                sees every valid key)
+ * oracle_attn_rows_ex is this with dk = dv = d and q_len = NULL.
  */
 int oracle_attn_rows_gen(const void* q, const void* k, const void* v, int dtype,
                          long long B, long long H, long long Nq, long long Nk, long long dk,
                          long long dv, double scale, int causal, const long long* k_len,
-                         const long long* rows, long long n_rows,
+                         const long long* q_len, const long long* rows, long long n_rows,
                          double* o_out, double* lse_out, int threads);
 
 /*
@@ -137,12 +144,14 @@ int oracle_attn_bwd_ex(const void* q, const void* k, const void* v, const void* 
  * q [B][H][Nq][dk], k [B][H][Nk][dk], v [B][H][Nk][dv], dout [B][H][Nq][dv];
  * dq_out [n_q][dk], dk_out [n_k][dk], dv_out [n_k][dv].  dP_ij = <g_i, v_j>
  * and D_i = <g_i, o_i> contract the dv columns, the scores and dq, dk the dk
- * columns.  oracle_attn_bwd_ex is this with dk = dv = d.
+ * columns; q_len as in oracle_attn_rows_gen (a padding query row has dq = 0
+ * and adds nothing to dk, dv).  oracle_attn_bwd_ex is this with dk = dv = d
+ * and q_len = NULL.
  */
 int oracle_attn_bwd_gen(const void* q, const void* k, const void* v, const void* dout, int dtype,
                         long long B, long long H, long long Nq, long long Nk, long long dk,
                         long long dv, double scale, int causal, const long long* k_len,
-                        const long long* q_rows, long long n_q,
+                        const long long* q_len, const long long* q_rows, long long n_q,
                         const long long* k_rows, long long n_k,
                         double* dq_out, double* dk_out, double* dv_out, int threads);
 

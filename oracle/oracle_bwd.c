@@ -37,6 +37,7 @@ typedef struct {
   double scale;
   int causal;
   const long long* k_len; /* per-batch valid keys, or NULL (all Nk) */
+  const long long* q_len; /* per-batch valid queries, or NULL (all Nq) */
   /* per touched head: lse and D of every query row, [n_heads][N] */
   const long long* heads; /* touched heads, ascending */
   long long n_heads;
@@ -73,11 +74,20 @@ static long long valid_keys(const bjob_t* jb, long long head) {
   return L;
 }
 
-/* |J_i|: query i keeps keys 0 .. nkeys-1 (j < L and, causal, j <= i + L - Nq) */
+/* valid queries Lq of the batch that head `head` belongs to */
+static long long valid_queries(const bjob_t* jb, long long head) {
+  long long L = jb->q_len ? jb->q_len[head / jb->H] : jb->Nq;
+  if (L < 0) L = 0;
+  if (L > jb->Nq) L = jb->Nq;
+  return L;
+}
+
+/* |J_i|: query i keeps keys 0 .. nkeys-1 (i < Lq, j < L and, causal,
+ * j <= i + L - Lq); a query at or past Lq keeps none */
 static long long kept_keys(const bjob_t* jb, long long head, long long i) {
-  const long long L = valid_keys(jb, head);
-  long long n = L;
-  if (jb->causal && i + (L - jb->Nq) + 1 < n) n = i + (L - jb->Nq) + 1;
+  const long long L = valid_keys(jb, head), Lq = valid_queries(jb, head);
+  long long n = i < Lq ? L : 0;
+  if (jb->causal && i + (L - Lq) + 1 < n) n = i + (L - Lq) + 1;
   return n < 0 ? 0 : n;
 }
 
@@ -233,13 +243,13 @@ int oracle_attn_bwd_ex(const void* q, const void* k, const void* v, const void* 
                        const long long* k_rows, long long n_k,
                        double* dq_out, double* dk_out, double* dv_out, int threads) {
   return oracle_attn_bwd_gen(q, k, v, dout, dtype, B, H, Nq, Nk, d, d, scale, causal, k_len,
-                             q_rows, n_q, k_rows, n_k, dq_out, dk_out, dv_out, threads);
+                             NULL, q_rows, n_q, k_rows, n_k, dq_out, dk_out, dv_out, threads);
 }
 
 int oracle_attn_bwd_gen(const void* q, const void* k, const void* v, const void* dout, int dtype,
                         long long B, long long H, long long Nq, long long Nk, long long d_qk,
                         long long d_v, double scale, int causal, const long long* k_len,
-                        const long long* q_rows, long long n_q,
+                        const long long* q_len, const long long* q_rows, long long n_q,
                         const long long* k_rows, long long n_k,
                         double* dq_out, double* dk_out, double* dv_out, int threads) {
   if (!q || !k || !v || !dout) return -1;
@@ -279,6 +289,7 @@ int oracle_attn_bwd_gen(const void* q, const void* k, const void* v, const void*
   jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.d_qk = d_qk; jb.d_v = d_v;
   jb.scale = scale; jb.causal = causal;
   jb.k_len = k_len;
+  jb.q_len = q_len;
   jb.heads = heads; jb.n_heads = u; jb.lse = lse; jb.D = D;
   jb.q_rows = q_rows; jb.k_rows = k_rows; jb.n_q = n_q; jb.n_k = n_k;
   jb.dq = dq_out; jb.dk = dk_out; jb.dv = dv_out;
