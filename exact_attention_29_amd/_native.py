@@ -59,7 +59,7 @@ def library():
         L.fa_fwd_gen.restype = ctypes.c_int
         L.fa_fwd_gen.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_size_t, ctypes.c_void_p]
+            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.fa_fwd_gen_workspace_size.restype = ctypes.c_size_t
         L.fa_fwd_gen_workspace_size.argtypes = [ctypes.c_int] * 8
         L.fa_fwd_gen_supported.restype = ctypes.c_int
@@ -79,7 +79,7 @@ def library():
         L.fa_bwd_gen.restype = ctypes.c_int
         L.fa_bwd_gen.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_size_t, ctypes.c_void_p]
+            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.fa_bwd_gen_workspace_size.restype = ctypes.c_size_t
         L.fa_bwd_gen_workspace_size.argtypes = [ctypes.c_int] * 8
         L.fa_bwd_gen_supported.restype = ctypes.c_int
@@ -144,10 +144,11 @@ def fa_fwd_ex_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, causal: i
 
 def fa_fwd_gen(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
                d_qk: int, d_v: int, scale: float, causal: int, dtype: int, k_len: int,
-               workspace: int, workspace_bytes: int, stream: int) -> int:
-    """The raw C entry point with separate query/key and value head dims."""
+               q_len: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    """The raw C entry point with separate query/key and value head dims and
+    per-batch key and query counts."""
     return library().fa_fwd_gen(q, k, v, o, lse, B, H, Nq, Nk, d_qk, d_v, ctypes.c_float(scale),
-                                int(causal), int(dtype), k_len, workspace,
+                                int(causal), int(dtype), k_len, q_len, workspace,
                                 int(workspace_bytes), stream)
 
 
@@ -161,22 +162,33 @@ def fa_fwd_gen_supported(d_qk: int, d_v: int, dtype: int, causal: int) -> bool:
     return bool(library().fa_fwd_gen_supported(int(d_qk), int(d_v), int(dtype), int(causal)))
 
 
+def _check_counts(c, name, B, device):
+    """Per-batch counts must be a contiguous int32 tensor [B] on q's device."""
+    if c is not None:
+        if not isinstance(c, torch.Tensor) or c.dtype != torch.int32 or c.shape != (B,) \
+                or not c.is_contiguous() or c.device != device:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor [B]")
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               scale: float | None = None, out: torch.Tensor | None = None,
               lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
-              split_keys: bool = True, k_len: torch.Tensor | None = None):
+              split_keys: bool = True, k_len: torch.Tensor | None = None,
+              q_len: torch.Tensor | None = None):
     """O = softmax(scale * Q K^T) V and the per-row log-sum-exp, on the GPU.
 
     q: contiguous device tensor [B, H, Nq, d]; k: [B, H, Nk, d]; v:
-    [B, H, Nk, dv] (dv may differ from d), one dtype.  k_len: optional int32
-    device tensor [B] of valid key counts (key padding).  scale defaults to
-    1/sqrt(d).  Returns (o [B,H,Nq,dv] in q's dtype, lse [B,H,Nq] fp32); rows
-    with no kept key give o = 0, lse = -inf.  The launch is asynchronous on
+    [B, H, Nk, dv] (dv may differ from d), one dtype.  k_len, q_len: optional
+    int32 device tensors [B] of valid key and query counts (padding; a query
+    row at or past its batch's count is padding, and causal alignment puts the
+    last valid query on the last valid key).  scale defaults to 1/sqrt(d).
+    Returns (o [B,H,Nq,dv] in q's dtype, lse [B,H,Nq] fp32); rows with no kept
+    key give o = 0, lse = -inf.  The launch is asynchronous on
     `stream` (default: torch's current stream).  Equal lengths and head dims
     without k_len run through fa_fwd (fa_fwd_ws when split_keys and the
     library would split fp32 keys over ranges; the workspace comes from
     torch's allocator on `stream`); other shapes through fa_fwd_ex, and
-    unequal head dims through fa_fwd_gen.
+    unequal head dims or query counts through fa_fwd_gen.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
@@ -193,10 +205,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
         raise ValueError("q, k, v must be on one device")
     B, H, N, d = q.shape
     Nk, dv = k.shape[2], v.shape[3]
-    if k_len is not None:
-        if not isinstance(k_len, torch.Tensor) or k_len.dtype != torch.int32 \
-                or k_len.shape != (B,) or not k_len.is_contiguous() or k_len.device != q.device:
-            raise ValueError("k_len must be a contiguous int32 device tensor [B]")
+    _check_counts(k_len, "k_len", B, q.device)
+    _check_counts(q_len, "q_len", B, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -212,7 +222,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     code = _DTYPE_CODE[q.dtype]
-    if dv != d:
+    if dv != d or q_len is not None:
         with torch.cuda.device(q.device):
             ws_bytes = fa_fwd_gen_workspace_size(B, H, N, Nk, d, dv, int(bool(causal)), code) \
                 if split_keys else 0
@@ -223,6 +233,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
             st = fa_fwd_gen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), B, H, N, Nk, d, dv, float(scale), int(bool(causal)),
                             code, None if k_len is None else k_len.data_ptr(),
+                            None if q_len is None else q_len.data_ptr(),
                             None if ws is None else ws.data_ptr(), ws_bytes, stream.cuda_stream)
             if ws is not None:
                 ws.record_stream(stream)
@@ -301,11 +312,13 @@ def fa_bwd_ex_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, causal: i
 
 def fa_bwd_gen(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
                B: int, H: int, Nq: int, Nk: int, d_qk: int, d_v: int, scale: float, causal: int,
-               dtype: int, k_len: int, workspace: int, workspace_bytes: int, stream: int) -> int:
-    """The raw C entry point with separate query/key and value head dims."""
+               dtype: int, k_len: int, q_len: int, workspace: int, workspace_bytes: int,
+               stream: int) -> int:
+    """The raw C entry point with separate query/key and value head dims and
+    per-batch key and query counts."""
     return library().fa_bwd_gen(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d_qk, d_v,
-                                ctypes.c_float(scale), int(causal), int(dtype), k_len, workspace,
-                                int(workspace_bytes), stream)
+                                ctypes.c_float(scale), int(causal), int(dtype), k_len, q_len,
+                                workspace, int(workspace_bytes), stream)
 
 
 def fa_bwd_gen_workspace_size(B: int, H: int, Nq: int, Nk: int, d_qk: int, d_v: int,
@@ -322,16 +335,18 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
                   lse: torch.Tensor, dout: torch.Tensor, causal: bool = False,
                   scale: float | None = None, dq: torch.Tensor | None = None,
                   dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
-                  stream: torch.cuda.Stream | None = None, k_len: torch.Tensor | None = None):
+                  stream: torch.cuda.Stream | None = None, k_len: torch.Tensor | None = None,
+                  q_len: torch.Tensor | None = None):
     """Gradients (dq, dk, dv) of the attention `attention()` computes.
 
     q: contiguous device tensor [B, H, Nq, d]; k: [B, H, Nk, d]; v: [B, H,
     Nk, dv]; o, dout: [B, H, Nq, dv]; one dtype (bf16, fp16, or fp32); o and
-    lse as returned by attention() for the same arguments (k_len included).
+    lse as returned by attention() for the same arguments (k_len, q_len
+    included; padding query rows get dq = 0 and are never read).
     The workspace comes from torch's allocator on `stream`.  Asynchronous on
     `stream` (default: torch's current stream).  Equal lengths and head dims
     without k_len run through fa_bwd, other shapes fa_bwd_ex, unequal head dims
-    fa_bwd_gen.  Returns (dq like q, dk like k, dv like v).
+    or query counts fa_bwd_gen.  Returns (dq like q, dk like k, dv like v).
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
@@ -350,10 +365,8 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32 \
             or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
-    if k_len is not None:
-        if not isinstance(k_len, torch.Tensor) or k_len.dtype != torch.int32 \
-                or k_len.shape != (B,) or not k_len.is_contiguous() or k_len.device != q.device:
-            raise ValueError("k_len must be a contiguous int32 device tensor [B]")
+    _check_counts(k_len, "k_len", B, q.device)
+    _check_counts(q_len, "q_len", B, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     outs = []
@@ -367,7 +380,7 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     code = _DTYPE_CODE[q.dtype]
-    square = Nk == N and k_len is None and d_v == d
+    square = Nk == N and k_len is None and q_len is None and d_v == d
     with torch.cuda.device(q.device):
         ws_bytes = fa_bwd_gen_workspace_size(B, H, N, Nk, d, d_v, int(bool(causal)), code)
         if ws_bytes == 0:
@@ -382,14 +395,15 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
             where = "fa_bwd"
             st = fa_bwd(*ptrs, B, H, N, d, float(scale), int(bool(causal)), code, ws.data_ptr(),
                         ws_bytes, stream.cuda_stream)
-        elif d_v == d:
+        elif d_v == d and q_len is None:
             where = "fa_bwd_ex"
             st = fa_bwd_ex(*ptrs, B, H, N, Nk, d, float(scale), int(bool(causal)), code, kl,
                            ws.data_ptr(), ws_bytes, stream.cuda_stream)
         else:
             where = "fa_bwd_gen"
             st = fa_bwd_gen(*ptrs, B, H, N, Nk, d, d_v, float(scale), int(bool(causal)), code, kl,
-                            ws.data_ptr(), ws_bytes, stream.cuda_stream)
+                            None if q_len is None else q_len.data_ptr(), ws.data_ptr(), ws_bytes,
+                            stream.cuda_stream)
         ws.record_stream(stream)
     if st != FA_OK:
         raise FaError(st, where) if st == FA_ERR_HIP else ValueError(

@@ -158,17 +158,20 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ dO,
                                                      const float* __restrict__ LSE,
                                                      float* __restrict__ NL, float* __restrict__ ND,
-                                                     int N, int n_pad, long long padded_rows,
+                                                     int N, int H, const int* __restrict__ q_len,
+                                                     int n_pad, long long padded_rows,
                                                      float inv_scale) {
-  // N: query rows per head (the rows of O, dO and lse)
+  // N: query rows per head (the rows of O, dO and lse); rows from the batch's
+  // valid query count on are padding: P = 0 there (nl = -inf), never read
   constexpr int TPR = D / 8, RPB = 256 / TPR;
   const int t = threadIdx.x % TPR;
   const long long prow = (long long)blockIdx.x * RPB + threadIdx.x / TPR;  // padded row id
   if (prow >= padded_rows) return;  // whole rows only: TPR divides the wave
   const long long bh = prow / n_pad;
   const int i = (int)(prow % n_pad);
-  float acc = 0.f, nl = 0.f;
-  if (i < N) {
+  const int nq = q_len ? min(max(q_len[bh / H], 0), N) : N;
+  float acc = 0.f, nl = i < N ? -INFINITY : 0.f;
+  if (i < nq) {
     const size_t row = (size_t)bh * N + i;
     const u32x4 a = *(const u32x4*)(O + row * D + 8 * t);
     const u32x4 b = *(const u32x4*)(dO + row * D + 8 * t);
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int H,
-    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale, int n_split,
+    const int* __restrict__ k_len, const int* __restrict__ q_len, int n_pad, int n_kblocks, int total, float scale, int n_split,
     float* __restrict__ part, long long kstride, long long vstride) {
   constexpr int BQ = 32, CGK = DK / 32, CGV = DV / 32;
   // 1 KB blocks and bytes of one 32-row Q tile and one dO tile
@@ -227,10 +230,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   const int split = item % n_split, work = item / n_split;
   const int bh = work / n_kblocks;
   const int kb = work % n_kblocks;  // ascending: causal key blocks near 0 see the most queries
-  // as in the forward: key j is kept for query i iff j < nk and, when causal,
-  // j <= i + diag
+  // as in the forward: key j is kept for query i < nq iff j < nk and, when
+  // causal, j <= i + diag; query rows from nq on are padding
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
-  const int diag = nk - Nq;
+  const int nq = q_len ? min(max(q_len[bh / H], 0), Nq) : Nq;
+  const int diag = nk - nq;
   const size_t head = (size_t)bh * Nq * DK, ohead = (size_t)bh * Nq * DV;
   const size_t khead = (size_t)bh * Nk * DK, vhead = (size_t)bh * Nk * DV;
   const int k0 = kb * 32 * NW;              // the block's first key
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   const float* nl_row = NL + (size_t)bh * n_pad;
   const float* nd_row = ND + (size_t)bh * n_pad;
 
-  const int nqt = (Nq + BQ - 1) / BQ;
+  const int nqt = (nq + BQ - 1) / BQ;
   // first tile holding a query that keeps a key of this block (q + diag >= k0);
   // a block wholly past the valid keys has none and only writes zeros
   const int qt0 = k0 >= nk ? nqt : CAUSAL ? max(0, k0 - diag) / BQ : 0;
@@ -279,8 +283,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       const float* src = (wave == 0 ? nl_row : nd_row) + r0;
       dma16(buffer_desc(src, BQ * 4), base + TBQ + TBD + 1024 * wave, lane * 16);
     }
-    const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * DK, (unsigned)(Nq - r0) * DK * 2);
-    const u32x4 dd = buffer_desc(dO + ohead + (size_t)r0 * DV, (unsigned)(Nq - r0) * DV * 2);
+    // rows past nq read as zero (never loaded)
+    const u32x4 dq = buffer_desc(Q + head + (size_t)r0 * DK, (unsigned)(nq - r0) * DK * 2);
+    const u32x4 dd = buffer_desc(dO + ohead + (size_t)r0 * DV, (unsigned)(nq - r0) * DV * 2);
     if constexpr (DK == DV) {  // the same block pattern in both tiles
 #pragma unroll
       for (int i = 0; i < (TBLKQ + NW - 1) / NW; ++i) {
@@ -417,7 +422,7 @@ template <class TT, int DK, int DV, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV == 128 ? 3 : 2, DK + DV == 128 ? 3 : 2))) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
-    uint16_t* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
+    uint16_t* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, const int* __restrict__ q_len, int n_pad,
     int n_qblocks, int total, float scale, int n_split, float* __restrict__ part,
     long long qstride) {
   // DK: head dim of Q, K and dQ; DV: of V and dO
@@ -440,7 +445,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   int qb = work % n_qblocks;
   if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the dK/dV kernel
-  const int diag = nk - Nq;
+  const int nq = q_len ? min(max(q_len[bh / H], 0), Nq) : Nq;
+  const int diag = nk - nq;
   const size_t head = (size_t)bh * Nq * DK, ohead = (size_t)bh * Nq * DV;
   const size_t khead = (size_t)bh * Nk * DK, vhead = (size_t)bh * Nk * DV;
   const int q_first = qb * BR + 32 * wave;
@@ -453,31 +459,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     if constexpr (DK == DV) {
 #pragma unroll
       for (int c = 0; c < DK / 16; ++c) {
-        qf[c] = my_q < Nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
-        of[c] = my_q < Nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
+        qf[c] = my_q < nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
+        of[c] = my_q < nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
       }
     } else {
 #pragma unroll
       for (int c = 0; c < DK / 16; ++c)
-        qf[c] = my_q < Nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
+        qf[c] = my_q < nq ? *(const u32x4*)(qr + 16 * c) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int c = 0; c < DV / 16; ++c)
-        of[c] = my_q < Nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
+        of[c] = my_q < nq ? *(const u32x4*)(dr + 16 * c) : u32x4{0, 0, 0, 0};
     }
   }
   const float c2 = scale * kLog2e;
-  // (rows past N are never stored; the block's last rows may lie past the padding)
-  const float nl2 = my_q < Nq ? NL[(size_t)bh * n_pad + my_q] * c2 : 0.f;
-  const float nd = my_q < Nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
+  // rows from nq on get no weight (P = 0) and store dQ = 0; rows past Nq are
+  // never stored (the block's last rows may lie past the row padding)
+  const float nl2 = my_q < nq ? NL[(size_t)bh * n_pad + my_q] * c2 : -INFINITY;
+  const float nd = my_q < nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
   f32x16 dq[DK / 32];
 #pragma unroll
   for (int b = 0; b < DK / 32; ++b) dq[b] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(nk, (qb + 1) * BR + diag) : nk;
+  const int kv_end = qb * BR >= nq ? 0 : CAUSAL ? min(nk, min((qb + 1) * BR, nq) + diag) : nk;
   const int T = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
   const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
-  // a wave whose rows all lie past Nq only helps load the tiles
-  const int my_T = q_first >= Nq ? 0 : CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
+  // a wave whose rows all lie past nq only helps load the tiles
+  const int my_T = q_first >= nq ? 0 : CAUSAL ? (last_key < 0 ? 0 : min(T, last_key / BC + 1)) : T;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto load = [&](int j, int buf) {
     const int k0 = j * BC;
@@ -576,7 +583,8 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_f32(const float* __restrict
                                                          const float* __restrict__ dO,
                                                          const float* __restrict__ LSE,
                                                          float* __restrict__ NL, float* __restrict__ ND,
-                                                         int N, int n_pad, long long padded_rows,
+                                                         int N, int H, const int* __restrict__ q_len,
+                                                         int n_pad, long long padded_rows,
                                                          float inv_scale) {
   constexpr int TPR = D / 4 < 64 ? D / 4 : 64, RPB = 256 / TPR, CH = D / (4 * TPR);
   const int t = threadIdx.x % TPR;
@@ -584,8 +592,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_f32(const float* __restrict
   if (prow >= padded_rows) return;  // whole rows only: TPR divides the wave
   const long long bh = prow / n_pad;
   const int i = (int)(prow % n_pad);
-  float acc = 0.f, nl = 0.f;
-  if (i < N) {
+  const int nq = q_len ? min(max(q_len[bh / H], 0), N) : N;  // as in the 16-bit kernel
+  float acc = 0.f, nl = i < N ? -INFINITY : 0.f;
+  if (i < nq) {
     const size_t row = (size_t)bh * N + i;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -655,7 +664,7 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
     float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int H,
-    const int* __restrict__ k_len, int n_pad, int n_kblocks, int total, float scale, int n_split,
+    const int* __restrict__ k_len, const int* __restrict__ q_len, int n_pad, int n_kblocks, int total, float scale, int n_split,
     float* __restrict__ part, long long kstride, long long vstride) {
   constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSL / 32, NBV = DSLV / 32;
   __shared__ f32x16 red[DS > 1 ? 2 * DS * 64 : 1];
@@ -665,7 +674,8 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
   const int split = item % n_split, work = item / n_split;  // a block's splits are neighbours
   const int bh = work / n_kblocks, kb = work % n_kblocks;
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernels
-  const int diag = nk - Nq;
+  const int nq = q_len ? min(max(q_len[bh / H], 0), Nq) : Nq;
+  const int diag = nk - nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
   const size_t ohead = (size_t)bh * Nq * DV, vhead = (size_t)bh * Nk * DV;
   const int k0 = kb * 32, my_k = k0 + x, col0 = wave * DSL, colv0 = wave * DSLV;
@@ -706,7 +716,7 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
   const float c2 = scale * kLog2e;
   const float* nl_row = NL + (size_t)bh * n_pad;
   const float* nd_row = ND + (size_t)bh * n_pad;
-  const int nqt = (Nq + 31) / 32;
+  const int nqt = (nq + 31) / 32;
   const int qt_first = k0 >= nk ? nqt : CAUSAL ? max(0, k0 - diag) / 32 : 0;
   // this workgroup's share of the block's query tiles (all of them unsplit)
   const int span = nqt - qt_first;
@@ -719,7 +729,7 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
     const int q0 = t * 32;
     f32x16 s = f32x16{}, dp = f32x16{};
     {
-      const bool ok = q0 + x < Nq;
+      const bool ok = q0 + x < nq;
       const float* qr = Q + head + (size_t)(q0 + x) * D + col0 + 4 * h;
       const float* gr = dO + ohead + (size_t)(q0 + x) * DV + colv0 + 4 * h;
       if constexpr (DSL == DSLV) {
@@ -774,8 +784,8 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dkdv_f32(
     for (int r = 0; r < 16; ++r) {
       const int q = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
       float gv[NBV], qv[NB];
-      load_nb<NBV>(dO + ohead + (size_t)q * DV + colv0 + NBV * x, q < Nq, gv);
-      load_nb<NB>(Q + head + (size_t)q * D + col0 + NB * x, q < Nq, qv);
+      load_nb<NBV>(dO + ohead + (size_t)q * DV + colv0 + NBV * x, q < nq, gv);
+      load_nb<NB>(Q + head + (size_t)q * D + col0 + NB * x, q < nq, qv);
       if constexpr (DSL == DSLV) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -825,7 +835,7 @@ template <int DSL, int DSLV, int DS, bool CAUSAL>
 __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ ND,
-    float* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, int n_pad,
+    float* __restrict__ dQ, int Nq, int Nk, int H, const int* __restrict__ k_len, const int* __restrict__ q_len, int n_pad,
     int n_qblocks, int total, float scale, int n_split, float* __restrict__ part,
     long long part_stride) {
   constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSL / 32;
@@ -838,7 +848,8 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
   int qb = work % n_qblocks;
   if (CAUSAL) qb = n_qblocks - 1 - qb;  // longest rows first
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
-  const int diag = nk - Nq;
+  const int nq = q_len ? min(max(q_len[bh / H], 0), Nq) : Nq;
+  const int diag = nk - nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
   const size_t ohead = (size_t)bh * Nq * DV, vhead = (size_t)bh * Nk * DV;
   const int q0 = qb * 32, my_q = q0 + x, col0 = wave * DSL, colv0 = wave * DSLV;
@@ -854,23 +865,24 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
     if constexpr (DSL == DSLV) {
 #pragma unroll
       for (int u = 0; u < NF; ++u) {
-        qf[u] = my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
-        gf[u] = my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
+        qf[u] = my_q < nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+        gf[u] = my_q < nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < NF; ++u) qf[u] = my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+      for (int u = 0; u < NF; ++u) qf[u] = my_q < nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int u = 0; u < NFV; ++u) gf[u] = my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
+      for (int u = 0; u < NFV; ++u) gf[u] = my_q < nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0};
     }
   }
   const float c2 = scale * kLog2e;
-  const float nl2 = my_q < Nq ? NL[(size_t)bh * n_pad + my_q] * c2 : 0.f;
-  const float nd = my_q < Nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
+  // padding rows (from nq on) get no weight and store dQ = 0
+  const float nl2 = my_q < nq ? NL[(size_t)bh * n_pad + my_q] * c2 : -INFINITY;
+  const float nd = my_q < nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
   f32x16 dq[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
-  const int kv_end = CAUSAL ? min(nk, q0 + 32 + diag) : nk;
+  const int kv_end = q0 >= nq ? 0 : CAUSAL ? min(nk, min(q0 + 32, nq) + diag) : nk;
   const int T = kv_end > 0 ? (kv_end + 31) / 32 : 0;
   const int j0 = (int)((long long)T * split / n_split), j1 = (int)((long long)T * (split + 1) / n_split);
   const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1);
@@ -888,9 +900,9 @@ __global__ __launch_bounds__(DS * 64) void attn_bwd_dq_f32(
           const f32x4 ka = ok ? *(const f32x4*)(kr + 8 * u) : f32x4{0, 0, 0, 0};
           const f32x4 va = ok ? *(const f32x4*)(vr + 8 * u) : f32x4{0, 0, 0, 0};
           const f32x4 qa = HOLD ? qf[HOLD ? u : 0]
-                                : (my_q < Nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0});
+                                : (my_q < nq ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0});
           const f32x4 ga = HOLD ? gf[HOLD ? u : 0]
-                                : (my_q < Nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0});
+                                : (my_q < nq ? *(const f32x4*)(grow + 8 * u) : f32x4{0, 0, 0, 0});
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             st = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[v], qa[v], st, 0, 0, 0);
@@ -1020,7 +1032,8 @@ BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype)
 template <class TT, int DK, int DV>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, int BH, int H, int Nq, int Nk,
-                      const int* k_len, float scale, bool causal, float* ws, const BwdSplit& sp,
+                      const int* k_len, const int* q_len, float scale, bool causal, float* ws,
+                      const BwdSplit& sp,
                       hipStream_t st) {
   const int n_pad = (Nq + kRowPad - 1) / kRowPad * kRowPad;
   const long long prow = (long long)BH * n_pad;
@@ -1029,7 +1042,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   {
     constexpr int RPB = 256 / (DV / 8);  // delta = <dO, O> over the value dim
     hipLaunchKernelGGL((attn_bwd_prep<TT, DV>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256), 0,
-                       st, (const uint16_t*)o, (const uint16_t*)dout, lse, nl, nd, Nq, n_pad, prow,
+                       st, (const uint16_t*)o, (const uint16_t*)dout, lse, nl, nd, Nq, H, q_len, n_pad, prow,
                        1.f / scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
@@ -1046,22 +1059,22 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   if (causal) {
     hipLaunchKernelGGL((attn_bwd_dkdv<TT, DK, DV, true, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale,
+                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, q_len, n_pad, nkb, tk, scale,
                        sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq<TT, DK, DV, true, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart,
+                       (uint16_t*)dq, Nq, Nk, H, k_len, q_len, n_pad, nqb, tq, scale, sp.q, qpart,
                        qstride);
   } else {
     hipLaunchKernelGGL((attn_bwd_dkdv<TT, DK, DV, false, NWK>), dim3(tk), bk, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale,
+                       (uint16_t*)dk, (uint16_t*)dv, Nq, Nk, H, k_len, q_len, n_pad, nkb, tk, scale,
                        sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq<TT, DK, DV, false, NWQ>), dim3(tq), bq, 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, nl, nd,
-                       (uint16_t*)dq, Nq, Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart,
+                       (uint16_t*)dq, Nq, Nk, H, k_len, q_len, n_pad, nqb, tq, scale, sp.q, qpart,
                        qstride);
   }
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -1083,8 +1096,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
 template <int DSL, int DSLV, int DS>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int BH,
-                          int H, int Nq, int Nk, const int* k_len, float scale, bool causal,
-                          float* ws, const BwdSplit& sp, hipStream_t st) {
+                          int H, int Nq, int Nk, const int* k_len, const int* q_len, float scale,
+                          bool causal, float* ws, const BwdSplit& sp, hipStream_t st) {
   constexpr int D = DSL * DS, DV = DSLV * DS;
   const int n_pad = (Nq + kRowPad - 1) / kRowPad * kRowPad;
   const long long prow = (long long)BH * n_pad;
@@ -1093,7 +1106,7 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
   {
     constexpr int TPR = DV / 4 < 64 ? DV / 4 : 64, RPB = 256 / TPR;  // delta over the value dim
     hipLaunchKernelGGL((attn_bwd_prep_f32<DV>), dim3((unsigned)((prow + RPB - 1) / RPB)), dim3(256),
-                       0, st, (const float*)o, (const float*)dout, lse, nl, nd, Nq, n_pad, prow,
+                       0, st, (const float*)o, (const float*)dout, lse, nl, nd, Nq, H, q_len, n_pad, prow,
                        1.f / scale);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
@@ -1107,19 +1120,19 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
   if (causal) {
     hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DSLV, DS, true>), dim3(tk), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
-                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride, vstride);
+                       (float*)dv, Nq, Nk, H, k_len, q_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DSLV, DS, true>), dim3(tq), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
-                       Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
+                       Nk, H, k_len, q_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
   } else {
     hipLaunchKernelGGL((attn_bwd_dkdv_f32<DSL, DSLV, DS, false>), dim3(tk), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dk,
-                       (float*)dv, Nq, Nk, H, k_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride, vstride);
+                       (float*)dv, Nq, Nk, H, k_len, q_len, n_pad, nkb, tk, scale, sp.kv, kvpart, kstride, vstride);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq_f32<DSL, DSLV, DS, false>), dim3(tq), blk, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)dout, nl, nd, (float*)dq, Nq,
-                       Nk, H, k_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
+                       Nk, H, k_len, q_len, n_pad, nqb, tq, scale, sp.q, qpart, qstride);
   }
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   auto sum = [&](const float* part, void* out, long long n, int n_split) {
@@ -1146,14 +1159,15 @@ namespace {
 template <class TT>
 hipError_t launch_bwd_dims(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           int bh, int H, int Nq, int Nk, const int* k_len, float scale,
+                           int bh, int H, int Nq, int Nk, const int* k_len, const int* q_len,
+                           float scale,
                            bool causal, int d_qk, int d_v, float* ws, const BwdSplit& sp,
                            hipStream_t st) {
   if (d_qk == 64)
-    return d_v == 64 ? launch_bwd<TT, 64, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st)
-                     : launch_bwd<TT, 64, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st);
-  return d_v == 64 ? launch_bwd<TT, 128, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st)
-                   : launch_bwd<TT, 128, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st);
+    return d_v == 64 ? launch_bwd<TT, 64, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st)
+                     : launch_bwd<TT, 64, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st);
+  return d_v == 64 ? launch_bwd<TT, 128, 64>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st)
+                   : launch_bwd<TT, 128, 128>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st);
 }
 
 }  // namespace
@@ -1195,7 +1209,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) 
 int fa_bwd_gen(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
                int d_qk, int d_v, float scale, int causal, int dtype, const int* k_len,
-               void* workspace, size_t workspace_bytes, void* stream) {
+               const int* q_len, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d_qk <= 0 || d_v <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -1217,26 +1231,26 @@ int fa_bwd_gen(const void* q, const void* k, const void* v, const void* o, const
   for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv,
                         (const void*)workspace})
     if (!aligned16(p)) return FA_ERR_UNSUPPORTED;
-  if (((uintptr_t)k_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  if (((uintptr_t)k_len & 3u) != 0 || ((uintptr_t)q_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   const int bh = (int)BH;
   float* ws = (float*)workspace;
   const BwdSplit sp = plan_bwd_split(BH, Nq, Nk, d_qk, d_v, dtype);
   hipError_t e;
   if (dtype == FA_DTYPE_BF16) {
-    e = launch_bwd_dims<Bf16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, sp, st);
+    e = launch_bwd_dims<Bf16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, d_qk, d_v, ws, sp, st);
   } else if (dtype == FA_DTYPE_FP16) {
-    e = launch_bwd_dims<F16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, d_qk, d_v, ws, sp, st);
+    e = launch_bwd_dims<F16>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, d_qk, d_v, ws, sp, st);
   } else if (d_qk != d_v) {
-    e = d_qk == 64 ? launch_bwd_f32<64, 128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st)
-                   : launch_bwd_f32<128, 64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st);
+    e = d_qk == 64 ? launch_bwd_f32<64, 128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st)
+                   : launch_bwd_f32<128, 64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st);
   } else {
     switch (d_qk) {
-      case 64: e = launch_bwd_f32<64, 64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      case 128: e = launch_bwd_f32<128, 128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      case 256: e = launch_bwd_f32<128, 128, 2>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      case 512: e = launch_bwd_f32<128, 128, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
-      default: e = launch_bwd_f32<256, 256, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, scale, causal, ws, sp, st); break;
+      case 64: e = launch_bwd_f32<64, 64, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st); break;
+      case 128: e = launch_bwd_f32<128, 128, 1>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st); break;
+      case 256: e = launch_bwd_f32<128, 128, 2>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st); break;
+      case 512: e = launch_bwd_f32<128, 128, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st); break;
+      default: e = launch_bwd_f32<256, 256, 4>(q, k, v, o, dout, lse, dq, dk, dv, bh, H, Nq, Nk, k_len, q_len, scale, causal, ws, sp, st); break;
     }
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -1247,7 +1261,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               float scale, int causal, int dtype, const int* k_len, void* workspace,
               size_t workspace_bytes, void* stream) {
   return fa_bwd_gen(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, d, scale, causal, dtype,
-                    k_len, workspace, workspace_bytes, stream);
+                    k_len, nullptr, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

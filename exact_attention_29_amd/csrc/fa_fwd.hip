@@ -136,8 +136,9 @@ template <class TT, int DK, int DV, bool CAUSAL, int NW, int NS, bool PERSIST, b
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV == 128 ? 3 : 2, DK + DV == 128 ? 3 : 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int Nq, int Nk, int H, const int* __restrict__ k_len, int n_qtiles, int total_items, int slot,
-    float scale, int n_split, float* __restrict__ Opart, float2* __restrict__ Lpart) {
+    int Nq, int Nk, int H, const int* __restrict__ k_len, const int* __restrict__ q_len,
+    int n_qtiles, int total_items, int slot, float scale, int n_split, float* __restrict__ Opart,
+    float2* __restrict__ Lpart) {
   static_assert(!(SPLIT && PERSIST), "a split launch has one workgroup per item");
   // DK: head dim of Q and K (the scores); DV: head dim of V and O
   constexpr int BR = 32 * NW, BC = 64;
@@ -175,10 +176,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     const int bh = wq / n_qtiles;
     int qt = wq % n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
-    // keys kept for query i: j < nk and, when causal, j <= i + diag (the last
-    // query row is aligned with the last valid key)
+    // keys kept for query i < nq: j < nk and, when causal, j <= i + diag (the
+    // last valid query row is aligned with the last valid key); rows from nq
+    // on are padding and keep no key
     const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;
-    const int diag = nk - Nq;
+    const int nq = q_len ? min(max(q_len[bh / H], 0), Nq) : Nq;
+    const int diag = nk - nq;
     const size_t qhead = (size_t)bh * Nq * DK, ohead = (size_t)bh * Nq * DV;
     const size_t khead = (size_t)bh * Nk * DK, vhead = (size_t)bh * Nk * DV;
     const int q_first = qt * BR + 32 * wave;
@@ -189,10 +192,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       const uint16_t* qrow = Q + qhead + (size_t)my_q * DK + 8 * hf;
 #pragma unroll
       for (int c = 0; c < DK / 16; ++c)
-        qf[c] = (my_q < Nq) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
+        qf[c] = (my_q < nq) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
     }
 
-    const int kv_end = CAUSAL ? min(nk, (qt + 1) * BR + diag) : nk;
+    const int kv_end = qt * BR >= nq ? 0 : CAUSAL ? min(nk, min((qt + 1) * BR, nq) + diag) : nk;
     const int T_all = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
     // this workgroup's tiles: [tile0, tile0 + T) of the block's T_all (all of
     // them unsplit); tile t below is key tile tile0 + t
@@ -200,11 +203,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     const int T = SPLIT ? (int)((long long)T_all * (split + 1) / n_split) - tile0 : T_all;
     const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
     const int my_T_all = CAUSAL ? (last_key < 0 ? 0 : min(T_all, last_key / BC + 1)) : T_all;
-    // A wave whose rows all lie past Nq (the ragged last block; a single
-    // decoding query leaves seven of eight waves so) only helps load the tiles
-    // and meets the barriers.  Not at d = 64, whose three-wave occupancy
-    // leaves no registers for the extra control flow.
-    const bool idle = DK + DV > 128 && q_first >= Nq;
+    // A wave whose rows all lie past nq (the ragged last block, padding; a
+    // single decoding query leaves seven of eight waves so) only helps load
+    // the tiles and meets the barriers.  Not at d = 64, whose three-wave
+    // occupancy leaves no registers for the extra control flow.
+    const bool idle = DK + DV > 128 && q_first >= nq;
     const int my_T = idle ? 0 : SPLIT ? min(T, max(0, my_T_all - tile0)) : my_T_all;
 
     const uint16_t* const kbase = K + khead;
@@ -487,7 +490,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       wait_keep(keep);
     }
     __syncthreads();
-    // Every wave with rows below Nq scores tile 0 when the block has one, even
+    // Every wave with rows below nq scores tile 0 when the block has one, even
     // a wave whose rows keep no key (causal, more queries than keys): its
     // scores are then all masked, so the steady steps below see -inf instead
     // of stale registers.  An idle wave runs no steady step at all.
@@ -548,8 +551,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     // touch 32 rows; instead each wave passes its normalised, rounded rows
     // through its own LDS area (the stage buffers are free after the last
     // barrier) and stores whole 128-byte row segments, 8 lanes per segment.
-    const float l_tot = half_sum(l_run);
-    const float lw_tot = half_sum(lw_run);
+    // a padding row (my_q >= nq) stores the empty sum: O = 0, lse = -inf
+    const bool pad = my_q >= nq;
+    const float l_tot = pad ? 0.f : half_sum(l_run);
+    const float lw_tot = pad ? 0.f : half_sum(lw_run);
     if constexpr (SPLIT) {
       // this share's output and weights, fp32, straight from the registers
       // (block b, register 4g+e of lane (q, h) is column 32b + 8g + 4h + e)
@@ -670,8 +675,8 @@ template <int DSL, int DSLV, int DS, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int H,
-    const int* __restrict__ k_len, int n_qtiles, int total_wg, float scale, int n_split, int tps,
-    float* __restrict__ Opart, float* __restrict__ LSEpart) {
+    const int* __restrict__ k_len, const int* __restrict__ q_len, int n_qtiles, int total_wg,
+    float scale, int n_split, int tps, float* __restrict__ Opart, float* __restrict__ LSEpart) {
   // D: head dim of Q and K (DSL columns per wave); DV: of V and O (DSLV per wave)
   constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSLV / 32, BC = 32;
   __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
@@ -685,7 +690,8 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   int qt = work % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;
   const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernel
-  const int diag = nk - Nq;
+  const int nq = q_len ? min(max(q_len[bh / H], 0), Nq) : Nq;
+  const int diag = nk - nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
   const size_t vhead = (size_t)bh * Nk * DV, ohead = (size_t)bh * Nq * DV;
   const int q_first = qt * 32;
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
 #pragma unroll
     for (int u = 0; u < DSL / 8; ++u)
-      qf[u] = (my_q < Nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+      qf[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
   }
   f32x16 o[NB];
 #pragma unroll
@@ -705,7 +711,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   // running state as in the 16-bit kernel: raw max, exponent reference, sum
   float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
   const float c2 = scale * kLog2e;
-  const int kv_end = CAUSAL ? min(nk, q_first + 32 + diag) : nk;
+  const int kv_end = q_first >= nq ? 0 : CAUSAL ? min(nk, min(q_first + 32, nq) + diag) : nk;
   const int ntiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
   const int j_begin = SPLIT ? split * tps : 0;
   const int j_end = SPLIT ? min(ntiles, j_begin + tps) : ntiles;
@@ -786,7 +792,8 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     }
   }
 
-  const float l_tot = half_sum(l_run);
+  const float l_sum = half_sum(l_run);
+  const float l_tot = my_q < nq ? l_sum : 0.f;  // a padding row: the empty sum
   if (my_q < Nq) {
     // a split may hold no kept key of this row: weight 0, lse -inf
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -853,10 +860,12 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
 // host side
 
 // Shape of one call: Nq query rows and Nk key rows per head, optional
-// per-batch valid key counts (device array, clamped to [0, Nk] on the GPU).
+// per-batch valid key and query counts (device arrays, clamped to [0, Nk]
+// and [0, Nq] on the GPU).
 struct Shape {
   int BH, H, Nq, Nk;
   const int* k_len;
+  const int* q_len = nullptr;
 };
 
 // Key-split plan for grids too small to fill the GPU.  fp32: about one
@@ -921,12 +930,12 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
     if (causal)
       hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, false, true>), grid, block, 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o,
-                         lse, sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, 0, scale, plan.n_split,
+                         lse, sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, 0, scale, plan.n_split,
                          opart, lpart);
     else
       hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, false, true>), grid, block, 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o,
-                         lse, sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, 0, scale, plan.n_split,
+                         lse, sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, 0, scale, plan.n_split,
                          opart, lpart);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     constexpr int RPB = 256 / (DV / 8);
@@ -947,11 +956,11 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   if (causal)
     hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, PERSIST, false>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale, 1, nullptr, nullptr);
+                       sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, slot, scale, 1, nullptr, nullptr);
   else
     hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, PERSIST, false>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       sh.Nq, sh.Nk, sh.H, sh.k_len, nq, total, slot, scale, 1, nullptr, nullptr);
+                       sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, slot, scale, 1, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -969,11 +978,11 @@ hipError_t launch32(const void* q, const void* k, const void* v, void* o, float*
     if (causal)
       hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, true, true>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
-                         sh.k_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
+                         sh.k_len, sh.q_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
     else
       hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, false, true>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
-                         sh.k_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
+                         sh.k_len, sh.q_len, nq, total, scale, plan.n_split, plan.tps, opart, lpart);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     constexpr int RPB = D / 4 >= 256 ? 1 : 256 / (D / 4);
     const int rows = sh.BH * sh.Nq;
@@ -987,11 +996,11 @@ hipError_t launch32(const void* q, const void* k, const void* v, void* o, float*
   if (causal)
     hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, true, false>), grid, block, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
-                       sh.k_len, nq, total, scale, 1, 0, nullptr, nullptr);
+                       sh.k_len, sh.q_len, nq, total, scale, 1, 0, nullptr, nullptr);
   else
     hipLaunchKernelGGL((attn_fwd_f32<DSL, DSLV, DS, false, false>), grid, block, 0, st, (const float*)q,
                        (const float*)k, (const float*)v, (float*)o, lse, sh.Nq, sh.Nk, sh.H,
-                       sh.k_len, nq, total, scale, 1, 0, nullptr, nullptr);
+                       sh.k_len, sh.q_len, nq, total, scale, 1, 0, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -1099,12 +1108,13 @@ size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal,
 
 int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Nq, int Nk, int d_qk, int d_v, float scale, int causal, int dtype,
-               const int* k_len, void* workspace, size_t workspace_bytes, void* stream) {
+               const int* k_len, const int* q_len, void* workspace, size_t workspace_bytes,
+               void* stream) {
   if (int err = check_args(q, k, v, o, lse, B, H, Nq, Nk, d_qk, d_v, scale, causal, dtype);
       err != FA_OK)
     return err;
-  if (((uintptr_t)k_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
-  const Shape sh{B * H, H, Nq, Nk, k_len};
+  if (((uintptr_t)k_len & 3u) != 0 || ((uintptr_t)q_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  const Shape sh{B * H, H, Nq, Nk, k_len, q_len};
   if (workspace == nullptr || workspace_bytes == 0)
     return dispatch(q, k, v, o, lse, sh, d_qk, d_v, scale, causal, dtype, SplitPlan{}, nullptr,
                     stream);
@@ -1117,8 +1127,8 @@ int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int Nq, int Nk, int d, float scale, int causal, int dtype, const int* k_len,
               void* workspace, size_t workspace_bytes, void* stream) {
-  return fa_fwd_gen(q, k, v, o, lse, B, H, Nq, Nk, d, d, scale, causal, dtype, k_len, workspace,
-                    workspace_bytes, stream);
+  return fa_fwd_gen(q, k, v, o, lse, B, H, Nq, Nk, d, d, scale, causal, dtype, k_len, nullptr,
+                    workspace, workspace_bytes, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -1148,6 +1158,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 300; }
+int fa_version(void) { return 400; }
 
 }  // extern "C"

@@ -168,14 +168,23 @@ size_t fa_fwd_ex_workspace_size(int B, int H, int Nq, int Nk, int d, int causal,
  *   o : [B][H][Nq][d_v];   lse : [B][H][Nq] fp32.
  * Supported pairs: fa_fwd_gen_supported (d_qk = d_v as for fa_fwd; otherwise
  * d_qk, d_v in {64, 128} for bf16, fp16 and fp32).  The workspace is sized by
- * fa_fwd_gen_workspace_size.  Everything else is as for fa_fwd_ex, which is
- * fa_fwd_gen with d_qk = d_v = d.  scale is the caller's (1/sqrt(d_qk) is the
- * usual choice).
+ * fa_fwd_gen_workspace_size.
+ *   q_len : per-batch padding of the queries too (the same padding mask):
+ *           device pointer to B int32 valid query counts (4-byte aligned; each
+ *           clamped to [0, Nq] when read), or NULL for Nq.  With Lq the
+ *           batch's count and L its key count, query row i < Lq keeps key j
+ *           iff j < L and, when causal, j <= i + (L - Lq): the last valid
+ *           query is aligned with the last valid key.  A row at or past Lq is
+ *           padding: O = 0, lse = -inf, and its q row is never read.  NULL
+ *           gives fa_fwd_ex's rule (Lq = Nq).
+ * Everything else is as for fa_fwd_ex, which is fa_fwd_gen with
+ * d_qk = d_v = d and q_len = NULL.  scale is the caller's (1/sqrt(d_qk) is
+ * the usual choice).
  */
 int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int Nq, int Nk, int d_qk, int d_v, float scale, int causal,
-               int dtype, const int* k_len, void* workspace, size_t workspace_bytes,
-               void* stream);
+               int dtype, const int* k_len, const int* q_len, void* workspace,
+               size_t workspace_bytes, void* stream);
 
 /* fa_fwd_ex_workspace_size for fa_fwd_gen's shapes (0: none needed, or invalid). */
 size_t fa_fwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v, int causal,
@@ -272,13 +281,15 @@ int fa_bwd_supported(int d, int dtype, int causal);
  * d_v columns; the scores, dq and dk the d_qk columns.  Supported pairs:
  * fa_bwd_gen_supported (d_qk = d_v as for fa_bwd; otherwise d_qk, d_v in
  * {64, 128} for bf16, fp16 and fp32).  The workspace must hold
- * fa_bwd_gen_workspace_size(...) bytes.  Everything else is as for fa_bwd_ex,
- * which is fa_bwd_gen with d_qk = d_v = d.
+ * fa_bwd_gen_workspace_size(...) bytes.  q_len as for fa_fwd_gen: a padding
+ * query row (i >= Lq) gets dq = 0 and adds nothing to dk, dv; its q, o, dout
+ * and lse entries are never read.  Everything else is as for fa_bwd_ex,
+ * which is fa_bwd_gen with d_qk = d_v = d and q_len = NULL.
  */
 int fa_bwd_gen(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
                int d_qk, int d_v, float scale, int causal, int dtype, const int* k_len,
-               void* workspace, size_t workspace_bytes, void* stream);
+               const int* q_len, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace of fa_bwd_gen (as fa_bwd_ex_workspace_size, for both head dims). */
 size_t fa_bwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v, int causal,
@@ -293,7 +304,7 @@ int fa_fwd_supported(int d, int dtype, int causal);
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* fa_status_string(int status);
 
-/* Library version, major*10000 + minor*100 + patch (300: 0.3.0). */
+/* Library version, major*10000 + minor*100 + patch (400: 0.4.0). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -210,11 +210,12 @@ def test_bwd_ex_checks_arguments_first():
 # ------------------------------------------------------------------ value head dim of its own
 def call_gen(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=16, Nk=40, d_qk=64, d_v=128,
-             scale=0.125, causal=0, dtype=fa.FA_DTYPE_BF16, k_len=None, ws=None, ws_bytes=0)
+             scale=0.125, causal=0, dtype=fa.FA_DTYPE_BF16, k_len=None, q_len=None, ws=None,
+             ws_bytes=0)
     a.update(kw)
     return fa.fa_fwd_gen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
                          a["Nk"], a["d_qk"], a["d_v"], a["scale"], a["causal"], a["dtype"],
-                         a["k_len"], a["ws"], a["ws_bytes"], None)
+                         a["k_len"], a["q_len"], a["ws"], a["ws_bytes"], None)
 
 
 def test_gen_supported_table():
@@ -236,7 +237,7 @@ def test_gen_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(d_v=256), dict(d_qk=96), dict(dtype=7), dict(v=FAKE + 8),
-                                dict(k_len=FAKE + 2)])
+                                dict(k_len=FAKE + 2), dict(q_len=FAKE + 1)])
 def test_gen_unsupported_configurations(kw):
     assert call_gen(**kw) == fa.FA_ERR_UNSUPPORTED
 
@@ -262,18 +263,18 @@ def test_bwd_gen_table_and_workspace():
     assert fa.fa_bwd_gen_workspace_size(2, 3, 100, 50, 64, 128, 1, fa.FA_DTYPE_BF16) == 2 * 6 * 128 * 4
     base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
                 B=1, H=1, Nq=16, Nk=40, d_qk=64, d_v=128, scale=0.125, causal=0,
-                dtype=fa.FA_DTYPE_BF16, k_len=None, ws=FAKE, ws_bytes=1 << 20)
+                dtype=fa.FA_DTYPE_BF16, k_len=None, q_len=None, ws=FAKE, ws_bytes=1 << 20)
 
     def run(**kw):
         a = dict(base)
         a.update(kw)
         return fa.fa_bwd_gen(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"],
                              a["dk"], a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["d_qk"],
-                             a["d_v"], a["scale"], a["causal"], a["dtype"], a["k_len"], a["ws"],
-                             a["ws_bytes"], None)
+                             a["d_v"], a["scale"], a["causal"], a["dtype"], a["k_len"],
+                             a["q_len"], a["ws"], a["ws_bytes"], None)
     for kw in (dict(d_v=0), dict(Nk=0), dict(dv=None), dict(ws=None), dict(ws_bytes=4)):
         assert run(**kw) == fa.FA_ERR_INVALID_ARG, kw
-    for kw in (dict(d_v=256), dict(d_qk=32), dict(dtype=4), dict(v=FAKE + 4)):
+    for kw in (dict(d_v=256), dict(d_qk=32), dict(dtype=4), dict(v=FAKE + 4), dict(q_len=FAKE + 2)):
         assert run(**kw) == fa.FA_ERR_UNSUPPORTED, kw
 
 

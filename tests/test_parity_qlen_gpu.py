@@ -1,0 +1,146 @@
+"""GPU parity for per-batch query counts (q_len): fa_fwd_gen and fa_bwd_gen
+(through the C ABI, via attention() and attention_bwd()) against the fp64
+oracle with the same counts, element by element.
+
+A padding query row (i >= the batch's count) keeps no key: O = 0, lse = -inf
+and dq = 0 exactly, and it adds nothing to dk, dv.  The causal diagonal
+aligns each batch's last valid query with its last valid key.  The padding
+rows of q, o, dout and lse are filled with NaN before the calls: the kernels
+must never read them, so every output stays finite.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_29_amd as fa
+import oracle
+from exact_attention_29_amd.inputs import make_dout, make_qkv
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU; run with -m 'not gpu' on a CPU host"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def inputs(B, H, Nq, Nk, dk, dv, dt, seed):
+    q, k, _ = make_qkv(B, H, max(Nq, Nk), dk, dt, seed)
+    _, _, v = make_qkv(B, H, Nk, dv, dt, seed + 1)
+    g = make_dout(B, H, Nq, dv, dt, seed + 2)
+    return q[:, :, :Nq].contiguous(), k[:, :, :Nk].contiguous(), v, g
+
+
+def poison(x, q_len):
+    """Device copy of x with every padding query row set to NaN."""
+    y = x.clone()
+    for b, L in enumerate(q_len):
+        y[b, :, max(L, 0):] = float("nan")
+    return y
+
+
+def grad_errors(got, ref):
+    g = got.detach().to("cpu").double().numpy().reshape(ref.shape)
+    d = np.abs(g - ref)
+    big = max(float(np.abs(ref).max()), 1e-2)
+    return dict(max_rel=float(d.max()) / big, mean_rel=float(d.mean()) / big,
+                finite=bool(np.isfinite(g).all()))
+
+
+def check_grad(stats, dtype, name):
+    tol = parity.TOL_BWD[dtype]
+    assert stats["finite"], (name, stats)
+    assert stats["max_rel"] <= tol["max_rel"], (name, stats, tol)
+    assert stats["mean_rel"] <= tol["mean_rel"], (name, stats, tol)
+
+
+def run_case(dt, dk, dv, B, H, Nq, Nk, q_len, k_len, causal, seed):
+    q, k, v, g = inputs(B, H, Nq, Nk, dk, dv, dt, seed)
+    scale = 1 / math.sqrt(dk)
+    ql = torch.tensor(q_len, dtype=torch.int32, device="cuda")
+    kl = None if k_len is None else torch.tensor(k_len, dtype=torch.int32, device="cuda")
+    qc = poison(q.cuda(), q_len)
+    o, lse = fa.attention(qc, k.cuda(), v.cuda(), causal=causal, scale=scale, k_len=kl, q_len=ql)
+    torch.cuda.synchronize()
+    # forward against the oracle
+    o_ref, l_ref = oracle.attn_rows_ex(q, k, v, scale, causal, None, k_len, q_len=q_len)
+    og = o.double().cpu().reshape(-1, dv).numpy()
+    lg = lse.double().cpu().reshape(-1).numpy()
+    empty = np.isneginf(l_ref)
+    assert np.all(og[empty] == 0) and np.all(np.isneginf(lg[empty])), "rows that keep no key"
+    assert np.isfinite(og).all() and np.isfinite(lg[~empty]).all()
+    if (~empty).any():
+        do = np.abs(og[~empty] - o_ref[~empty])
+        parity.check(dict(max_o=float(do.max()), mean_o=float(do.mean()),
+                          max_lse=float(np.abs(lg[~empty] - l_ref[~empty]).max()), finite=True,
+                          rows=int((~empty).sum())), DT[dt])
+    # gradients, with the padding rows of every query-side input poisoned
+    dq, dkk, dvv = fa.attention_bwd(qc, k.cuda(), v.cuda(), poison(o, q_len), poison(lse, q_len),
+                                    poison(g.cuda(), q_len), causal=causal, scale=scale,
+                                    k_len=kl, q_len=ql)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd_ex(q, k, v, g, scale, causal, k_len, q_len=q_len)
+    for name, got, ref in (("dq", dq, rq), ("dk", dkk, rk), ("dv", dvv, rv)):
+        check_grad(grad_errors(got, ref), DT[dt], name)
+    for b, L in enumerate(q_len):
+        assert torch.all(dq[b, :, max(L, 0):] == 0), "padding rows have dq = 0"
+
+
+SHAPES = [  # Nq, Nk, q_len, k_len
+    (300, 300, [300, 77, 0], None),
+    (190, 333, [1, 190, 64], [333, 150, 0]),
+    (257, 100, [257, 256, 129], [100, 99, 1]),
+    (64, 700, [63, 1, 64], None),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128)])
+@pytest.mark.parametrize("Nq,Nk,q_len,k_len", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_query_counts_match_oracle(dt, dk, dv, Nq, Nk, q_len, k_len, causal):
+    run_case(dt, dk, dv, 3, 2, Nq, Nk, q_len, k_len, causal,
+             9000 + Nq + 3 * Nk + dk + 2 * dv + int(causal))
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64), ("fp32", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_grids_split_with_query_counts(dt, d, causal):
+    """One head, few query rows, many keys: the forward splits the keys and
+    the gradients split the blocks' tiles; padding rows stay exact zeros."""
+    B, H, Nq, Nk = 2, 1, 300, 3000
+    assert fa.fa_fwd_gen_workspace_size(B, H, Nq, Nk, d, d, int(causal),
+                                        fa._native._DTYPE_CODE[DT[dt]]) > 0
+    run_case(dt, d, d, B, H, Nq, Nk, [200, 300], [3000, 2100], causal, 9500 + d + int(causal))
+
+
+def test_full_counts_equal_the_call_without_counts():
+    """q_len = Nq for every batch is the ordinary call, bit for bit."""
+    B, H, Nq, Nk, d = 2, 4, 333, 555, 128
+    q, k, v, g = (t.cuda() for t in inputs(B, H, Nq, Nk, d, d, "bf16", 9900))
+    kl = torch.tensor([555, 300], dtype=torch.int32, device="cuda")
+    ql = torch.full((B,), Nq, dtype=torch.int32, device="cuda")
+    for causal in (False, True):
+        a = fa.attention(q, k, v, causal=causal, k_len=kl)
+        b = fa.attention(q, k, v, causal=causal, k_len=kl, q_len=ql)
+        ga = fa.attention_bwd(q, k, v, a[0], a[1], g, causal=causal, k_len=kl)
+        gb = fa.attention_bwd(q, k, v, b[0], b[1], g, causal=causal, k_len=kl, q_len=ql)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+        for x, y in zip(ga, gb):
+            assert torch.equal(x, y)
+
+
+def test_bad_counts_are_rejected():
+    q = torch.zeros(2, 1, 16, 64, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q, q_len=torch.tensor([1], dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q, q_len=torch.tensor([1, 2], dtype=torch.int64, device="cuda"))
