@@ -869,7 +869,10 @@ struct Shape {
 };
 
 // Key-split plan for grids too small to fill the GPU.  fp32: about one
-// workgroup per CU, at least 4 key tiles (of 32) per split, `tps` tiles each.
+// workgroup per CU, at least one key tile (of 32) per split, `tps` tiles each
+// (its kernel runs one dependent chain of products per tile, so a tiny grid
+// is latency-bound and gains even from one-tile ranges: 20.6 -> 12.1 us on
+// one head of 128 rows at d = 64).
 // 16-bit: about as many workgroups as the CUs hold at once (one at d = 128,
 // three at d = 64), at least 4 key tiles (of 64) per share, each query
 // block's tiles cut into n_split equal shares.  n_split = 1: none.
@@ -886,7 +889,7 @@ SplitPlan plan_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype) {
   if (dtype == FA_DTYPE_FP32) {
     const long long items = (long long)((Nq + 31) / 32) * BH, ntiles = (Nk + 31) / 32;
     if (items >= cus) return p;
-    long long sp = std::min<long long>((cus + items - 1) / items, ntiles / 4);
+    long long sp = std::min<long long>((cus + items - 1) / items, ntiles);
     if (sp < 2) return p;
     p.tps = (int)((ntiles + sp - 1) / sp);
     p.n_split = (int)((ntiles + p.tps - 1) / p.tps);

@@ -83,6 +83,20 @@ def test_key_split_matches_oracle_and_unsplit_path(d, causal):
     assert torch.equal(o_s, o_s2) and torch.equal(l_s, l_s2)
 
 
+def test_tiny_fp32_grids_split_into_single_tiles():
+    """Workload 1's shape (one head, 128 rows, d = 64): four key ranges of one
+    32-key tile each, merged; it must match the oracle and the unsplit path."""
+    q, k, v = make_qkv(1, 1, 128, 64, "fp32", 77)
+    assert fa.fa_fwd_workspace_size(1, 1, 128, 64, 0, fa.FA_DTYPE_FP32) == 4 * 128 * 65 * 4
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    for causal in (False, True):
+        o_s, l_s = fa.attention(qc, kc, vc, causal=causal)
+        o_u, l_u = fa.attention(qc, kc, vc, causal=causal, split_keys=False)
+        torch.cuda.synchronize()
+        parity.check(parity.compare(o_s, l_s, q, k, v, 0.125, causal), torch.float32)
+        assert (o_s - o_u).abs().max().item() <= 2e-6 and (l_s - l_u).abs().max().item() <= 2e-6
+
+
 def test_workspace_size_and_rejection():
     """No workspace for grids that fill the GPU; a workspace smaller than the
     reported size is rejected before anything is written."""
