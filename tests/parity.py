@@ -7,13 +7,14 @@ import torch
 import oracle
 
 # Tolerances on |O_gpu - O_oracle| and |lse_gpu - lse_oracle| (all in fp64).
-# bf16 and fp32 are the stated bounds of the workload definitions; fp16 has
-# three more mantissa bits than bf16 (probabilities and outputs round 8x
-# finer), so its bound is taken 2x tighter than bf16's to stay well clear of
-# its rounding while still catching any real error.
+# bf16 and fp32 are the stated bounds of the workload definitions.  fp16 has
+# three more mantissa bits than bf16, so the roundings of P and O -- the
+# error of the 16-bit path -- are 8x finer, and its O bounds are bf16's
+# divided by 8 (measured: fp16 errors run 8-9x below bf16's on the same
+# shapes, max |dO| at most 1e-3); the lse bound is the fp32 statistics' own.
 TOL = {
     torch.bfloat16: dict(max_o=2e-2, mean_o=2e-3, max_lse=1e-3),
-    torch.float16: dict(max_o=1e-2, mean_o=1e-3, max_lse=1e-3),
+    torch.float16: dict(max_o=2.5e-3, mean_o=2.5e-4, max_lse=1e-3),
     torch.float32: dict(max_o=1e-4, mean_o=1e-4, max_lse=1e-3),
 }
 
