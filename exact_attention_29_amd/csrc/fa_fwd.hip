@@ -188,12 +188,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     const int my_q = q_first + lq;
 
     u32x4 qf[DK / 16];
-    {
-      const uint16_t* qrow = Q + qhead + (size_t)my_q * DK + 8 * hf;
-#pragma unroll
-      for (int c = 0; c < DK / 16; ++c)
-        qf[c] = (my_q < nq) ? *(const u32x4*)(qrow + 16 * c) : u32x4{0, 0, 0, 0};
-    }
 
     const int kv_end = qt * BR >= nq ? 0 : CAUSAL ? min(nk, min((qt + 1) * BR, nq) + diag) : nk;
     const int T_all = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
@@ -482,6 +476,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
 #pragma unroll
     for (int st = 0; st <= NS - 2; ++st)
       if (st < T) load_stage(st);
+    // Q after the first stages: its latency overlaps theirs
+    if (my_q < nq) {
+      const uint16_t* qrow = Q + qhead + (size_t)my_q * DK + 8 * hf;
+#pragma unroll
+      for (int c = 0; c < DK / 16; ++c) qf[c] = *(const u32x4*)(qrow + 16 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < DK / 16; ++c) qf[c] = u32x4{0, 0, 0, 0};
+    }
     // stages -1 and 0 must be in; stages 1 .. NS-2 may stay in flight
     {
       int keep = 0;
