@@ -84,7 +84,7 @@ def test_key_split_matches_oracle_and_unsplit_path(d, causal):
 
 
 def test_tiny_fp32_grids_split_into_single_tiles():
-    """Workload 1's shape (one head, 128 rows, d = 64): four key ranges of one
+    """The single-head fp32 shape (one head, 128 rows, d = 64): four key ranges of one
     32-key tile each, merged; it must match the oracle and the unsplit path."""
     q, k, v = make_qkv(1, 1, 128, 64, "fp32", 77)
     assert fa.fa_fwd_workspace_size(1, 1, 128, 64, 0, fa.FA_DTYPE_FP32) == 4 * 128 * 65 * 4
