@@ -163,7 +163,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   // (lw) in the d = 128 arrangement, where those 16 packed adds per tile
   // cost nothing measurable; at d = 64 the vector unit, not the matrix core,
   // bounds the kernel, and dividing by the fp32 sum l of the unrounded
-  // weights -- the normaliser of the online softmax as the pages write it --
+  // weights -- the running denominator of the online softmax ("Deep
+  // Learning - Flash Attention", "An Example", the final division by l) --
   // is 8-9% faster.
   constexpr bool LW = DK + DV > 128;
   // Work loop.  Persistent: the workgroup claims items until none is left;
