@@ -1006,9 +1006,13 @@ BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype)
   BwdSplit p;
   int cus = 0;
   if (compute_units(&cus) != hipSuccess) return p;
+  // at least two tiles per share for the 16-bit kernels; one for fp32, whose
+  // small grids are latency-bound (one head of 256 rows at d = 128:
+  // 64.5 -> 48.4 us against two-tile shares)
   auto pick = [&](long long blocks, long long tiles, long long slots) {
     if (blocks >= slots) return 1;
-    const long long sp = std::min<long long>((slots + blocks - 1) / blocks, tiles / 2);
+    const long long per = dtype == FA_DTYPE_FP32 ? tiles : tiles / 2;
+    const long long sp = std::min<long long>((slots + blocks - 1) / blocks, per);
     return sp < 2 ? 1 : (int)sp;
   };
   if (dtype == FA_DTYPE_FP32) {  // 32-row blocks of keys and of queries, one workgroup per CU
