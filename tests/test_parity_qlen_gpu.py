@@ -144,3 +144,22 @@ def test_bad_counts_are_rejected():
         fa.attention(q, q, q, q_len=torch.tensor([1], dtype=torch.int32, device="cuda"))
     with pytest.raises(ValueError):
         fa.attention(q, q, q, q_len=torch.tensor([1, 2], dtype=torch.int64, device="cuda"))
+
+
+def test_counts_out_of_range_are_clamped():
+    """A negative count acts as 0 and one past Nq as Nq (the kernels clamp
+    what they read; the library cannot check device data before a launch)."""
+    B, H, Nq, Nk, d = 2, 2, 200, 300, 64
+    q, k, v, g = (t.cuda() for t in inputs(B, H, Nq, Nk, d, d, "bf16", 9950))
+    wild = torch.tensor([-5, Nq + 100], dtype=torch.int32, device="cuda")
+    tame = torch.tensor([0, Nq], dtype=torch.int32, device="cuda")
+    for causal in (False, True):
+        a = fa.attention(q, k, v, causal=causal, q_len=wild)
+        b = fa.attention(q, k, v, causal=causal, q_len=tame)
+        ga = fa.attention_bwd(q, k, v, a[0], a[1], g, causal=causal, q_len=wild)
+        gb = fa.attention_bwd(q, k, v, b[0], b[1], g, causal=causal, q_len=tame)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+        assert torch.all(a[0][0] == 0) and torch.all(torch.isneginf(a[1][0]))
+        for x, y in zip(ga, gb):
+            assert torch.equal(x, y)
