@@ -694,6 +694,13 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   // D: head dim of Q and K (DSL columns per wave); DV: of V and O (DSLV per wave)
   constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSLV / 32, BC = 32;
   __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
+  // Each wave's Q slice (32 rows x DSL columns) lives in LDS, not in
+  // registers: the registers it frees hold the next key tile's K and the
+  // current tile's V while they load, so that both loads overlap products.
+  // Row q's 16-byte chunk c sits in slot c ^ (q % 16): the 16 rows one
+  // 16-lane group reads fall in 16 distinct bank groups.
+  static_assert(DSL >= 64, "the chunk swizzle needs 16 chunks per row");
+  __shared__ __attribute__((aligned(16))) float qsm[DS * 32 * DSL];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane & 31, hf = lane >> 5;
@@ -712,12 +719,13 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int my_q = q_first + lq;
   const int col0 = wave * DSL, colv0 = wave * DSLV;
 
-  f32x4 qf[DSL / 8];
+  float* const qw = qsm + wave * 32 * DSL + lq * DSL;  // this lane's Q row in LDS
+  auto qslot = [&](int u) { return qw + 4 * ((2 * u + hf) ^ (lq & 15)); };
   {
     const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
 #pragma unroll
     for (int u = 0; u < DSL / 8; ++u)
-      qf[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+      *(f32x4*)qslot(u) = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
   }
   f32x16 o[NB];
 #pragma unroll
@@ -730,20 +738,49 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int j_begin = SPLIT ? split * tps : 0;
   const int j_end = SPLIT ? min(ntiles, j_begin + tps) : ntiles;
 
+  // K rows of tile j: lane (key, h) holds K[k0 + key][col0 + 8u + 4h .. +3]
+  f32x4 kf[DSL / 8];
+  auto load_k = [&](int j) {
+    const int key = j * BC + lq;
+    const float* krow = K + khead + (size_t)key * D + col0 + 4 * hf;
+#pragma unroll
+    for (int u = 0; u < DSL / 8; ++u) kf[u] = key < nk ? *(const f32x4*)(krow + 8 * u) : f32x4{0, 0, 0, 0};
+  };
+  if (j_begin < j_end) load_k(j_begin);
   for (int j = j_begin; j < j_end; ++j) {
     const int k0 = j * BC;
-    // partial S^T over this wave's columns
-    f32x16 s = f32x16{};
-    {
-      const int key = k0 + lq;
-      const float* krow = K + khead + (size_t)key * D + col0 + 4 * hf;
+    // V rows of tile j, requested before the score products so that they
+    // arrive while those run: step r takes key 8(r/4) + 4h + r%4
+    float vv[16][NB];
 #pragma unroll
-      for (int u = 0; u < DSL / 8; ++u) {
-        const f32x4 kv = key < nk ? *(const f32x4*)(krow + 8 * u) : f32x4{0, 0, 0, 0};
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const float* vrow = V + vhead + (size_t)key * DV + colv0 + NB * lq;
+      if (key < nk) {
+        if constexpr (NB == 4) {
+          const f32x4 t = *(const f32x4*)vrow;
+          vv[r][0] = t[0]; vv[r][1] = t[1]; vv[r][2] = t[2]; vv[r][3] = t[3];
+        } else if constexpr (NB == 2) {
+          const f32x2 t = *(const f32x2*)vrow;
+          vv[r][0] = t[0]; vv[r][1] = t[1];
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[v], qf[u][v], s, 0, 0, 0);
+          for (int b = 0; b < NB; ++b) vv[r][b] = vrow[b];
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) vv[r][b] = 0.f;
       }
     }
+    // partial S^T over this wave's columns
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int u = 0; u < DSL / 8; ++u) {
+      const f32x4 qa = *(const f32x4*)qslot(u);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[u][v], qa[v], s, 0, 0, 0);
+    }
+
     if (DS > 1) {  // full scores = sum of the DS partials, in wave order
       red[wave * 64 + lane] = s;
       __syncthreads();
@@ -780,29 +817,13 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     mc_run = mc_new;
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] *= alpha;
-    // O^T += V^T P^T
+    // O^T += V^T P^T; the next tile's K is requested halfway, once the
+    // first half of V's registers are free
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float* vrow = V + vhead + (size_t)key * DV + colv0 + NB * lq;
-      float vv[NB];
-      if (key < nk) {
-        if constexpr (NB == 4) {
-          const f32x4 t = *(const f32x4*)vrow;
-          vv[0] = t[0]; vv[1] = t[1]; vv[2] = t[2]; vv[3] = t[3];
-        } else if constexpr (NB == 2) {
-          const f32x2 t = *(const f32x2*)vrow;
-          vv[0] = t[0]; vv[1] = t[1];
-        } else {
+      if (r == 8 && j + 1 < j_end) load_k(j + 1);
 #pragma unroll
-          for (int b = 0; b < NB; ++b) vv[b] = vrow[b];
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) vv[b] = 0.f;
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[b], s[r], o[b], 0, 0, 0);
+      for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][b], s[r], o[b], 0, 0, 0);
     }
   }
 
