@@ -44,7 +44,7 @@ def gpu():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("i", range(36))
+@pytest.mark.parametrize("i", range(96))
 def test_random_case_matches_oracle(i):
     dt, B, H, Nq, Nk, dk, dv, causal, k_len, q_len, scale = draw(i)
     print("case", i, dict(dt=dt, B=B, H=H, Nq=Nq, Nk=Nk, dk=dk, dv=dv, causal=causal,
