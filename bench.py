@@ -1,10 +1,15 @@
 """Benchmark: attention forward TFLOPS and fraction of the MI355X bf16 MFMA peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--pass fwd|bwd]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--pass fwd|bwd]
 
 A step is one fa_fwd call (the whole forward pass) over one batch of the
-workload, inputs already resident in device memory.  W untimed steps, then K
-timed steps between two synchronizations; one JSON line on stdout.
+workload, inputs already resident in device memory.  The default workload is
+the largest single-GPU one: causal bf16, B=1, H=32, N=65536, d=128, with 1% of
+the key rows scaled by 8.  W untimed steps, then K timed steps between two
+synchronizations; one JSON line on stdout.  Before every timed step a 1 GiB
+device buffer is cleared on the launch stream, outside the step's HIP-event
+pair, so that no step starts with the previous step's data in L2 or the
+256 MB MALL (--no-flush turns this off).
 
 --pass bwd times the gradients instead: one fa_bwd call (its three kernels)
 per step, with the forward outputs O, lse and a seeded dL/dO resident, counted
@@ -146,6 +151,18 @@ def gemm_reference(n: int, steps: int = 20) -> None:
                       "steps": steps}))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s: float, seed: int = 0):
     """Time the oracle on a seeded uniform sample of rows sized to ~target_s."""
     import oracle
@@ -180,6 +197,7 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s: float, seed: int = 0):
               "max_abs_lse": float(np.abs(lg - l_ref).max())}
     return {
         "value": fl / secs / 1e12, "unit": "TFLOPS", "cores": int(nt), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{len(rows)} of {total_rows} query rows of the workload, seeded uniform "
                    f"over batch, head and position; FLOPs counted 4*|keys kept|*d per row; "
                    f"{secs:.1f} s of oracle time"),
@@ -210,7 +228,7 @@ def cpu_baseline_bwd(w, q, k, v, g, dq, dk, dv, target_s: float):
             break
     return {
         "value": heads * per_head / secs / 1e12, "unit": "TFLOPS", "cores": int(nt),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": cpu_model(),
         "sample": (f"all rows of {heads} of {B * H} heads of the workload (dq, dk, dv), FLOPs "
                    f"counted 10*N^2*d per head{' halved for causal' if w.causal else ''}; "
                    f"{secs:.1f} s of oracle time"),
@@ -223,7 +241,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not clear a 1 GiB buffer before each timed step")
     ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -278,16 +298,27 @@ def main() -> int:
             fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
         flops = w.flops
 
+    # L2 and MALL eviction between timed steps: clearing 1 GiB (4x the MALL)
+    # on the launch stream, outside each step's event pair
+    flush_buf = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            with torch.cuda.stream(stream):
+                flush_buf.zero_()
+
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize(dev)
 
-    # timed region: K steps; a HIP event pair around every launch on its stream
+    # timed region: K steps; a HIP event pair around every step on its stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for a, b in ev:
+        flush()
         a.record(stream)
         step()
         b.record(stream)
@@ -296,7 +327,10 @@ def main() -> int:
     per_launch = [a.elapsed_time(b) for a, b in ev]
     kernel_ms = float(np.mean(per_launch))
 
-    ms_per_step = wall * 1e3 / args.steps
+    # the step time is the event-timed step (the flush between steps is not
+    # part of the step); the wall time of the whole timed loop, flushes
+    # included, is reported beside it
+    ms_per_step = kernel_ms if flush_buf is not None else wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype in ("bf16", "fp16") else PEAK_FP32_TFLOPS
@@ -313,7 +347,9 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) per the workload recipe)",
         "config": {**w.as_dict(), "pass": args.pass_, "flops_per_step": flops,
-                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "l2_mall_flush_between_steps": flush_buf is not None,
+                   "wall_ms_per_step_incl_flush": round(wall * 1e3 / args.steps, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 4),

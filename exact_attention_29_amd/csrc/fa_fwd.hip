@@ -56,19 +56,94 @@ using namespace fa_dev;
 // blocks of one head go to one XCD's L2, longest first.  A workgroup takes
 // the next unclaimed item of its own XCD's range with an atomic counter, and
 // once that range is exhausted takes items from the other ranges, so no XCD
-// idles while another still has work.  Each launch uses one of kWorkSlots
-// counter sets (round-robin on the host), so launches that run concurrently
-// on different streams do not share counters; the last workgroup of a launch
-// clears its set for the launch that next uses it.  (More than kWorkSlots
-// launches in flight at once, or one captured launch replayed concurrently
-// with itself, would share a set.)
+// idles while another still has work.
+//
+// The counters live in one of kWorkSlots slots in the code object, chosen
+// round-robin by the host.  A slot belongs to one launch at a time: the
+// launch's tag (a hash of its dispatch packet's address and its dispatch id,
+// which together differ between any two launches in flight) is stored in
+// the slot's state word beside a count of the workgroups using it.  A
+// workgroup that finds the slot free or owned by its own launch joins it and
+// claims items from its counters; the last one to leave clears the counters,
+// records the tag as finished and frees the slot.  A workgroup that finds
+// the slot owned by another launch (a captured launch replayed beside a
+// later call that drew the same slot, or more than kWorkSlots launches in
+// flight) does not touch the counters: it runs the items of its own id,
+// blockIdx.x, blockIdx.x + gridDim.x, ..., so that its launch's items are
+// all computed whether or not any of its workgroups got the slot (an item
+// computed twice is written twice with the same bits).  A workgroup that
+// arrives after its launch has already finished every item exits.
 constexpr int kWorkSlots = 64;
-__device__ unsigned g_next_rank[kWorkSlots][8];  // per XCD: next item rank to hand out
-__device__ unsigned g_done_wg[kWorkSlots];       // workgroups that have left the launch
+struct WorkSlot {
+  unsigned long long state;     // tag << 16 | workgroups using the slot; 0 when free
+  unsigned long long done_tag;  // tag of the last launch that finished in this slot
+  unsigned next_rank[8];        // per XCD: next item rank to hand out
+};
+__device__ WorkSlot g_slots[kWorkSlots];
+
+enum { kJoinDynamic = 0, kJoinStatic = 1, kJoinDone = 2 };
+
+// dispatch id of the running launch: the index of its packet in its queue
+extern "C" __device__ unsigned long long fa_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// 48-bit, non-zero tag of this launch (splitmix64 finaliser over the packet
+// address and the dispatch id)
+__device__ __forceinline__ unsigned long long launch_tag() {
+  const unsigned long long p = (unsigned long long)(uintptr_t)__builtin_amdgcn_dispatch_ptr();
+  unsigned long long h = (p >> 6) * 0x9E3779B97F4A7C15ull ^ (fa_llvm_dispatch_id() + 0x632BE59BD9B4E019ull);
+  h ^= h >> 30;
+  h *= 0xBF58476D1CE4E5B9ull;
+  h ^= h >> 27;
+  h *= 0x94D049BB133111EBull;
+  h ^= h >> 31;
+  h &= 0xFFFFFFFFFFFFull;
+  return h ? h : 1;
+}
 
 __device__ __forceinline__ int xcd_id() {
   // hardware register XCC_ID (id 20), bits [3:0]
   return (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7u);
+}
+
+// Called once per workgroup by one thread, before its first claim.  Only
+// the first workgroup of a launch exchanges the free state for its own
+// (compare-and-swap); the others add themselves with one fetch-add, so the
+// start of a launch costs each workgroup a few atomics, not a contended loop.
+__device__ __forceinline__ int join_launch(int slot, unsigned long long tag) {
+  WorkSlot& w = g_slots[slot];
+  unsigned long long st = __hip_atomic_load(&w.state, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  for (int tries = 0; tries < 64; ++tries) {  // the bound only guarantees an end: static is always correct
+    if (st == 0) {
+      if (__hip_atomic_load(&w.done_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) return kJoinDone;
+      if (__hip_atomic_compare_exchange_strong(&w.state, &st, (tag << 16) | 1ull, __ATOMIC_ACQ_REL,
+                                               __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT))
+        return kJoinDynamic;
+      continue;  // st now holds the state another workgroup installed
+    }
+    if ((st >> 16) != tag)
+      return __hip_atomic_load(&w.done_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag ? kJoinDone
+                                                                                               : kJoinStatic;
+    const unsigned long long old =
+        __hip_atomic_fetch_add(&w.state, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if ((old >> 16) == tag) return kJoinDynamic;
+    // The slot changed between the load and the add (this launch had
+    // finished and freed it, and it may have a new owner): take the count
+    // back.  If that leaves a new owner with no workgroup, its workgroups
+    // have all left (one of them saw this one's count and did not free the
+    // slot), so free it on their behalf.
+    const unsigned long long prev =
+        __hip_atomic_fetch_sub(&w.state, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if ((prev & 0xFFFFull) == 1ull && (prev >> 16) != 0) {
+      unsigned long long dead = prev - 1;
+      __hip_atomic_store(&w.done_tag, prev >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int y = 0; y < 8; ++y)
+        __hip_atomic_store(&w.next_rank[y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_compare_exchange_strong(&w.state, &dead, 0ull, __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    st = __hip_atomic_load(&w.state, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return kJoinStatic;
 }
 
 __device__ __forceinline__ int take_item(int slot, int xcd, int total) {
@@ -76,7 +151,7 @@ __device__ __forceinline__ int take_item(int slot, int xcd, int total) {
     const int y = (xcd + i) & 7;
     const unsigned lo = (unsigned)((long long)y * total / 8);
     const unsigned n = (unsigned)((long long)(y + 1) * total / 8) - lo;
-    unsigned* ctr = &g_next_rank[slot][y];
+    unsigned* ctr = &g_slots[slot].next_rank[y];
     if (n == 0) continue;
     const unsigned t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (t < n) return (int)(lo + t);
@@ -84,15 +159,33 @@ __device__ __forceinline__ int take_item(int slot, int xcd, int total) {
   return -1;
 }
 
-// Called once per workgroup by one thread, after its last claim.
-__device__ __forceinline__ void leave_launch(int slot) {
+// The next item of a workgroup: from the slot's counters (joined), or the
+// next of its own stride (static).
+__device__ __forceinline__ int next_item(int mode, int slot, int xcd, int total, int cur) {
+  if (mode == kJoinDynamic) return take_item(slot, xcd, total);
+  const long long n = (long long)cur + gridDim.x;
+  return n < total ? (int)n : -1;
+}
+
+// Called once per joined workgroup by one thread, after its last claim (the
+// counters are exhausted, so every item of the launch has been claimed).  The
+// workgroup that takes the count to zero clears the counters, records the
+// launch as finished and frees the slot; should a late workgroup of the same
+// launch join in between, the exchange fails and that workgroup frees it
+// when it leaves (it finds the counters cleared and computes items again,
+// with the same results).
+__device__ __forceinline__ void leave_launch(int slot, unsigned long long tag) {
+  WorkSlot& w = g_slots[slot];
   __threadfence();
-  const unsigned prev = __hip_atomic_fetch_add(&g_done_wg[slot], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  if (prev == gridDim.x - 1) {
-    for (int y = 0; y < 8; ++y)
-      __hip_atomic_store(&g_next_rank[slot][y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&g_done_wg[slot], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  const unsigned long long old =
+      __hip_atomic_fetch_sub(&w.state, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old & 0xFFFFull) != 1ull) return;
+  unsigned long long mine = old - 1;  // this launch's tag with no workgroup left
+  __hip_atomic_store(&w.done_tag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int y = 0; y < 8; ++y)
+    __hip_atomic_store(&w.next_rank[y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_compare_exchange_strong(&w.state, &mine, 0ull, __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE,
+                                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -174,7 +267,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   // tile loads may overwrite the stage buffers.
   __shared__ int s_item;
   const int xcd = xcd_id();
-  if (tid == 0) s_item = PERSIST ? take_item(slot, xcd, total_items) : xcd_remap(blockIdx.x, total_items);
+  // thread 0 alone joins the launch's counter slot and claims items
+  int mode = kJoinStatic;
+  unsigned long long tag = 0;
+  if (tid == 0) {
+    if (PERSIST) {
+      tag = launch_tag();
+      mode = join_launch(slot, tag);
+      s_item = mode == kJoinDynamic ? take_item(slot, xcd, total_items)
+                                    : mode == kJoinStatic && (int)blockIdx.x < total_items ? (int)blockIdx.x : -1;
+    } else {
+      s_item = xcd_remap(blockIdx.x, total_items);
+    }
+  }
   __syncthreads();
   int work = __builtin_amdgcn_readfirstlane(s_item);
   while (work >= 0) {
@@ -538,7 +643,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       issue_for(j);
       // claim the next item during the last tile: claiming earlier would
       // reserve work that an idle workgroup could have started sooner
-      if (PERSIST && tid == 0 && j == T - 1) next = take_item(slot, xcd, total_items);
+      if (PERSIST && tid == 0 && j == T - 1) next = next_item(mode, slot, xcd, total_items, work);
       const uint8_t* kt = smem + stage_buf(j) * SB;  // K_{j+1}
       const uint8_t* vt = kt + TBK;                   // V_j
       if (j < my_T) {
@@ -558,6 +663,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       }
       end_iter(j);
     }
+    // An item without key tiles (a block of padding rows, no valid keys, or
+    // causal rows that all precede the first key) runs no tile above, so its
+    // successor is claimed here.
+    if (PERSIST && tid == 0 && T == 0) next = next_item(mode, slot, xcd, total_items, work);
 
     // Epilogue.  A lane holds 8-byte pieces of its row at 16-byte strides, so
     // storing straight from registers would make every store instruction
@@ -616,7 +725,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     __syncthreads();
     work = __builtin_amdgcn_readfirstlane(s_item);
   }
-  if (PERSIST && tid == 0) leave_launch(slot);
+  if (PERSIST && tid == 0 && mode == kJoinDynamic) leave_launch(slot, tag);
 }
 
 // Merge of the 16-bit kernel's key shares, per row: with a_s = mc_s +

@@ -15,8 +15,8 @@
  * pass").
  *
  * No function here allocates or frees device memory or synchronizes.  The
- * only state kept between calls is a fixed array of work counters in the
- * library's code object (see fa_fwd, "Scheduling").  No C++ exception
+ * only state kept between calls is a fixed table of work-counter slots in
+ * the library's code object (see fa_fwd, "Scheduling").  No C++ exception
  * crosses this boundary.
  */
 #ifndef FA_H
@@ -83,13 +83,17 @@ typedef enum {
  * to run (fixed reduction order).
  *
  * Scheduling: at head dim 128 (bf16/fp16) one workgroup per compute unit
- * claims work items through atomic counters in the library's code object:
- * 64 sets per device, taken round-robin per call and cleared by each call's
- * last workgroup.  Which workgroup computes an item never changes the result.
- * Calls that overlap in time use different sets unless more than 64 are in
- * flight at once on one device, or one captured call is replayed
- * concurrently with itself; such overlapping uses would share counters and
- * must be avoided.
+ * claims work items through atomic counters kept in the library's code
+ * object: 64 counter slots per device, drawn round-robin per call.  A slot
+ * belongs to one launch at a time, which the device identifies by a tag
+ * derived from the launch's dispatch packet (its address and dispatch id);
+ * the last workgroup of the owning launch clears the counters and frees the
+ * slot.  A launch whose slot is held by another launch still in flight (a
+ * captured call replayed beside a later call that drew the same slot, or
+ * more than 64 calls in flight on one device) runs its items in a fixed
+ * per-workgroup order instead, without the counters.  Which workgroup
+ * computes an item never changes the result, so calls may overlap freely,
+ * captured or not.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, int dtype,

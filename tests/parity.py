@@ -83,9 +83,12 @@ def score_rounding_bound(q, k, scale):
 
 
 def check(stats, dtype, extra_o=0.0, extra_lse=0.0):
+    """Assert the error statistics are within the dtype's bounds.  extra_o and
+    extra_lse widen the per-element (max) bounds by a derived worst-case term;
+    the mean bound is never widened: a per-element worst case says nothing
+    about the average error."""
     tol = dict(TOL[dtype])
     tol["max_o"] += extra_o
-    tol["mean_o"] += extra_o
     tol["max_lse"] += extra_lse
     assert stats["finite"], stats
     assert stats["max_o"] <= tol["max_o"], (stats, tol)

@@ -58,3 +58,61 @@ def test_captured_calls_replay_bitwise(B, H, N, d, causal, counts):
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), rep
         assert torch.equal(dq, dq_ref) and torch.equal(dk, dk_ref) and torch.equal(dv, dv_ref), rep
+
+
+def test_shared_counter_slot_concurrent_replays():
+    """Two captured calls that hold the same counter slot of the persistent
+    forward (the host hands out 64 slots round-robin; the second capture comes
+    64 calls after the first) replayed at the same time on two streams, next to
+    eager calls on a third: each writes its own outputs, and every output must
+    equal the eager result bit for bit.  A launch that finds its slot held by
+    another launch runs its items in its own static order instead."""
+    B, H, N, d = 1, 32, 16384, 128
+    q, k, v = (t.cuda() for t in make_qkv(B, H, N, d, "bf16", 77))
+    o_ref, l_ref = fa.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    outs = [(torch.empty_like(o_ref), torch.empty_like(l_ref)) for _ in range(3)]
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    graphs = []
+    for gi in range(2):
+        o, lse = outs[gi]
+        s1.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s1):
+            fa.attention(q, k, v, causal=True, out=o, lse=lse)  # warm-up call on the side stream
+        torch.cuda.current_stream().wait_stream(s1)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fa.attention(q, k, v, causal=True, out=o, lse=lse)
+        graphs.append(g)
+        if gi == 0:
+            # 62 calls of the same kernel, then the next warm-up call: the
+            # second capture is the 64th call after the first and draws its slot
+            for _ in range(62):
+                fa.attention(q, k, v, causal=True, out=outs[2][0], lse=outs[2][1])
+            torch.cuda.synchronize()
+    for rep in range(6):
+        for o, lse in outs:
+            o.fill_(float("nan"))
+            lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            graphs[0].replay()
+        with torch.cuda.stream(s2):
+            graphs[1].replay()
+        with torch.cuda.stream(s3):
+            for _ in range(3):
+                fa.attention(q, k, v, causal=True, out=outs[2][0], lse=outs[2][1])
+        torch.cuda.synchronize()
+        for i, (o, lse) in enumerate(outs):
+            assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), (rep, i)
+    # the same captured call replayed on two streams without a sync between
+    for rep in range(3):
+        outs[0][0].fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            graphs[0].replay()
+        with torch.cuda.stream(s2):
+            graphs[0].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], o_ref) and torch.equal(outs[0][1], l_ref), rep

@@ -203,8 +203,9 @@ def test_adding_a_constant_to_score_rows(causal):
 
 def test_large_scores_stay_finite():
     """Scaled scores of several hundred: no overflow, and agreement within the
-    workload tolerance widened by the fp32 score-rounding bound, which at
-    these magnitudes exceeds 1e-4 for any fp32 evaluation of the scores."""
+    workload tolerance.  The per-element (max) bounds are widened by the fp32
+    score-rounding bound, which at these magnitudes exceeds 1e-4 for any fp32
+    evaluation of the scores; the mean bound stays the workload's own."""
     q, k, v = make_qkv(1, 2, 200, 128, "fp32", 79)
     q, k = q * 12, k * 12
     scale = 1 / math.sqrt(128)
@@ -214,8 +215,10 @@ def test_large_scores_stay_finite():
         vmax = vv.double().abs().max().item()
         for causal in (False, True):
             o, lse = run(qq, kk, vv, causal)
-            parity.check(parity.compare(o, lse, qq, kk, vv, scale, causal), DT[dt],
-                         extra_o=2 * e * vmax, extra_lse=e)
+            st = parity.compare(o, lse, qq, kk, vv, scale, causal)
+            print(f"{dt} causal={causal}: max|dO| {st['max_o']:.3e} mean|dO| {st['mean_o']:.3e} "
+                  f"max|dlse| {st['max_lse']:.3e} (max bounds widened by {2 * e * vmax:.3e}, {e:.3e})")
+            parity.check(st, DT[dt], extra_o=2 * e * vmax, extra_lse=e)
 
 
 # ------------------------------------------------------------------ behaviour of the entry point
