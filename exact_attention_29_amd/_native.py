@@ -10,7 +10,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/fa.h
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: FA_DTYPE_FP32, torch.float16: FA_DTYPE_FP16,
                torch.bfloat16: FA_DTYPE_BF16}
@@ -60,6 +61,10 @@ def library():
         L.fa_fwd_gen.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.fa_fwd_gen_noalloc.restype = ctypes.c_int
+        L.fa_fwd_gen_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
         L.fa_fwd_gen_workspace_size.restype = ctypes.c_size_t
         L.fa_fwd_gen_workspace_size.argtypes = [ctypes.c_int] * 8
         L.fa_fwd_gen_supported.restype = ctypes.c_int
@@ -140,6 +145,16 @@ def fa_fwd_ex_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, causal: i
                              dtype: int) -> int:
     return int(library().fa_fwd_ex_workspace_size(int(B), int(H), int(Nq), int(Nk), int(d),
                                                   int(causal), int(dtype)))
+
+
+def fa_fwd_gen_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int,
+                       Nk: int, d_qk: int, d_v: int, scale: float, causal: int, dtype: int,
+                       k_len: int, q_len: int, stream: int) -> int:
+    """The raw allocation-free C entry point (fa_fwd_gen without a workspace;
+    a key split uses the library's fixed device scratch)."""
+    return library().fa_fwd_gen_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d_qk, d_v,
+                                        ctypes.c_float(scale), int(causal), int(dtype), k_len,
+                                        q_len, stream)
 
 
 def fa_fwd_gen(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,

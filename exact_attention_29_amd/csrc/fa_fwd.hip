@@ -1155,6 +1155,37 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
+// Scratch of the allocation-free entry point: the key-split partial outputs
+// and weights (the workspace fa_fwd_gen takes from the caller), held in the
+// code object on every device the library runs on, for the life of the
+// process.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_fwd_supported(int d, int dtype, int causal) {
@@ -1271,6 +1302,21 @@ int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse,
   return dispatch(q, k, v, o, lse, sh, d_qk, d_v, scale, causal, dtype, plan, workspace, stream);
 }
 
+int fa_fwd_gen_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int Nq, int Nk, int d_qk, int d_v, float scale, int causal, int dtype,
+                       const int* k_len, const int* q_len, void* stream) {
+  if (int err = check_args(q, k, v, o, lse, B, H, Nq, Nk, d_qk, d_v, scale, causal, dtype);
+      err != FA_OK)
+    return err;
+  if (((uintptr_t)k_len & 3u) != 0 || ((uintptr_t)q_len & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  const Shape sh{B * H, H, Nq, Nk, k_len, q_len};
+  const SplitPlan plan = plan_split((long long)B * H, Nq, Nk, d_qk, d_v, dtype);
+  if (plan.bytes > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (plan.n_split > 1 && scratch_address(&ws) != hipSuccess) return FA_ERR_HIP;
+  return dispatch(q, k, v, o, lse, sh, d_qk, d_v, scale, causal, dtype, plan, ws, stream);
+}
+
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int Nq, int Nk, int d, float scale, int causal, int dtype, const int* k_len,
               void* workspace, size_t workspace_bytes, void* stream) {
@@ -1301,6 +1347,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype or alignment";
     case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_SCRATCH: return "problem needs more split scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

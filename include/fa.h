@@ -42,7 +42,9 @@ typedef enum {
                              non-finite or non-positive scale, size overflow */
   FA_ERR_UNSUPPORTED = 2, /* head dim or dtype without a kernel, pointer not
                              16-byte aligned */
-  FA_ERR_HIP = 3          /* the kernel launch reported an error */
+  FA_ERR_HIP = 3,         /* the kernel launch reported an error */
+  FA_ERR_SCRATCH = 4      /* fa_fwd_gen_noalloc: the problem's key split needs
+                             more than FA_NOALLOC_SCRATCH_BYTES of scratch */
 } fa_status_t;
 
 /*
@@ -189,6 +191,30 @@ int fa_fwd_gen(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int Nq, int Nk, int d_qk, int d_v, float scale, int causal,
                int dtype, const int* k_len, const int* q_len, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_gen_noalloc -- fa_fwd_gen for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It calls no allocating routine.  Where fa_fwd_gen would
+ * split keys into a caller workspace (grids smaller than the device holds
+ * at once), this call uses a scratch array of FA_NOALLOC_SCRATCH_BYTES that
+ * the library's code object holds on every device it runs on, for the life
+ * of the process.  Arguments, outputs, errors and asynchrony are those of
+ * fa_fwd_gen without the workspace; the results equal fa_fwd_gen's with a
+ * workspace of fa_fwd_gen_workspace_size bytes, bit for bit.
+ *   Returns FA_ERR_SCRATCH (nothing launched) when that workspace size
+ *   exceeds FA_NOALLOC_SCRATCH_BYTES.
+ *   Every split call on one device uses the same scratch: calls that overlap
+ *   in time on one device (other streams, concurrent graph replays) race on
+ *   it and must be serialized by the caller.  Calls whose grids need no
+ *   split do not touch the scratch.  Its contents are never read before the
+ *   same call writes them.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fa_fwd_gen_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Nq, int Nk, int d_qk, int d_v, float scale,
+                       int causal, int dtype, const int* k_len, const int* q_len,
+                       void* stream);
 
 /* fa_fwd_ex_workspace_size for fa_fwd_gen's shapes (0: none needed, or invalid). */
 size_t fa_fwd_gen_workspace_size(int B, int H, int Nq, int Nk, int d_qk, int d_v, int causal,

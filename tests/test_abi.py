@@ -285,3 +285,25 @@ def test_largest_key_count_is_the_offset_limit():
         n_max = 0x7fffffff // (128 * elem) - 128
         over = call_ex(Nq=16, Nk=n_max + 1, d=128, dtype=dt)
         assert over == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG), (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG), (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(q=FAKE + 8), fa.FA_ERR_UNSUPPORTED),
+])
+def test_allocation_free_entry_point_checks_arguments_first(kw, code):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, scale=0.125,
+             causal=0)
+    a.update(kw)
+    st = fa.fa_fwd_gen_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                               a["N"], a["d"], a["d"], a["scale"], a["causal"], fa.FA_DTYPE_BF16,
+                               None, None, None)
+    assert st == code
+
+
+def test_scratch_status_and_size():
+    assert "scratch" in fa.fa_status_string(fa.FA_ERR_SCRATCH)
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES
