@@ -50,11 +50,6 @@ struct Bf16 {
     bf16x2 v = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(unsigned, v);
   }
-  // acc + both halves of a packed pair (v_dot2c_f32_bf16 against (1, 1))
-  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-  }
 };
 struct F16 {
   static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
@@ -64,10 +59,6 @@ struct F16 {
   static __device__ __forceinline__ unsigned pack(float x, float y) {
     f16x2 v = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(unsigned, v);
-  }
-  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
   }
 };
 

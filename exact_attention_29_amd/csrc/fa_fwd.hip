@@ -222,16 +222,16 @@ __device__ __forceinline__ void leave_launch(int slot, unsigned long long tag) {
 // Key split (SPLIT, for grids smaller than the GPU; never persistent): item
 // (query block, split s) covers the s-th of n_split equal shares of the
 // block's key tiles and writes, per row, its output normalised by its own
-// rounded-weight sum (fp32, Opart[s]) and the two log2 weights of the share,
-// mc + log2(lw) and mc + log2(l) (Lpart[s]); attn_combine_sp merges them.
-// A share with no kept key of a row writes 0 and -inf.
+// weight sum (fp32, Opart[s]) and the log2 weight of the share,
+// mc + log2(l) (Lpart[s]); attn_combine_sp merges them.  A share with no
+// kept key of a row writes 0 and -inf.
 template <class TT, int DK, int DV, bool CAUSAL, int NW, int NS, bool PERSIST, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV == 128 ? 3 : 2, DK + DV == 128 ? 3 : 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Nq, int Nk, int H, const int* __restrict__ k_len, const int* __restrict__ q_len,
     int n_qtiles, int total_items, int slot, float scale, int n_split, float* __restrict__ Opart,
-    float2* __restrict__ Lpart) {
+    float* __restrict__ Lpart) {
   static_assert(!(SPLIT && PERSIST), "a split launch has one workgroup per item");
   // DK: head dim of Q and K (the scores); DV: head dim of V and O
   constexpr int BR = 32 * NW, BC = 64;
@@ -252,28 +252,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
-  // O is divided by the sum of the weights as rounded for the P V product
-  // (lw) in the d = 128 arrangement, where those 16 packed adds per tile
-  // cost nothing measurable; at d = 64 the vector unit, not the matrix core,
-  // bounds the kernel, and dividing by the fp32 sum l of the unrounded
-  // weights -- the running denominator of the online softmax ("Deep
-  // Learning - Flash Attention", "An Example", the final division by l) --
-  // is 8-9% faster.
-  constexpr bool LW = DK + DV > 128;
+  // O is divided by the fp32 sum l of the unrounded weights, the running
+  // denominator of the online softmax ("Deep Learning - Flash Attention",
+  // "An Example", the final division by l).
   // Work loop.  Persistent: the workgroup claims items until none is left;
   // thread 0 claims the next item during the current one's last tile.
   // Otherwise the workgroup runs the one item its id maps to.  Every item
   // ends with a barrier after its last LDS read, so the next item's first
   // tile loads may overwrite the stage buffers.
   __shared__ int s_item;
+  // thread 0 alone joins the launch's counter slot and claims items; it keeps
+  // the launch tag and its join mode here rather than in registers
+  __shared__ unsigned long long s_tag;
+  __shared__ int s_mode;
   const int xcd = xcd_id();
-  // thread 0 alone joins the launch's counter slot and claims items
-  int mode = kJoinStatic;
-  unsigned long long tag = 0;
   if (tid == 0) {
     if (PERSIST) {
-      tag = launch_tag();
-      mode = join_launch(slot, tag);
+      const unsigned long long tag = launch_tag();
+      const int mode = join_launch(slot, tag);
+      s_tag = tag;
+      s_mode = mode;
       s_item = mode == kJoinDynamic ? take_item(slot, xcd, total_items)
                                     : mode == kJoinStatic && (int)blockIdx.x < total_items ? (int)blockIdx.x : -1;
     } else {
@@ -345,8 +343,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
 #pragma unroll
     for (int b = 0; b < DV / 32; ++b) o[b] = f32x16{};
     // running state: row max m, its scaled reference mc (exponents are taken
-    // against mc), fp32 sum l and the sum lw of the bf16-rounded weights
-    float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f, lw_run = 0.f;
+    // against mc) and the fp32 sum l of the weights
+    float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
     const float c2 = scale * kLog2e;
     u32x4 pf[BC / 16];  // P_j packed, B operand of the P V product
 
@@ -375,7 +373,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     };
     // Tile t's mask (if any), row max and reference move.  Returns the factor
     // for O, which the caller applies after O has received the previous tile;
-    // l and lw are rescaled here.  `resc` tells whether any row moved.
+    // l is rescaled here.  `resc` tells whether any row moved.
     auto part1 = [&](f32x16 (&sv)[BC / 32], int t, bool masked, bool& resc) -> float {
       if (masked) {
         const int k0 = (tile0 + t) * BC;
@@ -401,13 +399,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       const float alpha = (!resc || mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
       mc_run = resc ? mc_cand : mc_run;
       l_run *= alpha;
-      lw_run *= alpha;
       return alpha;
     };
-    // Exponentials against the current reference, the two sums, and P packed.
+    // Exponentials against the current reference, their sum, and P packed.
     auto part2 = [&](f32x16 (&sv)[BC / 32]) {
       const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
-      float ls[2] = {0.f, 0.f}, lws[2] = {0.f, 0.f};
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < BC / 32; ++b)
 #pragma unroll
@@ -422,10 +419,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         const f32x16& sb = sv[c >> 1];
         pf[c] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
                       TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
-        if (LW) lws[c & 1] = TT::sum2(pf[c][3], TT::sum2(pf[c][2], TT::sum2(pf[c][1], TT::sum2(pf[c][0], lws[c & 1]))));
       }
       l_run += ls[0] + ls[1];
-      lw_run += lws[0] + lws[1];
     };
     auto tile_masked = [&](int t) {
       const int k0 = (tile0 + t) * BC;
@@ -440,7 +435,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       constexpr int NQK = BC / 32 * DK / 16, NPV = BC / 16 * DV / 32;
       constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
       const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
-      float ls0 = 0.f, ls1 = 0.f, lw0 = 0.f, lw1 = 0.f;
+      float ls0 = 0.f, ls1 = 0.f;
       // ---- step A: S_{j+1} (MFMA) with exp / sums / packing of tile j (VALU)
       auto kaddr = [&](int i) {
         const int bb = i / (DK / 16), c = i % (DK / 16);
@@ -467,16 +462,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
             const f32x16& sb = cur[cc >> 1];
             pf[cc] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
                            TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
-            if (LW) {
-              if (cc & 1) lw1 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw1))));
-              else lw0 = TT::sum2(pf[cc][3], TT::sum2(pf[cc][2], TT::sum2(pf[cc][1], TT::sum2(pf[cc][0], lw0))));
-            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run += ls0 + ls1;
-      lw_run += lw0 + lw1;
       // ---- step B: O += P_j V_j (MFMA) with tile j+1's row max (VALU)
       auto vaddr = [&](int i) {
         const int cc = i / (DV / 32), bb = i % (DV / 32);
@@ -542,7 +532,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         const float alpha = mc_cand == -INFINITY ? 1.f : fast_exp2(mc_run - mc_cand);
         mc_run = mc_cand;
         l_run *= alpha;
-        lw_run *= alpha;
 #pragma unroll
         for (int bb = 0; bb < DV / 32; ++bb) o[bb] *= alpha;
       }
@@ -643,7 +632,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       issue_for(j);
       // claim the next item during the last tile: claiming earlier would
       // reserve work that an idle workgroup could have started sooner
-      if (PERSIST && tid == 0 && j == T - 1) next = next_item(mode, slot, xcd, total_items, work);
+      if (PERSIST && tid == 0 && j == T - 1) next = next_item(s_mode, slot, xcd, total_items, work);
       const uint8_t* kt = smem + stage_buf(j) * SB;  // K_{j+1}
       const uint8_t* vt = kt + TBK;                   // V_j
       if (j < my_T) {
@@ -666,7 +655,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     // An item without key tiles (a block of padding rows, no valid keys, or
     // causal rows that all precede the first key) runs no tile above, so its
     // successor is claimed here.
-    if (PERSIST && tid == 0 && T == 0) next = next_item(mode, slot, xcd, total_items, work);
+    if (PERSIST && tid == 0 && T == 0) next = next_item(s_mode, slot, xcd, total_items, work);
 
     // Epilogue.  A lane holds 8-byte pieces of its row at 16-byte strides, so
     // storing straight from registers would make every store instruction
@@ -676,11 +665,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     // a padding row (my_q >= nq) stores the empty sum: O = 0, lse = -inf
     const bool pad = my_q >= nq;
     const float l_tot = pad ? 0.f : half_sum(l_run);
-    const float lw_tot = pad ? 0.f : LW ? half_sum(lw_run) : l_tot;
     if constexpr (SPLIT) {
       // this share's output and weights, fp32, straight from the registers
       // (block b, register 4g+e of lane (q, h) is column 32b + 8g + 4h + e)
-      const float inv = lw_tot > 0.f ? __builtin_amdgcn_rcpf(lw_tot) : 0.f;
+      const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
       if (my_q < Nq) {
         const size_t rows = (size_t)(total_items / (n_qtiles * n_split)) * Nq;
         const size_t row = (size_t)split * rows + (size_t)bh * Nq + my_q;
@@ -691,13 +679,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
           for (int g = 0; g < 4; ++g)
             *(f32x4*)(orow + 32 * b + 8 * g) = f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv,
                                                      o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
-        if (hf == 0)
-          Lpart[row] = float2{lw_tot > 0.f ? mc_run + __builtin_amdgcn_logf(lw_tot) : -INFINITY,
-                              l_tot > 0.f ? mc_run + __builtin_amdgcn_logf(l_tot) : -INFINITY};
+        if (hf == 0) Lpart[row] = l_tot > 0.f ? mc_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
       }
     } else {
-      // a row without kept keys has lw = 0 and O = 0 (rows past Nq: not stored)
-      const float inv = lw_tot > 0.f ? __builtin_amdgcn_rcpf(lw_tot) : 0.f;
+      // a row without kept keys has l = 0 and O = 0 (rows past Nq: not stored)
+      const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
       uint8_t* stg = smem + wave * kOStageBytes;
 #pragma unroll
       for (int r = 0; r < DV / 64; ++r) {
@@ -725,20 +711,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     __syncthreads();
     work = __builtin_amdgcn_readfirstlane(s_item);
   }
-  if (PERSIST && tid == 0 && mode == kJoinDynamic) leave_launch(slot, tag);
+  if (PERSIST && tid == 0 && s_mode == kJoinDynamic) leave_launch(slot, s_tag);
 }
 
-// Merge of the 16-bit kernel's key shares, per row: with a_s = mc_s +
-// log2(lw_s) (the share's rounded-weight mass; lw is l at d = 64) and
-// b_s = mc_s + log2(l_s),
-// O = sum_s 2^(a_s) O_s / sum_s 2^(a_s) -- the normalisation by the rounded
-// weights that the unsplit kernel applies -- and lse = ln sum_s 2^(b_s), the
-// rule by which partial softmax results over disjoint key sets combine
-// ("FlashAttention Engine", "Core FlashAttention Mechanics", item 3).  DV/8
-// threads per row, 8 columns each; shares are added in order.
+// Merge of the 16-bit kernel's key shares, per row: with b_s = mc_s +
+// log2(l_s) the log2 weight of share s, O = sum_s 2^(b_s) O_s / sum_s 2^(b_s)
+// and lse = ln sum_s 2^(b_s), the rule by which partial softmax results over
+// disjoint key sets combine ("FlashAttention Engine", "Core FlashAttention
+// Mechanics", item 3).  DV/8 threads per row, 8 columns each; shares are
+// added in order.
 template <class TT, int DV>
 __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__ Opart,
-                                                       const float2* __restrict__ Lpart,
+                                                       const float* __restrict__ Lpart,
                                                        uint16_t* __restrict__ O,
                                                        float* __restrict__ LSE, long long rows,
                                                        int n_split) {
@@ -746,25 +730,19 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
   const int t = threadIdx.x % TPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
-  float amax = -INFINITY, bmax = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) {
-    const float2 w = Lpart[(size_t)sp * rows + row];
-    amax = fmaxf(amax, w.x);
-    bmax = fmaxf(bmax, w.y);
-  }
+  float bmax = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) bmax = fmaxf(bmax, Lpart[(size_t)sp * rows + row]);
   uint16_t* orow = O + (size_t)row * DV + 8 * t;
-  if (amax == -INFINITY) {  // no share kept a key of this row: the empty sum
+  if (bmax == -INFINITY) {  // no share kept a key of this row: the empty sum
     *(u32x4*)orow = u32x4{0, 0, 0, 0};
     if (t == 0) LSE[row] = -INFINITY;
     return;
   }
-  float wsum = 0.f, lsum = 0.f;
+  float wsum = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < n_split; ++sp) {
-    const float2 w = Lpart[(size_t)sp * rows + row];
-    const float e = fast_exp2(w.x - amax);  // 0 for a share without kept keys
+    const float e = fast_exp2(Lpart[(size_t)sp * rows + row] - bmax);  // 0 for a share without kept keys
     wsum += e;
-    lsum += fast_exp2(w.y - bmax);
     const f32x4* op = (const f32x4*)(Opart + ((size_t)sp * rows + row) * DV + 8 * t);
     acc0 += e * op[0];
     acc1 += e * op[1];
@@ -772,7 +750,7 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
   const float inv = 1.f / wsum;
   *(u32x4*)orow = u32x4{TT::pack(acc0[0] * inv, acc0[1] * inv), TT::pack(acc0[2] * inv, acc0[3] * inv),
                         TT::pack(acc1[0] * inv, acc1[1] * inv), TT::pack(acc1[2] * inv, acc1[3] * inv)};
-  if (t == 0) LSE[row] = (bmax + __builtin_amdgcn_logf(lsum)) * kLn2;
+  if (t == 0) LSE[row] = (bmax + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1049,7 +1027,7 @@ SplitPlan plan_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype) {
   const long long sp = std::min<long long>((slots + items - 1) / items, ntiles / 4);
   if (sp < 2) return p;
   p.n_split = (int)sp;
-  p.bytes = (size_t)p.n_split * rows * (size_t)(dv + 2) * sizeof(float);
+  p.bytes = (size_t)p.n_split * rows * (size_t)(dv + 1) * sizeof(float);
   return p;
 }
 
@@ -1072,7 +1050,7 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
     const int total = nq * sh.BH * plan.n_split;
     const long long rows = (long long)sh.BH * sh.Nq;
     float* opart = (float*)ws;
-    float2* lpart = (float2*)(opart + (size_t)plan.n_split * rows * DV);
+    float* lpart = opart + (size_t)plan.n_split * rows * DV;
     const dim3 grid(total), block(64 * NW);
     if (causal)
       hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, false, true>), grid, block, 0, st,
@@ -1087,7 +1065,7 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     constexpr int RPB = 256 / (DV / 8);
     hipLaunchKernelGGL((attn_combine_sp<TT, DV>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
-                       0, st, (const float*)opart, (const float2*)lpart, (uint16_t*)o, lse, rows,
+                       0, st, (const float*)opart, (const float*)lpart, (uint16_t*)o, lse, rows,
                        plan.n_split);
     return hipGetLastError();
   }

@@ -129,9 +129,9 @@ size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
  *                     it must be >= fa_fwd_workspace_size(...) for the same
  *                     problem on the same device, else FA_ERR_INVALID_ARG
  *                     (a misaligned workspace gives FA_ERR_UNSUPPORTED).
- * The key-split result equals fa_fwd's up to rounding (fp32: the merge adds
- * one rounding per range; 16-bit: each range normalises by its own rounded
- * weights before the merge); it is bitwise reproducible run to run.
+ * The key-split result equals fa_fwd's up to rounding (the merge adds one
+ * rounding per range, and 16-bit ranges keep their partial output in fp32);
+ * it is bitwise reproducible run to run.
  */
 int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype,
