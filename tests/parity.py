@@ -20,10 +20,14 @@ TOL = {
 
 
 # Gradient tolerances, relative to the largest element of the reference
-# gradient tensor (its natural scale; see the derivation in the gradient tests).
+# gradient tensor (its natural scale; see the derivation in the gradient
+# tests).  fp16's are bf16's divided by 8, as for the forward: its roundings
+# of P, dS and the outputs are 8x finer (measured over 72 gradient tensors,
+# 4 shapes x 6 seeds: fp16 max 5.8e-4 and mean 4.0e-5 of the scale at worst,
+# against bf16's 5.7e-3 and 3.2e-4).
 TOL_BWD = {
     torch.bfloat16: dict(max_rel=2e-2, mean_rel=2e-3),
-    torch.float16: dict(max_rel=4e-3, mean_rel=4e-4),
+    torch.float16: dict(max_rel=2.5e-3, mean_rel=2.5e-4),
     torch.float32: dict(max_rel=1e-4, mean_rel=1e-5),
 }
 
