@@ -8,7 +8,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB = os.path.join(_HERE, "libfa.so")
+# FA_LIB names another build of the same sources (the sanitizer test's
+# host-instrumented build); there is no fallback to anything else
+_LIB = os.environ.get("FA_LIB") or os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4
 FA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/fa.h

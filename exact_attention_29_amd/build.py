@@ -39,5 +39,26 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """libfa.so with its host half (argument checks, planning, the C ABI)
+    instrumented with AddressSanitizer and UndefinedBehaviorSanitizer, for the
+    CPU-only sanitizer test; the device code is built as usual.  Uses the
+    shared clang sanitizer runtime."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-shared", "-fPIC",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Xarch_host", "-g",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+           "-fsanitize=undefined", "-Xarch_host", "-shared-libsan", "-Xarch_host",
+           "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv, resource_usage="--resource-usage" in sys.argv))

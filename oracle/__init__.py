@@ -23,7 +23,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# FA_ORACLE_LIB names another build of the same sources (the sanitizer test)
+_LIB_PATH = os.environ.get("FA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 # element-type codes of oracle.h
