@@ -34,6 +34,12 @@
 //
 // Exponentials are exp2 of scores pre-multiplied by scale*log2(e) (v_exp_f32);
 // the log-sum-exp is converted back to natural-log units at the end.
+//
+// Built with FA_SYNC_PHASES defined (a separate check library, never the
+// product), the 16-bit kernel waits for every tile load and meets the whole
+// workgroup at a barrier before each tile's LDS reads and around each
+// epilogue staging phase: the same arithmetic with no overlap of loads,
+// reads and writes, which must give bitwise the same results.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -546,7 +552,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     // older load is done.
     constexpr int AHEAD = NS - 1;
     static_assert((NS & (NS - 1)) == 0 && NS <= 4, "power-of-two stage count, at most 4");
-    auto issue_for = [&](int j) { if (j + AHEAD < T) load_stage(j + AHEAD); };
+    auto issue_for = [&](int j) {
+      if (j + AHEAD < T) load_stage(j + AHEAD);
+#ifdef FA_SYNC_PHASES
+      // check build: every stage has landed and every wave has arrived
+      // before any wave reads a tile, so no load overlaps any LDS read
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+#endif
+    };
     // loads one wave issues for stage st: K tile (if st+1 < T) and V tile (if st >= 0)
     auto stage_loads = [&](int st) {
       return st >= T ? 0 : (st + 1 < T ? NDK : 0) + (st >= 0 ? NDV : 0);
@@ -687,6 +701,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       uint8_t* stg = smem + wave * kOStageBytes;
 #pragma unroll
       for (int r = 0; r < DV / 64; ++r) {
+#ifdef FA_SYNC_PHASES
+        __syncthreads();  // check build: a barrier around every staging phase
+#endif
 #pragma unroll
         for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
@@ -696,6 +713,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
                              TT::pack(ob[4 * g + 2] * inv, ob[4 * g + 3] * inv)};
             *(u32x2*)(stg + lq * kOStageRow + 2 * (32 * bl + 8 * g + 4 * hf)) = w;
           }
+#ifdef FA_SYNC_PHASES
+        __syncthreads();
+#endif
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 8 * i + (lane >> 3);
