@@ -734,6 +734,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   if (PERSIST && tid == 0 && s_mode == kJoinDynamic) leave_launch(slot, s_tag);
 }
 
+// splits whose partial results one merge thread has in flight at once
+constexpr int kCombineBatch = 8;
+
 // Merge of the 16-bit kernel's key shares, per row: with b_s = mc_s +
 // log2(l_s) the log2 weight of share s, O = sum_s 2^(b_s) O_s / sum_s 2^(b_s)
 // and lse = ln sum_s 2^(b_s), the rule by which partial softmax results over
@@ -750,8 +753,16 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
   const int t = threadIdx.x % TPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
+  // shares read kCombineBatch at a time, as in attn_combine_f32
   float bmax = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) bmax = fmaxf(bmax, Lpart[(size_t)sp * rows + row]);
+  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+    float l[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i)
+      l[i] = s0 + i < n_split ? Lpart[(size_t)(s0 + i) * rows + row] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) bmax = fmaxf(bmax, l[i]);
+  }
   uint16_t* orow = O + (size_t)row * DV + 8 * t;
   if (bmax == -INFINITY) {  // no share kept a key of this row: the empty sum
     *(u32x4*)orow = u32x4{0, 0, 0, 0};
@@ -760,12 +771,26 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
   }
   float wsum = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < n_split; ++sp) {
-    const float e = fast_exp2(Lpart[(size_t)sp * rows + row] - bmax);  // 0 for a share without kept keys
-    wsum += e;
-    const f32x4* op = (const f32x4*)(Opart + ((size_t)sp * rows + row) * DV + 8 * t);
-    acc0 += e * op[0];
-    acc1 += e * op[1];
+  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+    float l[kCombineBatch];
+    f32x4 op0[kCombineBatch], op1[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const bool in = s0 + i < n_split;
+      const f32x4* op = (const f32x4*)(Opart + ((size_t)(s0 + i) * rows + row) * DV + 8 * t);
+      l[i] = in ? Lpart[(size_t)(s0 + i) * rows + row] : -INFINITY;
+      op0[i] = in ? op[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+      op1[i] = in ? op[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      if (s0 + i < n_split) {
+        const float e = fast_exp2(l[i] - bmax);  // 0 for a share without kept keys
+        wsum += e;
+        acc0 += e * op0[i];
+        acc1 += e * op1[i];
+      }
+    }
   }
   const float inv = 1.f / wsum;
   *(u32x4*)orow = u32x4{TT::pack(acc0[0] * inv, acc0[1] * inv), TT::pack(acc0[2] * inv, acc0[3] * inv),
@@ -800,7 +825,10 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     float scale, int n_split, int tps, float* __restrict__ Opart, float* __restrict__ LSEpart) {
   // D: head dim of Q and K (DSL columns per wave); DV: of V and O (DSLV per wave)
   constexpr int D = DSL * DS, DV = DSLV * DS, NB = DSLV / 32, BC = 32;
-  __shared__ f32x16 red[DS > 1 ? DS * 64 : 1];
+  // partial scores exchanged between the waves: slot w, slice c of every
+  // lane, CH = 16/DS floats each, lanes contiguous (no bank conflicts)
+  constexpr int CH = 16 / DS;
+  __shared__ __attribute__((aligned(16))) float red[DS > 1 ? DS * DS * 64 * CH : 1];
   // Each wave's Q slice (32 rows x DSL columns) lives in LDS, not in
   // registers: the registers it frees hold the next key tile's K and the
   // current tile's V while they load, so that both loads overlap products.
@@ -828,11 +856,14 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 
   float* const qw = qsm + wave * 32 * DSL + lq * DSL;  // this lane's Q row in LDS
   auto qslot = [&](int u) { return qw + 4 * ((2 * u + hf) ^ (lq & 15)); };
+  // Q is requested first, then the first K tile; Q goes to LDS once it has
+  // arrived, while the K rows are still on their way
+  f32x4 qtmp[DSL / 8];
   {
     const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
 #pragma unroll
     for (int u = 0; u < DSL / 8; ++u)
-      *(f32x4*)qslot(u) = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+      qtmp[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
   }
   f32x16 o[NB];
 #pragma unroll
@@ -854,6 +885,8 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     for (int u = 0; u < DSL / 8; ++u) kf[u] = key < nk ? *(const f32x4*)(krow + 8 * u) : f32x4{0, 0, 0, 0};
   };
   if (j_begin < j_end) load_k(j_begin);
+#pragma unroll
+  for (int u = 0; u < DSL / 8; ++u) *(f32x4*)qslot(u) = qtmp[u];
   for (int j = j_begin; j < j_end; ++j) {
     const int k0 = j * BC;
     // V rows of tile j, requested before the score products so that they
@@ -888,13 +921,42 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
       for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[u][v], qa[v], s, 0, 0, 0);
     }
 
-    if (DS > 1) {  // full scores = sum of the DS partials, in wave order
-      red[wave * 64 + lane] = s;
-      __syncthreads();
-      s = red[lane];
+    if constexpr (DS > 1) {
+      // Full scores = the DS partials summed in wave order, each element once:
+      // wave w sums slice w (registers CH*w .. CH*w+CH-1) of every wave's
+      // partial and publishes it in its own slot at position w; every wave
+      // then reads the DS sums.  Position w of slot w is never written with a
+      // partial (wave w keeps that slice in registers), so the next tile's
+      // partials cannot overwrite a sum another wave may still be reading.
+      auto at = [&](int slot, int c) { return red + ((slot * DS + c) * 64 + lane) * CH; };
 #pragma unroll
-      for (int w = 1; w < DS; ++w) s += red[w * 64 + lane];
+      for (int c = 0; c < DS; ++c)
+        if (c != wave) {
+#pragma unroll
+          for (int i = 0; i < CH; ++i) at(wave, c)[i] = s[CH * c + i];
+        }
       __syncthreads();
+      float sum[CH];
+#pragma unroll
+      for (int w = 0; w < DS; ++w) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          float part = 0.f;
+#pragma unroll
+          for (int c = 0; c < DS; ++c)  // this wave's own slice, from registers
+            if (c == wave) part = s[CH * c + i];
+          if (w != wave) part = at(w, wave)[i];
+          sum[i] = w == 0 ? part : sum[i] + part;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) at(wave, wave)[i] = sum[i];
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < DS; ++c) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) s[CH * c + i] = c == wave ? sum[i] : at(c, c)[i];
+      }
     }
     const bool need_mask = (CAUSAL && k0 + BC - 1 > q_first + diag) || (k0 + BC > nk);
     if (need_mask) {
@@ -944,7 +1006,14 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * hf + (r & 3);
-      if constexpr (NB == 4) {
+      if constexpr (NB == 4 && DSLV <= DSL) {
+        // Staged in this wave's Q area (its last reader was this wave), row
+        // lq's 16-byte chunk i in slot i ^ lq, then stored whole rows at a
+        // time below: a direct store from these registers would write 32 B
+        // to each of 32 rows per instruction.
+        *(f32x4*)(qsm + wave * 32 * DSL + lq * DSLV + 4 * (i ^ lq)) =
+            f32x4{o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv};
+      } else if constexpr (NB == 4) {
         *(f32x4*)(orow + 4 * i) = f32x4{o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv};
       } else if constexpr (NB == 2) {
         *(f32x2*)(orow + 2 * i) = f32x2{o[0][r] * inv, o[1][r] * inv};
@@ -959,6 +1028,17 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
         LSEpart[(size_t)split * Nq * (total_wg / (n_qtiles * n_split)) + (size_t)bh * Nq + my_q] = lse_row;
       else
         LSE[(size_t)bh * Nq + my_q] = lse_row;
+    }
+  }
+  if constexpr (NB == 4 && DSLV <= DSL) {
+    // whole rows out, two per store: lane (c, h) takes chunk c of row 2t + h
+    float* obase = (SPLIT ? Opart + (size_t)split * ((size_t)Nq * DV * (total_wg / (n_qtiles * n_split))) : O) +
+                   ohead + colv0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int row = 2 * t + hf, c = lq;
+      const f32x4 val = *(const f32x4*)(qsm + wave * 32 * DSL + row * DSLV + 4 * (c ^ row));
+      if (q_first + row < Nq) *(f32x4*)(obase + (size_t)(q_first + row) * DV + 4 * c) = val;
     }
   }
 }
@@ -978,8 +1058,17 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
   const int t = threadIdx.x % TPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   if (threadIdx.x / TPR >= RPB || row >= rows) return;
+  // The splits are read kCombineBatch at a time, all loads of a batch issued
+  // before any is used; the sums still run over the splits in order.
   float m = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, LSEpart[(size_t)sp * rows + row]);
+  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+    float l[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i)
+      l[i] = s0 + i < n_split ? LSEpart[(size_t)(s0 + i) * rows + row] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) m = fmaxf(m, l[i]);
+  }
   if (m == -INFINITY) {  // no split kept a key of this row: the empty sum
     *(f32x4*)(O + (size_t)row * D + 4 * t) = f32x4{0.f, 0.f, 0.f, 0.f};
     if (t == 0) LSE[row] = -INFINITY;
@@ -987,11 +1076,23 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
   }
   float sum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < n_split; ++sp) {
-    const float w = __expf(LSEpart[(size_t)sp * rows + row] - m);  // 0 for an empty split
-    sum += w;
-    const f32x4 op = *(const f32x4*)(Opart + ((size_t)sp * rows + row) * D + 4 * t);
-    acc += w * op;
+  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+    float l[kCombineBatch];
+    f32x4 op[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const bool in = s0 + i < n_split;
+      l[i] = in ? LSEpart[(size_t)(s0 + i) * rows + row] : -INFINITY;
+      op[i] = in ? *(const f32x4*)(Opart + ((size_t)(s0 + i) * rows + row) * D + 4 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      if (s0 + i < n_split) {
+        const float w = __expf(l[i] - m);  // 0 for an empty split
+        sum += w;
+        acc += w * op[i];
+      }
+    }
   }
   const float inv = 1.f / sum;
   *(f32x4*)(O + (size_t)row * D + 4 * t) = acc * inv;
