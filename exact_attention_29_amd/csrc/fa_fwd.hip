@@ -28,6 +28,8 @@
 //    Head dims above 128 are split across the waves of a workgroup (128
 //    columns each); the partial scores are summed through LDS in a fixed wave
 //    order, so every wave sees bitwise the same scores and the same softmax.
+//    Q stays in registers; each wave's slice of the next K tile is loaded
+//    straight into LDS while the current tile's products run.
 //  * attn_combine_sp / attn_combine_f32: grids too small to fill the GPU
 //    split each query block's keys over several workgroups; these merge the
 //    partial results of the key ranges in a fixed order.
@@ -38,8 +40,10 @@
 // Built with FA_SYNC_PHASES defined (a separate check library, never the
 // product), the 16-bit kernel waits for every tile load and meets the whole
 // workgroup at a barrier before each tile's LDS reads and around each
-// epilogue staging phase: the same arithmetic with no overlap of loads,
-// reads and writes, which must give bitwise the same results.
+// epilogue staging phase, and the fp32 kernel waits for all of a tile's
+// loads (K and V) before its score products: the same arithmetic with no
+// overlap of loads, reads and writes, which must give bitwise the same
+// results.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -817,6 +821,16 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
 // log-sum-exp over those keys to Opart[s] / LSEpart[s] (rows*D and rows
 // floats per split); attn_combine_f32 merges the splits.  A split that holds
 // no kept key of a row writes 0 and -inf for it.
+// A raw buffer resource for compiler-visible buffer loads, its base and
+// record count read from the first lane (wave-uniform by construction), so
+// that the compiler keeps it in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint64_t u = (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)a) |
+                     ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)u, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
 template <int DSL, int DSLV, int DS, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -829,13 +843,15 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   // lane, CH = 16/DS floats each, lanes contiguous (no bank conflicts)
   constexpr int CH = 16 / DS;
   __shared__ __attribute__((aligned(16))) float red[DS > 1 ? DS * DS * 64 * CH : 1];
-  // Each wave's Q slice (32 rows x DSL columns) lives in LDS, not in
-  // registers: the registers it frees hold the next key tile's K and the
-  // current tile's V while they load, so that both loads overlap products.
-  // Row q's 16-byte chunk c sits in slot c ^ (q % 16): the 16 rows one
-  // 16-lane group reads fall in 16 distinct bank groups.
-  static_assert(DSL >= 64, "the chunk swizzle needs 16 chunks per row");
-  __shared__ __attribute__((aligned(16))) float qsm[DS * 32 * DSL];
+  // Each wave's slice of a K tile (32 keys x DSL columns, read by that wave
+  // only) is loaded straight into LDS by buffer loads, 16 bytes per lane:
+  // 1 KB blocks of 8 rows x 8 chunks (one 128-byte line of each row), block
+  // (rg, cg) = rows 8rg.., chunks 8cg.. at (rg * DSL/32 + cg) KB, and chunk
+  // ci of row ri in slot ri * 8 + (ci ^ ri ^ (rg & 1)).  A load instruction
+  // then reads 8 whole lines, and the 16 rows a 16-lane group reads for one
+  // operand fall in 16 distinct slots of a 256-byte bank row.
+  static_assert(DSL % 32 == 0, "K slices are whole 8-chunk blocks");
+  __shared__ __attribute__((aligned(1024))) float ksm[DS * 32 * DSL];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane & 31, hf = lane >> 5;
@@ -845,8 +861,10 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int bh = work / n_qtiles;
   int qt = work % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;
-  const int nk = k_len ? min(max(k_len[bh / H], 0), Nk) : Nk;  // as in the 16-bit kernel
-  const int nq = q_len ? min(max(q_len[bh / H], 0), Nq) : Nq;
+  // as in the 16-bit kernel; read from the first lane so that the compiler
+  // keeps them (and the buffer descriptors made from them) scalar
+  const int nk = __builtin_amdgcn_readfirstlane(k_len ? min(max(k_len[bh / H], 0), Nk) : Nk);
+  const int nq = __builtin_amdgcn_readfirstlane(q_len ? min(max(q_len[bh / H], 0), Nq) : Nq);
   const int diag = nk - nq;
   const size_t head = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
   const size_t vhead = (size_t)bh * Nk * DV, ohead = (size_t)bh * Nq * DV;
@@ -854,16 +872,13 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int my_q = q_first + lq;
   const int col0 = wave * DSL, colv0 = wave * DSLV;
 
-  float* const qw = qsm + wave * 32 * DSL + lq * DSL;  // this lane's Q row in LDS
-  auto qslot = [&](int u) { return qw + 4 * ((2 * u + hf) ^ (lq & 15)); };
-  // Q is requested first, then the first K tile; Q goes to LDS once it has
-  // arrived, while the K rows are still on their way
-  f32x4 qtmp[DSL / 8];
+  // Q rows in registers: lane (q, h) holds Q[q][col0 + 8u + 4h .. +3]
+  f32x4 qf[DSL / 8];
   {
     const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
 #pragma unroll
     for (int u = 0; u < DSL / 8; ++u)
-      qtmp[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+      qf[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
   }
   f32x16 o[NB];
 #pragma unroll
@@ -876,50 +891,75 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int j_begin = SPLIT ? split * tps : 0;
   const int j_end = SPLIT ? min(ntiles, j_begin + tps) : ntiles;
 
-  // K rows of tile j: lane (key, h) holds K[k0 + key][col0 + 8u + 4h .. +3]
-  f32x4 kf[DSL / 8];
-  auto load_k = [&](int j) {
-    const int key = j * BC + lq;
-    const float* krow = K + khead + (size_t)key * D + col0 + 4 * hf;
+  // K tile j into this wave's LDS slice: the descriptor starts at the
+  // tile's first key and ends at the last valid one (rows past it read 0)
+  constexpr int CG = DSL / 32;
+  float* const kw = ksm + wave * 32 * DSL;
+  const unsigned kw_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)kw;
+  // Block (rg, cg) gets a descriptor of its own, based at its first row and
+  // column and ending at the last valid key row, so lane L's offset is the
+  // same for every block: row L/8, chunk (L%8) ^ (L/8) ^ (rg & 1).
+  const int dma_lane0 = ((lane >> 3) * D + 4 * ((lane & 7) ^ (lane >> 3))) * 4;
+  const int dma_lane1 = ((lane >> 3) * D + 4 * ((lane & 7) ^ (lane >> 3) ^ 1)) * 4;
+  auto dma_k = [&](int j) {
 #pragma unroll
-    for (int u = 0; u < DSL / 8; ++u) kf[u] = key < nk ? *(const f32x4*)(krow + 8 * u) : f32x4{0, 0, 0, 0};
+    for (int blk = 0; blk < 4 * CG; ++blk) {
+      const int rg = blk / CG, cg = blk % CG, r0 = j * BC + 8 * rg;
+      const unsigned rows = (unsigned)min(max(nk - r0, 0), 8);
+      dma16(buffer_desc(K + khead + (size_t)r0 * D + col0 + 32 * cg, rows * D * 4), kw_lds + blk * 1024,
+            rg & 1 ? dma_lane1 : dma_lane0);
+    }
   };
-  if (j_begin < j_end) load_k(j_begin);
-#pragma unroll
-  for (int u = 0; u < DSL / 8; ++u) *(f32x4*)qslot(u) = qtmp[u];
+  // where lane (key, h) reads chunk 2u + h of its key row
+  const int krg = lq >> 3, kri = lq & 7;
+  const float* const kread = kw + (krg * CG * 64 + kri * 8) * 4;
+  auto kslot = [&](int u) {
+    const int c = 2 * u + hf;
+    return kread + ((c >> 3) * 64 + ((c & 7) ^ kri ^ (krg & 1))) * 4;
+  };
+  if (j_begin < j_end) dma_k(j_begin);
+  const int v_lane = (4 * hf * DV + colv0 + NB * lq) * 4;  // row 4h of a step, this lane's columns
   for (int j = j_begin; j < j_end; ++j) {
     const int k0 = j * BC;
     // V rows of tile j, requested before the score products so that they
-    // arrive while those run: step r takes key 8(r/4) + 4h + r%4
+    // arrive while those run: step r takes key 8(r/4) + 4h + r%4.  Buffer
+    // loads, one descriptor per step based at key k0 + 8(r/4) + r%4 and
+    // ending at the last valid key (rows past it read 0): exactly 16 load
+    // instructions, which the wait for this tile's K below counts.
     float vv[16][NB];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float* vrow = V + vhead + (size_t)key * DV + colv0 + NB * lq;
-      if (key < nk) {
-        if constexpr (NB == 4) {
-          const f32x4 t = *(const f32x4*)vrow;
-          vv[r][0] = t[0]; vv[r][1] = t[1]; vv[r][2] = t[2]; vv[r][3] = t[3];
-        } else if constexpr (NB == 2) {
-          const f32x2 t = *(const f32x2*)vrow;
-          vv[r][0] = t[0]; vv[r][1] = t[1];
-        } else {
-#pragma unroll
-          for (int b = 0; b < NB; ++b) vv[r][b] = vrow[b];
-        }
+      const int r0 = k0 + 8 * (r >> 2) + (r & 3);
+      const __amdgpu_buffer_rsrc_t vres = uniform_rsrc(V + vhead + (size_t)r0 * DV, min(max(nk - r0, 0), 8) * DV * 4);
+      if constexpr (NB == 4) {
+        const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, v_lane, 0, 0));
+        vv[r][0] = t[0]; vv[r][1] = t[1]; vv[r][2] = t[2]; vv[r][3] = t[3];
       } else {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) vv[r][b] = 0.f;
+        static_assert(NB == 2, "V rows are 64 or 128 columns per wave");
+        const f32x2 t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(vres, v_lane, 0, 0));
+        vv[r][0] = t[0]; vv[r][1] = t[1];
       }
     }
+    // this tile's K: issued before the 16 V loads, so done at vmcnt <= 16
+#ifdef FA_SYNC_PHASES
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#else
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
+#endif
     // partial S^T over this wave's columns
     f32x16 s = f32x16{};
 #pragma unroll
     for (int u = 0; u < DSL / 8; ++u) {
-      const f32x4 qa = *(const f32x4*)qslot(u);
+      const f32x4 ka = *(const f32x4*)kslot(u);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[u][v], qa[v], s, 0, 0, 0);
+      for (int v = 0; v < 4; ++v) s = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[v], qf[u][v], s, 0, 0, 0);
     }
+    // The V rows have arrived (they were requested first; waiting here also
+    // tells the compiler so, and it adds no wait later that would count the
+    // K loads below); this wave's reads of its K slice are done (consumed by
+    // the products above), so the next tile's K can go into it.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (j + 1 < j_end) dma_k(j + 1);
 
     if constexpr (DS > 1) {
       // Full scores = the DS partials summed in wave order, each element once:
@@ -986,11 +1026,9 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     mc_run = mc_new;
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] *= alpha;
-    // O^T += V^T P^T; the next tile's K is requested halfway, once the
-    // first half of V's registers are free
+    // O^T += V^T P^T
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      if (r == 8 && j + 1 < j_end) load_k(j + 1);
 #pragma unroll
       for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][b], s[r], o[b], 0, 0, 0);
     }
@@ -1007,11 +1045,11 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * hf + (r & 3);
       if constexpr (NB == 4 && DSLV <= DSL) {
-        // Staged in this wave's Q area (its last reader was this wave), row
+        // Staged in this wave's K area (no load is pending into it), row
         // lq's 16-byte chunk i in slot i ^ lq, then stored whole rows at a
         // time below: a direct store from these registers would write 32 B
         // to each of 32 rows per instruction.
-        *(f32x4*)(qsm + wave * 32 * DSL + lq * DSLV + 4 * (i ^ lq)) =
+        *(f32x4*)(kw + lq * DSLV + 4 * (i ^ lq)) =
             f32x4{o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv};
       } else if constexpr (NB == 4) {
         *(f32x4*)(orow + 4 * i) = f32x4{o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv};
@@ -1037,7 +1075,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int row = 2 * t + hf, c = lq;
-      const f32x4 val = *(const f32x4*)(qsm + wave * 32 * DSL + row * DSLV + 4 * (c ^ row));
+      const f32x4 val = *(const f32x4*)(kw + row * DSLV + 4 * (c ^ row));
       if (q_first + row < Nq) *(f32x4*)(obase + (size_t)(q_first + row) * DV + 4 * c) = val;
     }
   }

@@ -1,11 +1,11 @@
-"""Race check of the pipelined 16-bit forward: libfa_sync.so is the same
-source built with FA_SYNC_PHASES, in which every tile's loads complete and
-the whole workgroup meets at a barrier before any wave reads the tile, and
-barriers surround each epilogue staging phase.  Its arithmetic is the same,
-so on every shape its O and lse must equal libfa.so's bit for bit; a load
-that the pipelined kernel read too early, or a stage buffer overwritten while
-still being read, would show as a difference.  Both libraries are called
-through the C ABI.
+"""Race check of the pipelined forward kernels: libfa_sync.so is the same
+source built with FA_SYNC_PHASES, in which every tile's loads complete (and,
+in the 16-bit kernel, the whole workgroup meets at a barrier) before any wave
+reads the tile, and barriers surround each epilogue staging phase.  Its
+arithmetic is the same, so on every shape its O and lse must equal
+libfa.so's bit for bit; a load that the pipelined kernel read too early, or a
+stage buffer overwritten while still being read, would show as a difference.
+Both libraries are called through the C ABI.
 """
 import ctypes
 import math
@@ -19,7 +19,8 @@ from exact_attention_29_amd.inputs import make_qkv
 
 pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(fa.__file__))
-DT = {"bf16": (torch.bfloat16, fa.FA_DTYPE_BF16), "fp16": (torch.float16, fa.FA_DTYPE_FP16)}
+DT = {"bf16": (torch.bfloat16, fa.FA_DTYPE_BF16), "fp16": (torch.float16, fa.FA_DTYPE_FP16),
+      "fp32": (torch.float32, fa.FA_DTYPE_FP32)}
 
 
 @pytest.fixture(scope="module")
@@ -45,6 +46,12 @@ CASES = [
     ("fp16", 3, 5, 891, 891, 64, 64, True, None, None, False),
     ("bf16", 1, 4, 4096, 4096, 128, 128, True, None, None, True),      # key split
     ("fp16", 2, 2, 700, 2300, 64, 128, False, [2300, 1111], None, True),
+    # fp32: K tiles loaded into LDS behind the products, V rows into registers
+    ("fp32", 1, 1, 1024, 1024, 1024, 1024, False, None, None, True),  # the wide-head shape, key split
+    ("fp32", 2, 3, 333, 1000, 512, 512, True, [1000, 457], [333, 100], False),
+    ("fp32", 2, 4, 1500, 1500, 128, 128, True, None, None, False),
+    ("fp32", 3, 2, 777, 901, 64, 128, False, [901, 13], None, True),
+    ("fp32", 2, 2, 300, 300, 128, 64, True, [300, 299], [300, 31], False),
 ]
 
 
