@@ -896,18 +896,18 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   constexpr int CG = DSL / 32;
   float* const kw = ksm + wave * 32 * DSL;
   const unsigned kw_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)kw;
-  // Block (rg, cg) gets a descriptor of its own, based at its first row and
-  // column and ending at the last valid key row, so lane L's offset is the
-  // same for every block: row L/8, chunk (L%8) ^ (L/8) ^ (rg & 1).
+  // One descriptor per tile, based at its first key row and this wave's
+  // first column and ending at the last valid key row; lane L of block
+  // (rg, cg) reads row 8rg + L/8, chunk 8cg + ((L%8) ^ (L/8) ^ (rg & 1)).
   const int dma_lane0 = ((lane >> 3) * D + 4 * ((lane & 7) ^ (lane >> 3))) * 4;
   const int dma_lane1 = ((lane >> 3) * D + 4 * ((lane & 7) ^ (lane >> 3) ^ 1)) * 4;
   auto dma_k = [&](int j) {
+    const int k0 = j * BC;
+    const u32x4 desc = buffer_desc(K + khead + (size_t)k0 * D + col0, (unsigned)min(nk - k0, BC) * D * 4);
 #pragma unroll
     for (int blk = 0; blk < 4 * CG; ++blk) {
-      const int rg = blk / CG, cg = blk % CG, r0 = j * BC + 8 * rg;
-      const unsigned rows = (unsigned)min(max(nk - r0, 0), 8);
-      dma16(buffer_desc(K + khead + (size_t)r0 * D + col0 + 32 * cg, rows * D * 4), kw_lds + blk * 1024,
-            rg & 1 ? dma_lane1 : dma_lane0);
+      const int rg = blk / CG, cg = blk % CG;
+      dma16(desc, kw_lds + blk * 1024, (rg & 1 ? dma_lane1 : dma_lane0) + (8 * rg * D + 32 * cg) * 4);
     }
   };
   // where lane (key, h) reads chunk 2u + h of its key row
@@ -918,25 +918,25 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     return kread + ((c >> 3) * 64 + ((c & 7) ^ kri ^ (krg & 1))) * 4;
   };
   if (j_begin < j_end) dma_k(j_begin);
-  const int v_lane = (4 * hf * DV + colv0 + NB * lq) * 4;  // row 4h of a step, this lane's columns
+  const int v_lane = (4 * hf * DV + colv0 + NB * lq) * 4;  // row 4h of the tile, this lane's columns
   for (int j = j_begin; j < j_end; ++j) {
     const int k0 = j * BC;
     // V rows of tile j, requested before the score products so that they
     // arrive while those run: step r takes key 8(r/4) + 4h + r%4.  Buffer
-    // loads, one descriptor per step based at key k0 + 8(r/4) + r%4 and
-    // ending at the last valid key (rows past it read 0): exactly 16 load
-    // instructions, which the wait for this tile's K below counts.
+    // loads through one descriptor based at key k0 and ending at the last
+    // valid key (rows past it read 0): exactly 16 load instructions, which
+    // the wait for this tile's K below counts.
     float vv[16][NB];
+    const __amdgpu_buffer_rsrc_t vres = uniform_rsrc(V + vhead + (size_t)k0 * DV, min(nk - k0, BC) * DV * 4);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int r0 = k0 + 8 * (r >> 2) + (r & 3);
-      const __amdgpu_buffer_rsrc_t vres = uniform_rsrc(V + vhead + (size_t)r0 * DV, min(max(nk - r0, 0), 8) * DV * 4);
+      const int voff = v_lane + (8 * (r >> 2) + (r & 3)) * DV * 4;
       if constexpr (NB == 4) {
-        const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, v_lane, 0, 0));
+        const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff, 0, 0));
         vv[r][0] = t[0]; vv[r][1] = t[1]; vv[r][2] = t[2]; vv[r][3] = t[3];
       } else {
         static_assert(NB == 2, "V rows are 64 or 128 columns per wave");
-        const f32x2 t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(vres, v_lane, 0, 0));
+        const f32x2 t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(vres, voff, 0, 0));
         vv[r][0] = t[0]; vv[r][1] = t[1];
       }
     }
