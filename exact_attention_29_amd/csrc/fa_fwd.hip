@@ -872,14 +872,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int my_q = q_first + lq;
   const int col0 = wave * DSL, colv0 = wave * DSLV;
 
-  // Q rows in registers: lane (q, h) holds Q[q][col0 + 8u + 4h .. +3]
-  f32x4 qf[DSL / 8];
-  {
-    const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
-#pragma unroll
-    for (int u = 0; u < DSL / 8; ++u)
-      qf[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
-  }
+  f32x4 qf[DSL / 8];  // Q rows, loaded below
   f32x16 o[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) o[b] = f32x16{};
@@ -917,30 +910,45 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     const int c = 2 * u + hf;
     return kread + ((c >> 3) * 64 + ((c & 7) ^ kri ^ (krg & 1))) * 4;
   };
-  if (j_begin < j_end) dma_k(j_begin);
+  // V rows of a tile: step r takes key 8(r/4) + 4h + r%4.  Buffer loads
+  // through one descriptor per tile based at its first key and ending at the
+  // last valid key (rows past it read 0), one instruction per step, so that
+  // the wait for a tile's K below can count them.
   const int v_lane = (4 * hf * DV + colv0 + NB * lq) * 4;  // row 4h of the tile, this lane's columns
+  float vv[16][NB];
+  auto v_res = [&](int j) {
+    return uniform_rsrc(V + vhead + (size_t)j * BC * DV, min(nk - j * BC, BC) * DV * 4);
+  };
+  auto load_v = [&](__amdgpu_buffer_rsrc_t vres, int r) {
+    const int voff = v_lane + (8 * (r >> 2) + (r & 3)) * DV * 4;
+    if constexpr (NB == 4) {
+      const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff, 0, 0));
+      vv[r][0] = t[0]; vv[r][1] = t[1]; vv[r][2] = t[2]; vv[r][3] = t[3];
+    } else {
+      static_assert(NB == 2, "V rows are 64 or 128 columns per wave");
+      const f32x2 t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(vres, voff, 0, 0));
+      vv[r][0] = t[0]; vv[r][1] = t[1];
+    }
+  };
+  // first K tile, then Q; both are waited for before the first V rows are
+  // requested (V is not needed before the first P V product)
+  if (j_begin < j_end) dma_k(j_begin);
+  // Q rows in registers: lane (q, h) holds Q[q][col0 + 8u + 4h .. +3]
+  {
+    const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
+#pragma unroll
+    for (int u = 0; u < DSL / 8; ++u)
+      qf[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (j_begin < j_end) {
+    const __amdgpu_buffer_rsrc_t vres = v_res(j_begin);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load_v(vres, r);
+  }
   for (int j = j_begin; j < j_end; ++j) {
     const int k0 = j * BC;
-    // V rows of tile j, requested before the score products so that they
-    // arrive while those run: step r takes key 8(r/4) + 4h + r%4.  Buffer
-    // loads through one descriptor based at key k0 and ending at the last
-    // valid key (rows past it read 0): exactly 16 load instructions, which
-    // the wait for this tile's K below counts.
-    float vv[16][NB];
-    const __amdgpu_buffer_rsrc_t vres = uniform_rsrc(V + vhead + (size_t)k0 * DV, min(nk - k0, BC) * DV * 4);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int voff = v_lane + (8 * (r >> 2) + (r & 3)) * DV * 4;
-      if constexpr (NB == 4) {
-        const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff, 0, 0));
-        vv[r][0] = t[0]; vv[r][1] = t[1]; vv[r][2] = t[2]; vv[r][3] = t[3];
-      } else {
-        static_assert(NB == 2, "V rows are 64 or 128 columns per wave");
-        const f32x2 t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(vres, voff, 0, 0));
-        vv[r][0] = t[0]; vv[r][1] = t[1];
-      }
-    }
-    // this tile's K: issued before the 16 V loads, so done at vmcnt <= 16
+    // this tile's K: issued before its 16 V loads, so done at vmcnt <= 16
 #ifdef FA_SYNC_PHASES
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #else
@@ -1026,11 +1034,15 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     mc_run = mc_new;
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] *= alpha;
-    // O^T += V^T P^T
+    // O^T += V^T P^T; each step's V registers then take the next tile's
+    // rows of that step, so the loads spread over the products
+    const bool more = j + 1 < j_end;
+    const __amdgpu_buffer_rsrc_t vnext = v_res(more ? j + 1 : j);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][b], s[r], o[b], 0, 0, 0);
+      if (more) load_v(vnext, r);
     }
   }
 
