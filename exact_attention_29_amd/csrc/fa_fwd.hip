@@ -884,14 +884,13 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
   const int j_begin = SPLIT ? split * tps : 0;
   const int j_end = SPLIT ? min(ntiles, j_begin + tps) : ntiles;
 
-  // K tile j into this wave's LDS slice: the descriptor starts at the
-  // tile's first key and ends at the last valid one (rows past it read 0)
+  // K tile j into this wave's LDS slice, through one descriptor per tile
+  // based at its first key row and this wave's first column and ending at
+  // the last valid key row (rows past it read 0); lane L of block (rg, cg)
+  // reads row 8rg + L/8, chunk 8cg + ((L%8) ^ (L/8) ^ (rg & 1)).
   constexpr int CG = DSL / 32;
   float* const kw = ksm + wave * 32 * DSL;
   const unsigned kw_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)kw;
-  // One descriptor per tile, based at its first key row and this wave's
-  // first column and ending at the last valid key row; lane L of block
-  // (rg, cg) reads row 8rg + L/8, chunk 8cg + ((L%8) ^ (L/8) ^ (rg & 1)).
   const int dma_lane0 = ((lane >> 3) * D + 4 * ((lane & 7) ^ (lane >> 3))) * 4;
   const int dma_lane1 = ((lane >> 3) * D + 4 * ((lane & 7) ^ (lane >> 3) ^ 1)) * 4;
   auto dma_k = [&](int j) {
