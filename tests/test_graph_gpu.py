@@ -1,4 +1,5 @@
-"""HIP graph capture of the forward and gradient calls: each captured call
+"""HIP graph capture of the forward and gradient calls (bf16, and fp32 at
+d = 1024 and with per-batch counts): each captured call
 replays several times, with other eager work and synchronisations between
 the replays, and every replay must equal the eager result bit for bit (the
 persistent forward resets its work counters at the end of each launch, the
@@ -21,15 +22,17 @@ def gpu():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("B,H,N,d,causal,counts", [
-    (2, 8, 1024, 128, True, False),    # persistent forward
-    (1, 2, 4096, 128, False, False),   # key split of the 16-bit forward
-    (2, 4, 700, 64, True, False),      # one workgroup per block (d = 64)
-    (2, 4, 900, 128, True, True),      # per-batch key and query counts
+@pytest.mark.parametrize("dt,B,H,N,d,causal,counts", [
+    ("bf16", 2, 8, 1024, 128, True, False),    # persistent forward
+    ("bf16", 1, 2, 4096, 128, False, False),   # key split of the 16-bit forward
+    ("bf16", 2, 4, 700, 64, True, False),      # one workgroup per block (d = 64)
+    ("bf16", 2, 4, 900, 128, True, True),      # per-batch key and query counts
+    ("fp32", 1, 1, 1024, 1024, False, False),  # fp32 wide heads: eight waves, key split
+    ("fp32", 2, 3, 600, 128, True, True),      # fp32 with per-batch counts
 ])
-def test_captured_calls_replay_bitwise(B, H, N, d, causal, counts):
-    q, k, v = (t.cuda() for t in make_qkv(B, H, N, d, "bf16", 31 + N))
-    g = make_dout(B, H, N, d, "bf16", 32 + N).cuda()
+def test_captured_calls_replay_bitwise(dt, B, H, N, d, causal, counts):
+    q, k, v = (t.cuda() for t in make_qkv(B, H, N, d, dt, 31 + N))
+    g = make_dout(B, H, N, d, dt, 32 + N).cuda()
     kw = dict(causal=causal)
     if counts:
         kw.update(k_len=torch.tensor([N, N // 3], dtype=torch.int32, device="cuda"),
