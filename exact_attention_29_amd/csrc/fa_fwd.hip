@@ -929,16 +929,24 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
       vv[r][0] = t[0]; vv[r][1] = t[1];
     }
   };
-  // first K tile, then Q; both are waited for before the first V rows are
-  // requested (V is not needed before the first P V product)
-  if (j_begin < j_end) dma_k(j_begin);
-  // Q rows in registers: lane (q, h) holds Q[q][col0 + 8u + 4h .. +3]
+  // Q rows in registers: lane (q, h) holds Q[q][col0 + 8u + 4h .. +3],
+  // staged through this wave's LDS slice in the K layout (whole-line loads)
   {
-    const float* qrow = Q + head + (size_t)my_q * D + col0 + 4 * hf;
+    const u32x4 desc = buffer_desc(Q + head + (size_t)q_first * D + col0,
+                                   (unsigned)min(max(nq - q_first, 0), 32) * D * 4);
 #pragma unroll
-    for (int u = 0; u < DSL / 8; ++u)
-      qf[u] = (my_q < nq) ? *(const f32x4*)(qrow + 8 * u) : f32x4{0, 0, 0, 0};
+    for (int blk = 0; blk < 4 * CG; ++blk) {
+      const int rg = blk / CG, cg = blk % CG;
+      dma16(desc, kw_lds + blk * 1024, (rg & 1 ? dma_lane1 : dma_lane0) + (8 * rg * D + 32 * cg) * 4);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+    for (int u = 0; u < DSL / 8; ++u) qf[u] = *(const f32x4*)kslot(u);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slice is read before K overwrites it
   }
+  // first K tile; waited for before the first V rows are requested (V is
+  // not needed before the first P V product)
+  if (j_begin < j_end) dma_k(j_begin);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if (j_begin < j_end) {
     const __amdgpu_buffer_rsrc_t vres = v_res(j_begin);
