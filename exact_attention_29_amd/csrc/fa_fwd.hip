@@ -1113,7 +1113,10 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
                                                         int n_split) {
   constexpr int TPR = D / 4, RPB = TPR >= 256 ? 1 : 256 / TPR;  // threads per row, rows per block
   const int t = threadIdx.x % TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  // Row blocks go to XCDs in contiguous ranges, as the split kernel's query
+  // blocks did, so that a row's partials are mostly read from the L2 of the
+  // XCD that wrote them.
+  const long long row = (long long)xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;
   if (threadIdx.x / TPR >= RPB || row >= rows) return;
   // The splits are read kCombineBatch at a time, all loads of a batch issued
   // before any is used; the sums still run over the splits in order.
