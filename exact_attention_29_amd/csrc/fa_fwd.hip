@@ -755,7 +755,8 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
                                                        int n_split) {
   constexpr int TPR = DV / 8, RPB = 256 / TPR;  // threads per row, rows per block
   const int t = threadIdx.x % TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  // row blocks on XCDs as the split kernel's blocks were (see attn_combine_f32)
+  const long long row = (long long)xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   // shares read kCombineBatch at a time, as in attn_combine_f32
   float bmax = -INFINITY;
