@@ -1042,15 +1042,21 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
     mc_run = mc_new;
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] *= alpha;
-    // O^T += V^T P^T; each step's V registers then take the next tile's
-    // rows of that step, so the loads spread over the products
+    // O^T += V^T P^T; the next tile's V rows of step r go into that step's
+    // registers four steps later, so the loads spread over the products and
+    // never wait for a product that still has to read the registers
+    constexpr int LAG = 4;
     const bool more = j + 1 < j_end;
     const __amdgpu_buffer_rsrc_t vnext = v_res(more ? j + 1 : j);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][b], s[r], o[b], 0, 0, 0);
-      if (more) load_v(vnext, r);
+      if (more && r >= LAG) load_v(vnext, r - LAG);
+    }
+    if (more) {
+#pragma unroll
+      for (int r = 16 - LAG; r < 16; ++r) load_v(vnext, r);
     }
   }
 
