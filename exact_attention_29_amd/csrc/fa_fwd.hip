@@ -199,78 +199,6 @@ __device__ __forceinline__ void leave_launch(int slot, unsigned long long tag) {
 }
 
 // ---------------------------------------------------------------------------
-// Products of the 16-bit kernel at one wave per SIMD (RB = 2), written as
-// inline asm so that each operand sits in the register file chosen for it:
-// the scores accumulate in VGPRs (the vector unit reads them), Q is read from
-// AGPRs and O accumulates in AGPRs (only the products touch them), which is
-// what lets one wave hold 64 query rows.  The compiler cannot see into these
-// statements, so the kernel itself keeps the distances the ISA requires
-// around them: 12 wait states between a product and any other instruction
-// that reads its result (kMfmaResultWait), 1 between a vector write and a
-// product that reads the register.  Products that accumulate into exactly
-// the registers of the previous product need none.
-#define FA_MFMA32_FORMS(TRAITS, OPC)                                                             \
-  template <>                                                                                    \
-  struct Mfma32<TRAITS> {                                                                        \
-    /* d = a b, b from AGPRs, d in VGPRs */                                                      \
-    static __device__ __forceinline__ void zv(u32x4 a, u32x4 b, f32x16& d) {                    \
-      asm volatile(OPC " %0, %1, %2, 0" : "=v"(d) : "v"(a), "a"(b));                             \
-    }                                                                                            \
-    /* d += a b, b from AGPRs, d in VGPRs */                                                     \
-    static __device__ __forceinline__ void accv(u32x4 a, u32x4 b, f32x16& d) {                  \
-      asm volatile(OPC " %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));                            \
-    }                                                                                            \
-    /* d += a b, d in AGPRs */                                                                   \
-    static __device__ __forceinline__ void acca(u32x4 a, u32x4 b, f32x16& d) {                  \
-      asm volatile(OPC " %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));                            \
-    }                                                                                            \
-  };
-template <class TT>
-struct Mfma32;
-FA_MFMA32_FORMS(Bf16, "v_mfma_f32_32x32x16_bf16")
-FA_MFMA32_FORMS(F16, "v_mfma_f32_32x32x16_f16")
-#undef FA_MFMA32_FORMS
-
-// Wait states after products before another instruction reads their results
-// (12), and after vector writes before a product reads them (1).  Each
-// statement names the registers it guards as read-written operands, so the
-// compiler places every later access to them after it.
-__device__ __forceinline__ void mfma_result_wait_v(f32x16& a, f32x16& b) {
-  asm volatile("s_nop 11" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void mfma_result_wait_a(f32x16 (&o)[4]) {
-  asm volatile("s_nop 11" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
-}
-__device__ __forceinline__ void order_after_a(f32x16 (&o)[4]) {
-  asm volatile("" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
-}
-__device__ __forceinline__ void valu_to_mfma_wait_v(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
-  asm volatile("s_nop 0" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-
-// One wave's share of a K (V) tile of ROWS keys in the TileLayout blocks:
-// blocks wave, wave + NW, ... of its (ROWS / 16) * D / 32.
-template <int D, bool IS_V, int NW, int ROWS>
-__device__ __forceinline__ void dma_tile_rows(u32x4 desc, unsigned lds_tile, int wave, int lane) {
-  using L = TileLayout<D>;
-  constexpr int BLOCKS = ROWS / 16 * L::CG;
-  static_assert(BLOCKS % NW == 0, "tile blocks split evenly over the waves");
-#pragma unroll
-  for (int i = 0; i < BLOCKS / NW; ++i) {
-    const int blk = wave + i * NW;
-    dma16(desc, lds_tile + blk * 1024, (IS_V ? L::v_src(blk, lane) : L::k_src(blk, lane)) * 2);
-  }
-}
-
-// A 16-byte value moved into AGPRs (the tied operand makes the compiler
-// place it there; later statements read it with an "a" constraint).
-__device__ __forceinline__ u32x4 to_agpr(u32x4 x) {
-  u32x4 r;
-  asm volatile("" : "=a"(r) : "0"(x));
-  return r;
-}
-
-// ---------------------------------------------------------------------------
 // bf16 / fp16 kernel, software-pipelined
 //
 // A wave issues in order, so its matrix-core work overlaps its vector work
@@ -307,8 +235,8 @@ __device__ __forceinline__ u32x4 to_agpr(u32x4 x) {
 // weight sum (fp32, Opart[s]) and the log2 weight of the share,
 // mc + log2(l) (Lpart[s]); attn_combine_sp merges them.  A share with no
 // kept key of a row writes 0 and -inf.
-template <class TT, int DK, int DV, bool CAUSAL, int NW, int NS, bool PERSIST, bool SPLIT, int RB>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 ? 1 : DK + DV == 128 ? 3 : 2, RB > 1 ? 1 : DK + DV == 128 ? 3 : 2))) void attn_fwd_sp(
+template <class TT, int DK, int DV, bool CAUSAL, int NW, int NS, bool PERSIST, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV == 128 ? 3 : 2, DK + DV == 128 ? 3 : 2))) void attn_fwd_sp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Nq, int Nk, int H, const int* __restrict__ k_len, const int* __restrict__ q_len,
@@ -316,20 +244,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
     float* __restrict__ Lpart) {
   static_assert(!(SPLIT && PERSIST), "a split launch has one workgroup per item");
   // DK: head dim of Q and K (the scores); DV: head dim of V and O
-  // keys per tile: 64, or 32 with two row blocks per wave (the same products
-  // per wave and tile, and half the score registers)
-  constexpr int BR = 32 * RB * NW, BC = RB > 1 ? 32 : 64;
-  constexpr bool AS = RB > 1;  // products as inline asm, Q and O in AGPRs
-  static_assert(!AS || (DK == 128 && DV == 128 && RB == 2), "two row blocks per wave at d = 128 only");
+  constexpr int BR = 32 * NW, BC = 64;
   using LK = TileLayout<DK>;
   using LV = TileLayout<DV>;
-  constexpr int CGK = LK::CG, CGV = LV::CG;
-  constexpr int KBLK = BC / 16 * CGK, VBLK = BC / 16 * CGV;  // 1 KB blocks of a K / V tile
-  constexpr int TBK = KBLK * 1024, TBV = VBLK * 1024;
+  constexpr int TBK = LK::BYTES, TBV = LV::BYTES, CGK = LK::CG, CGV = LV::CG;
   constexpr int SB = TBK + TBV;  // bytes of one stage (K tile, then V tile)
   // DMA instructions one wave issues for a K tile and for a V tile
-  constexpr int NDK = KBLK / NW, NDV = VBLK / NW;
-  static_assert(KBLK % NW == 0 && VBLK % NW == 0 && NS >= 2, "stages split evenly over the waves");
+  constexpr int NDK = LK::BLOCKS / NW, NDV = LV::BLOCKS / NW;
+  static_assert(LK::BLOCKS % NW == 0 && LV::BLOCKS % NW == 0 && NS >= 2,
+                "stages split evenly over the waves");
   static_assert(DK == DV || NS == 2, "more than two stages only with equal head dims");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SB];  // [stage buffer][K, V]
   // O staging in the epilogue: per wave 32 rows x 64 columns (bf16) at a
@@ -382,14 +305,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
     const int diag = nk - nq;
     const size_t qhead = (size_t)bh * Nq * DK, ohead = (size_t)bh * Nq * DV;
     const size_t khead = (size_t)bh * Nk * DK, vhead = (size_t)bh * Nk * DV;
-    // this wave's rows: RB blocks of 32 from q_first; lane lq has row
-    // q_first + 32 rb + lq of block rb
-    const int q_first = qt * BR + 32 * RB * wave;
-    int my_q[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) my_q[rb] = q_first + 32 * rb + lq;
+    const int q_first = qt * BR + 32 * wave;
+    const int my_q = q_first + lq;
 
-    u32x4 qf[RB][DK / 16];
+    u32x4 qf[DK / 16];
 
     const int kv_end = qt * BR >= nq ? 0 : CAUSAL ? min(nk, min((qt + 1) * BR, nq) + diag) : nk;
     const int T_all = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
@@ -397,7 +316,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
     // them unsplit); tile t below is key tile tile0 + t
     const int tile0 = SPLIT ? (int)((long long)T_all * split / n_split) : 0;
     const int T = SPLIT ? (int)((long long)T_all * (split + 1) / n_split) - tile0 : T_all;
-    const int last_key = q_first + 32 * RB - 1 + diag;  // this wave's last kept key (causal)
+    const int last_key = q_first + 31 + diag;  // this wave's last kept key (causal)
     const int my_T_all = CAUSAL ? (last_key < 0 ? 0 : min(T_all, last_key / BC + 1)) : T_all;
     // A wave whose rows all lie past nq (the ragged last block, padding; a
     // single decoding query leaves seven of eight waves so) only helps load
@@ -417,11 +336,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
       const unsigned base = lds0 + ((st + 1) % NS) * SB;
       if (st + 1 < T) {
         const int k0 = (tile0 + st + 1) * BC;
-        dma_tile_rows<DK, false, NW, BC>(buffer_desc(kbase + (size_t)k0 * DK, (unsigned)(nk - k0) * DK * 2), base, wave, lane);
+        dma_tile<DK, false, NW>(buffer_desc(kbase + (size_t)k0 * DK, (unsigned)(nk - k0) * DK * 2), base, 0, wave, lane);
       }
       if (st >= 0) {
         const int k0 = (tile0 + st) * BC;
-        dma_tile_rows<DV, true, NW, BC>(buffer_desc(vbase + (size_t)k0 * DV, (unsigned)(nk - k0) * DV * 2), base + TBK, wave, lane);
+        dma_tile<DV, true, NW>(buffer_desc(vbase + (size_t)k0 * DV, (unsigned)(nk - k0) * DV * 2), base + TBK, 0, wave, lane);
       }
     };
     auto stage_buf = [&](int st) { return (st + 1) % NS; };
@@ -430,41 +349,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
     const int v_lane = (4 * (tr_grp >> 1) + (tr_i >> 2)) * 64 + (2 * (tr_grp & 1) + ((tr_i & 3) >> 1)) * 16 +
                        8 * (tr_i & 1);
 
-    f32x16 o[RB][DV / 32];
-    // running state per row block: row max m, its scaled reference mc
-    // (exponents are taken against mc) and the fp32 sum l of the weights
-    float m_run[RB], mc_run[RB], l_run[RB];
+    f32x16 o[DV / 32];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int b = 0; b < DV / 32; ++b) o[rb][b] = f32x16{};
-      m_run[rb] = -INFINITY;
-      mc_run[rb] = -INFINITY;
-      l_run[rb] = 0.f;
-    }
+    for (int b = 0; b < DV / 32; ++b) o[b] = f32x16{};
+    // running state: row max m, its scaled reference mc (exponents are taken
+    // against mc) and the fp32 sum l of the weights
+    float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
     const float c2 = scale * kLog2e;
-    u32x4 pf[RB][BC / 16];  // P_j packed, B operand of the P V product
+    u32x4 pf[BC / 16];  // P_j packed, B operand of the P V product
 
-    // Each K (V) operand read from LDS feeds the products of all RB row blocks.
-    auto qk = [&](const uint8_t* kt, f32x16 (&acc)[RB][BC / 32]) {
+    auto qk = [&](const uint8_t* kt, f32x16 (&acc)[BC / 32]) {
 #pragma unroll
       for (int b = 0; b < BC / 32; ++b) {
-        if constexpr (!AS) {
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[rb][b] = f32x16{};
-        }
+        acc[b] = f32x16{};
 #pragma unroll
         for (int c = 0; c < DK / 16; ++c) {
           const u32x4 a = *(const u32x4*)(kt + k_lane + (2 * b * CGK + (c >> 1)) * 1024 + (c & 1) * 512);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            if constexpr (AS) {
-              if (c == 0) Mfma32<TT>::zv(a, qf[rb][c], acc[rb][b]);
-              else Mfma32<TT>::accv(a, qf[rb][c], acc[rb][b]);
-            } else {
-              acc[rb][b] = TT::mma(a, qf[rb][c], acc[rb][b]);
-            }
-          }
+          acc[b] = TT::mma(a, qf[c], acc[b]);
         }
       }
     };
@@ -477,19 +378,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const u32x4 vo = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-            if constexpr (AS) Mfma32<TT>::acca(vo, pf[rb][cc], o[rb][b]);
-            else o[rb][b] = TT::mma(vo, pf[rb][cc], o[rb][b]);
-          }
+          o[b] = TT::mma(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pf[cc], o[b]);
         }
     };
-    // Tile t's mask (if any), row max and reference move for row block rb.
-    // Returns the factor for O, which the caller applies after O has received
-    // the previous tile; l is rescaled here.  `resc` tells whether any row of
-    // the block moved.
-    auto part1 = [&](f32x16 (&sv)[BC / 32], int rb, int t, bool masked, bool& resc) -> float {
+    // Tile t's mask (if any), row max and reference move.  Returns the factor
+    // for O, which the caller applies after O has received the previous tile;
+    // l is rescaled here.  `resc` tells whether any row moved.
+    auto part1 = [&](f32x16 (&sv)[BC / 32], int t, bool masked, bool& resc) -> float {
       if (masked) {
         const int k0 = (tile0 + t) * BC;
 #pragma unroll
@@ -497,7 +392,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool keep = key < nk && (!CAUSAL || key <= my_q[rb] + diag);
+            const bool keep = key < nk && (!CAUSAL || key <= my_q + diag);
             if (!keep) sv[b][r] = -INFINITY;
           }
       }
@@ -507,18 +402,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[b][r]);
       mt = half_max(mt);
-      m_run[rb] = fmaxf(m_run[rb], mt);
-      const float mc_cand = (m_run[rb] == -INFINITY) ? -INFINITY : m_run[rb] * c2;
-      resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run[rb] + kLazyRescale) != 0;
+      m_run = fmaxf(m_run, mt);
+      const float mc_cand = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
+      resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
       // 0 for a row's first finite tile; a still fully masked row keeps alpha 1
-      const float alpha = (!resc || mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run[rb] - mc_cand);
-      mc_run[rb] = resc ? mc_cand : mc_run[rb];
-      l_run[rb] *= alpha;
+      const float alpha = (!resc || mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
+      mc_run = resc ? mc_cand : mc_run;
+      l_run *= alpha;
       return alpha;
     };
     // Exponentials against the current reference, their sum, and P packed.
-    auto part2 = [&](f32x16 (&sv)[BC / 32], int rb) {
-      const float off = (mc_run[rb] == -INFINITY) ? 0.f : mc_run[rb];
+    auto part2 = [&](f32x16 (&sv)[BC / 32]) {
+      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
       float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < BC / 32; ++b)
@@ -532,10 +427,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
       for (int c = 0; c < BC / 16; ++c) {
         const int r0 = 8 * (c & 1);
         const f32x16& sb = sv[c >> 1];
-        pf[rb][c] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
-                          TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
+        pf[c] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
+                      TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
       }
-      l_run[rb] += ls[0] + ls[1];
+      l_run += ls[0] + ls[1];
     };
     auto tile_masked = [&](int t) {
       const int k0 = (tile0 + t) * BC;
@@ -544,20 +439,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
 
     // One steady-state step (tile j's softmax and product, tile j+1's scores
     // and statistics), written in issue order and fenced so that every MFMA is
-    // followed by the independent vector work that hides it.  With RB row
-    // blocks, each operand read from LDS is followed by one MFMA per block,
-    // each with that block's share of the vector work.
-    auto steady = [&](f32x16 (&cur)[RB][BC / 32], f32x16 (&nxt)[RB][BC / 32], const uint8_t* kt,
+    // followed by the independent vector work that hides it.
+    auto steady = [&](f32x16 (&cur)[BC / 32], f32x16 (&nxt)[BC / 32], const uint8_t* kt,
                       const uint8_t* vt, int t_next, bool mask_next) {
       constexpr int NQK = BC / 32 * DK / 16, NPV = BC / 16 * DV / 32;
-      constexpr int ELEM = BC / 2;  // scores of a tile held by one lane, per row block
-      float off[RB], ls0[RB], ls1[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        off[rb] = (mc_run[rb] == -INFINITY) ? 0.f : mc_run[rb];
-        ls0[rb] = 0.f;
-        ls1[rb] = 0.f;
-      }
+      constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
+      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
+      float ls0 = 0.f, ls1 = 0.f;
       // ---- step A: S_{j+1} (MFMA) with exp / sums / packing of tile j (VALU)
       auto kaddr = [&](int i) {
         const int bb = i / (DK / 16), c = i % (DK / 16);
@@ -573,36 +461,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
       for (int i = 0; i < NQK; ++i) {
         if (i + KP < NQK) kop[(i + KP) % (KP + 1)] = *kaddr(i + KP);
         const int bb = i / (DK / 16), c = i % (DK / 16);
+        nxt[bb] = TT::mma(kop[i % (KP + 1)], qf[c], c == 0 ? f32x16{} : nxt[bb]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if constexpr (AS) {
-            if (c == 0) Mfma32<TT>::zv(kop[i % (KP + 1)], qf[rb][c], nxt[rb][bb]);
-            else Mfma32<TT>::accv(kop[i % (KP + 1)], qf[rb][c], nxt[rb][bb]);
-          } else {
-            nxt[rb][bb] = TT::mma(kop[i % (KP + 1)], qf[rb][c], c == 0 ? f32x16{} : nxt[rb][bb]);
+        for (int e = EPM * i; e < EPM * (i + 1); ++e) {
+          const float pe = fast_exp2(fmaf(cur[e >> 4][e & 15], c2, -off));
+          cur[e >> 4][e & 15] = pe;
+          if (e & 1) ls1 += pe; else ls0 += pe;
+          if ((e & 7) == 7) {  // a 16-key chunk's probabilities are complete: pack them
+            const int cc = e >> 3, r0 = 8 * (cc & 1);
+            const f32x16& sb = cur[cc >> 1];
+            pf[cc] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
+                           TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
           }
-#pragma unroll
-          for (int e = EPM * i; e < EPM * (i + 1); ++e) {
-            const float pe = fast_exp2(fmaf(cur[rb][e >> 4][e & 15], c2, -off[rb]));
-            cur[rb][e >> 4][e & 15] = pe;
-            if (e & 1) ls1[rb] += pe; else ls0[rb] += pe;
-            if ((e & 7) == 7) {  // a 16-key chunk's probabilities are complete: pack them
-              const int cc = e >> 3, r0 = 8 * (cc & 1);
-              const f32x16& sb = cur[rb][cc >> 1];
-              pf[rb][cc] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
-                                 TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
-              // One wave per SIMD: nothing else hides a run of vector work, so
-              // the chunk's exponentials, sums and packing are pinned here,
-              // between the products, instead of being sunk past the mask
-              // branch below next to their first use.
-              if constexpr (AS) asm volatile("" : "+v"(pf[rb][cc]), "+v"(ls0[rb]), "+v"(ls1[rb]));
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls0[rb] + ls1[rb];
+      l_run += ls0 + ls1;
       // ---- step B: O += P_j V_j (MFMA) with tile j+1's row max (VALU)
       auto vaddr = [&](int i) {
         const int cc = i / (DV / 32), bb = i % (DV / 32);
@@ -622,16 +496,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
       if (mask_next) {
         // keys past the row (causal) or past the valid keys score -inf: lane
         // (q, h) keeps key offsets 32b + 8(r/4) + r%4 <= lim within tile t_next
-        if constexpr (AS) mfma_result_wait_v(nxt[0][0], nxt[1][0]);  // the last score products were just issued
+        const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1) - ((tile0 + t_next) * BC + 4 * hf);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int lim = min(CAUSAL ? my_q[rb] + diag : nk - 1, nk - 1) - ((tile0 + t_next) * BC + 4 * hf);
+        for (int b = 0; b < BC / 32; ++b)
 #pragma unroll
-          for (int b = 0; b < BC / 32; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (32 * b + 8 * (r >> 2) + (r & 3) > lim) nxt[rb][b][r] = -INFINITY;
-        }
+          for (int r = 0; r < 16; ++r)
+            if (32 * b + 8 * (r >> 2) + (r & 3) > lim) nxt[b][r] = -INFINITY;
       }
       // Raised wave priority while this wave feeds the matrix core: when the
       // other wave on the SIMD is in its exponential-heavy step, the arbiter
@@ -639,190 +509,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
       // vector instructions.
       __builtin_amdgcn_s_setprio(2);
       __builtin_amdgcn_sched_barrier(0);
-      float mt0[RB], mt1[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        mt0[rb] = -INFINITY;
-        mt1[rb] = -INFINITY;
-      }
+      float mt0 = -INFINITY, mt1 = -INFINITY;
       constexpr int MPM = (ELEM / 2 + NPV - 3) / (NPV - 2);  // score pairs per MFMA from the third on
       int e = 0;
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         if (i + VP < NPV) vop[(i + VP) % (VP + 1)] = vload(i + VP);
         const int cc = i / (DV / 32), bb = i % (DV / 32);
-        const int e_start = e;
+        o[bb] = TT::mma(vop[i % (VP + 1)], pf[cc], o[bb]);
+        if (i >= 2) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if constexpr (AS) Mfma32<TT>::acca(vop[i % (VP + 1)], pf[rb][cc], o[rb][bb]);
-          else o[rb][bb] = TT::mma(vop[i % (VP + 1)], pf[rb][cc], o[rb][bb]);
-          e = e_start;
-          if (i >= 2) {
-#pragma unroll
-            for (int k = 0; k < MPM; ++k) {
-              if (e < ELEM / 2) {  // two scores of tile j+1 per max3
-                const int e0 = 2 * e, e1 = 2 * e + 1;
-                if (e & 1) mt1[rb] = max3(mt1[rb], nxt[rb][e0 >> 4][e0 & 15], nxt[rb][e1 >> 4][e1 & 15]);
-                else mt0[rb] = max3(mt0[rb], nxt[rb][e0 >> 4][e0 & 15], nxt[rb][e1 >> 4][e1 & 15]);
-                ++e;
-              }
+          for (int k = 0; k < MPM; ++k) {
+            if (e < ELEM / 2) {  // two scores of tile j+1 per max3
+              const int e0 = 2 * e, e1 = 2 * e + 1;
+              if (e & 1) mt1 = max3(mt1, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
+              else mt0 = max3(mt0, nxt[e0 >> 4][e0 & 15], nxt[e1 >> 4][e1 & 15]);
+              ++e;
             }
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
       // tile j+1's statistics; a row whose keys in this tile are all masked
       // keeps its max (the kept keys are a prefix, so tile 0 gave every row
       // with a kept key a finite one; a row without any stays at -inf)
+      const float mt = half_max(max3(mt0, mt1, mt1));
+      m_run = fmaxf(m_run, mt);
+      const float mc_cand = m_run * c2;
+      const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0;
+      if (resc) {
+        const float alpha = mc_cand == -INFINITY ? 1.f : fast_exp2(mc_run - mc_cand);
+        mc_run = mc_cand;
+        l_run *= alpha;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float mt = half_max(max3(mt0[rb], mt1[rb], mt1[rb]));
-        m_run[rb] = fmaxf(m_run[rb], mt);
-        const float mc_cand = m_run[rb] * c2;
-        const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run[rb] + kLazyRescale) != 0;
-        if (resc) {
-          if constexpr (AS) mfma_result_wait_a(o[rb]);  // O's last products were just issued
-          const float alpha = mc_cand == -INFINITY ? 1.f : fast_exp2(mc_run[rb] - mc_cand);
-          mc_run[rb] = mc_cand;
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int bb = 0; bb < DV / 32; ++bb) o[rb][bb] *= alpha;
-        }
+        for (int bb = 0; bb < DV / 32; ++bb) o[bb] *= alpha;
       }
-    };
-
-    // The steady step at one wave per SIMD (RB = 2, 32-key tiles).  A single
-    // wave issues in order, so after each product it may issue only as much
-    // vector work as the matrix core takes for that product; the
-    // exponentials (quarter-rate instructions) are spread over three phases,
-    // each slot issuing one product per row block:
-    //   A  (8 slots): S_{j+1} = K_{j+1} Q^T, with tile j's first 16 keys (one
-    //                 exponential per product);
-    //   B1 (4 slots): O += P_j V_j over those keys, with tile j's last 16 keys
-    //                 (two per product);
-    //   B2 (4 slots): O += P_j V_j over the last 16 keys, with tile j+1's
-    //                 mask and row max.
-    // The sums, the packing and the max run in the same order as in the
-    // two-waves-per-SIMD step, so the results are the same.
-    auto steady1w = [&](f32x16 (&cur)[RB][BC / 32], f32x16 (&nxt)[RB][BC / 32], const uint8_t* kt,
-                        const uint8_t* vt, int t_next, bool mask_next) {
-     if constexpr (AS) {
-      static_assert(BC == 32 && DK == 128 && DV == 128, "one key block and four O blocks per row block");
-      constexpr int NQK = DK / 16, NPV = 2 * (DV / 32);  // 8 and 8 slots
-      float off[RB], ls0[RB], ls1[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        off[rb] = (mc_run[rb] == -INFINITY) ? 0.f : mc_run[rb];
-        ls0[rb] = 0.f;
-        ls1[rb] = 0.f;
-      }
-      // exponential of tile j's element e of row block rb, its sum, and the
-      // packing of its 16-key chunk once the chunk is complete
-      auto expo = [&](int rb, int e) {
-        const float pe = fast_exp2(fmaf(cur[rb][0][e], c2, -off[rb]));
-        cur[rb][0][e] = pe;
-        if (e & 1) ls1[rb] += pe; else ls0[rb] += pe;
-        if ((e & 7) == 7) {
-          const int cc = e >> 3, r0 = 8 * cc;
-          const f32x16& sb = cur[rb][0];
-          pf[rb][cc] = u32x4{TT::pack(sb[r0 + 0], sb[r0 + 1]), TT::pack(sb[r0 + 2], sb[r0 + 3]),
-                             TT::pack(sb[r0 + 4], sb[r0 + 5]), TT::pack(sb[r0 + 6], sb[r0 + 7])};
-          // pinned here, between the products (the compiler would otherwise
-          // sink this vector work next to its first use)
-          asm volatile("" : "+v"(pf[rb][cc]), "+v"(ls0[rb]), "+v"(ls1[rb]));
-        }
-      };
-      // ---- A
-      auto kaddr = [&](int c) {
-        return (const u32x4*)(kt + k_lane + (c >> 1) * 1024 + (c & 1) * 512);
-      };
-      constexpr int KP = 4;  // K operands in flight ahead of the matrix core
-      u32x4 kop[KP + 1];
-#pragma unroll
-      for (int i = 0; i < KP; ++i) kop[i] = *kaddr(i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        if (i + KP < NQK) kop[(i + KP) % (KP + 1)] = *kaddr(i + KP);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if (i == 0) Mfma32<TT>::zv(kop[i % (KP + 1)], qf[rb][i], nxt[rb][0]);
-          else Mfma32<TT>::accv(kop[i % (KP + 1)], qf[rb][i], nxt[rb][0]);
-          expo(rb, i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // ---- B1, B2
-      auto vload = [&](int i) {
-        const uint8_t* va = vt + v_lane + ((i >> 2) * CGV + (i & 3)) * 1024;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 512));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-      };
-      constexpr int VP = 4;  // V operands in flight ahead of the matrix core
-      u32x4 vop[VP + 1];
-#pragma unroll
-      for (int i = 0; i < VP; ++i) vop[i] = vload(i);
-      __builtin_amdgcn_sched_barrier(0);
-      float mt0[RB], mt1[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        mt0[rb] = -INFINITY;
-        mt1[rb] = -INFINITY;
-      }
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        if (i + VP < NPV) vop[(i + VP) % (VP + 1)] = vload(i + VP);
-        if (i == NPV / 2 && mask_next) {
-          // keys past the row (causal) or past the valid keys score -inf:
-          // lane (q, h) keeps key offsets 8(r/4) + r%4 <= lim within tile t_next
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int lim = min(CAUSAL ? my_q[rb] + diag : nk - 1, nk - 1) - ((tile0 + t_next) * BC + 4 * hf);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (8 * (r >> 2) + (r & 3) > lim) nxt[rb][0][r] = -INFINITY;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          Mfma32<TT>::acca(vop[i % (VP + 1)], pf[rb][i >> 2], o[rb][i & 3]);
-          if (i < NPV / 2) {
-            expo(rb, 8 + 2 * i);
-            expo(rb, 9 + 2 * i);
-          } else {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {  // two scores of tile j+1 per max3, pairs in order
-              const int p = 2 * (i - NPV / 2) + k;
-              if (p & 1) mt1[rb] = max3(mt1[rb], nxt[rb][0][2 * p], nxt[rb][0][2 * p + 1]);
-              else mt0[rb] = max3(mt0[rb], nxt[rb][0][2 * p], nxt[rb][0][2 * p + 1]);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls0[rb] + ls1[rb];
-      // tile j+1's statistics (as in the two-waves-per-SIMD step)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float mt = half_max(max3(mt0[rb], mt1[rb], mt1[rb]));
-        m_run[rb] = fmaxf(m_run[rb], mt);
-        const float mc_cand = m_run[rb] * c2;
-        const bool resc = __builtin_amdgcn_ballot_w64(mc_cand > mc_run[rb] + kLazyRescale) != 0;
-        if (resc) {
-          mfma_result_wait_a(o[rb]);  // O's last products were just issued
-          const float alpha = mc_cand == -INFINITY ? 1.f : fast_exp2(mc_run[rb] - mc_cand);
-          mc_run[rb] = mc_cand;
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int bb = 0; bb < DV / 32; ++bb) o[rb][bb] *= alpha;
-        }
-      }
-     }
     };
 
     // Stages are issued AHEAD = NS-1 iterations early: iteration j issues stage
@@ -871,29 +593,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
     };
 
     // prologue: stages -1 (K_0), 0 (K_1, V_0), ..., NS-2; S_0 and its statistics
-    f32x16 sA[RB][BC / 32], sB[RB][BC / 32];
+    f32x16 sA[BC / 32], sB[BC / 32];
     load_stage(-1);
 #pragma unroll
     for (int st = 0; st <= NS - 2; ++st)
       if (st < T) load_stage(st);
     // Q after the first stages: its latency overlaps theirs
+    if (my_q < nq) {
+      const uint16_t* qrow = Q + qhead + (size_t)my_q * DK + 8 * hf;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (my_q[rb] < nq) {
-        const uint16_t* qrow = Q + qhead + (size_t)my_q[rb] * DK + 8 * hf;
+      for (int c = 0; c < DK / 16; ++c) qf[c] = *(const u32x4*)(qrow + 16 * c);
+    } else {
 #pragma unroll
-        for (int c = 0; c < DK / 16; ++c) {
-          const u32x4 qv = *(const u32x4*)(qrow + 16 * c);
-          if constexpr (AS) qf[rb][c] = to_agpr(qv);
-          else qf[rb][c] = qv;
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < DK / 16; ++c) {
-          if constexpr (AS) qf[rb][c] = to_agpr(u32x4{0, 0, 0, 0});
-          else qf[rb][c] = u32x4{0, 0, 0, 0};
-        }
-      }
+      for (int c = 0; c < DK / 16; ++c) qf[c] = u32x4{0, 0, 0, 0};
     }
     // stages -1 and 0 must be in; stages 1 .. NS-2 may stay in flight
     {
@@ -908,13 +620,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
     // scores are then all masked, so the steady steps below see -inf instead
     // of stale registers.  An idle wave runs no steady step at all.
     if (0 < T && !idle) {
+      bool resc;
       qk(smem + stage_buf(-1) * SB, sA);
-      if constexpr (AS) mfma_result_wait_v(sA[0][0], sA[1][0]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        bool resc;
-        part1(sA[rb], rb, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
-      }
+      part1(sA, 0, tile_masked(0), resc);  // O is still zero: its factor is not needed
     }
     __syncthreads();  // every wave is done with stage -1's buffer before it is refilled
 
@@ -927,13 +635,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
       issue_for(j);
       {
         const uint8_t* kt = smem + stage_buf(j) * SB;
-        if (!idle) { if constexpr (AS) steady1w(sA, sB, kt, kt + TBK, j + 1, tile_masked(j + 1)); else steady(sA, sB, kt, kt + TBK, j + 1, tile_masked(j + 1)); }
+        if (!idle) steady(sA, sB, kt, kt + TBK, j + 1, tile_masked(j + 1));
       }
       end_iter(j);
       issue_for(j + 1);
       {
         const uint8_t* kt = smem + stage_buf(j + 1) * SB;
-        if (!idle) { if constexpr (AS) steady1w(sB, sA, kt, kt + TBK, j + 2, tile_masked(j + 2)); else steady(sB, sA, kt, kt + TBK, j + 2, tile_masked(j + 2)); }
+        if (!idle) steady(sB, sA, kt, kt + TBK, j + 2, tile_masked(j + 2));
       }
       end_iter(j + 1);
     }
@@ -946,25 +654,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
       const uint8_t* kt = smem + stage_buf(j) * SB;  // K_{j+1}
       const uint8_t* vt = kt + TBK;                   // V_j
       if (j < my_T) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) part2(sA[rb], rb);
-        if constexpr (AS) valu_to_mfma_wait_v(pf[0][0], pf[0][1], pf[1][0], pf[1][1]);  // P before its products
+        part2(sA);
         pv(vt);
         if (j + 1 < my_T) {
+          bool resc;
           qk(kt, sB);
-          if constexpr (AS) mfma_result_wait_v(sB[0][0], sB[1][0]);
+          const float alpha = part1(sB, j + 1, tile_masked(j + 1), resc);
+          if (resc) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            bool resc;
-            const float alpha = part1(sB[rb], rb, j + 1, tile_masked(j + 1), resc);
-            if (resc) {
-              if constexpr (AS) mfma_result_wait_a(o[rb]);
-#pragma unroll
-              for (int b = 0; b < DV / 32; ++b) o[rb][b] *= alpha;
-            }
-#pragma unroll
-            for (int b = 0; b < BC / 32; ++b) sA[rb][b] = sB[rb][b];
+            for (int b = 0; b < DV / 32; ++b) o[b] *= alpha;
           }
+#pragma unroll
+          for (int b = 0; b < BC / 32; ++b) sA[b] = sB[b];
         }
       }
       end_iter(j);
@@ -980,64 +681,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB > 1 
     // through its own LDS area (the stage buffers are free after the last
     // barrier) and stores whole 128-byte row segments, 8 lanes per segment.
     // a padding row (my_q >= nq) stores the empty sum: O = 0, lse = -inf
-    if constexpr (AS) {  // O's last products
-      mfma_result_wait_a(o[0]);
-      order_after_a(o[RB - 1]);
-    }
+    const bool pad = my_q >= nq;
+    const float l_tot = pad ? 0.f : half_sum(l_run);
+    if constexpr (SPLIT) {
+      // this share's output and weights, fp32, straight from the registers
+      // (block b, register 4g+e of lane (q, h) is column 32b + 8g + 4h + e)
+      const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+      if (my_q < Nq) {
+        const size_t rows = (size_t)(total_items / (n_qtiles * n_split)) * Nq;
+        const size_t row = (size_t)split * rows + (size_t)bh * Nq + my_q;
+        float* orow = Opart + row * DV + 4 * hf;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const bool pad = my_q[rb] >= nq;
-      const float l_tot = pad ? 0.f : half_sum(l_run[rb]);
-      const int row0 = q_first + 32 * rb;  // the block's first row
-      if constexpr (SPLIT) {
-        // this share's output and weights, fp32, straight from the registers
-        // (block b, register 4g+e of lane (q, h) is column 32b + 8g + 4h + e)
-        const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-        if (my_q[rb] < Nq) {
-          const size_t rows = (size_t)(total_items / (n_qtiles * n_split)) * Nq;
-          const size_t row = (size_t)split * rows + (size_t)bh * Nq + my_q[rb];
-          float* orow = Opart + row * DV + 4 * hf;
+        for (int b = 0; b < DV / 32; ++b)
 #pragma unroll
-          for (int b = 0; b < DV / 32; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              *(f32x4*)(orow + 32 * b + 8 * g) = f32x4{o[rb][b][4 * g] * inv, o[rb][b][4 * g + 1] * inv,
-                                                       o[rb][b][4 * g + 2] * inv, o[rb][b][4 * g + 3] * inv};
-          if (hf == 0) Lpart[row] = l_tot > 0.f ? mc_run[rb] + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-        }
-      } else {
-        // a row without kept keys has l = 0 and O = 0 (rows past Nq: not stored)
-        const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-        uint8_t* stg = smem + wave * kOStageBytes;
-#pragma unroll
-        for (int r = 0; r < DV / 64; ++r) {
-#ifdef FA_SYNC_PHASES
-          __syncthreads();  // check build: a barrier around every staging phase
-#endif
-#pragma unroll
-          for (int bl = 0; bl < 2; ++bl)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x16& ob = o[rb][2 * r + bl];
-              const u32x2 w = {TT::pack(ob[4 * g + 0] * inv, ob[4 * g + 1] * inv),
-                               TT::pack(ob[4 * g + 2] * inv, ob[4 * g + 3] * inv)};
-              *(u32x2*)(stg + lq * kOStageRow + 2 * (32 * bl + 8 * g + 4 * hf)) = w;
-            }
-#ifdef FA_SYNC_PHASES
-          __syncthreads();
-#endif
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 8 * i + (lane >> 3);
-            const u32x4 v = *(const u32x4*)(stg + row * kOStageRow + 16 * (lane & 7));
-            if (row0 + row < Nq)
-              *(u32x4*)(O + ohead + (size_t)(row0 + row) * DV + 64 * r + 8 * (lane & 7)) = v;
-          }
-        }
-        // a row without kept keys: -inf + ln 0 = -inf, the log of the empty sum
-        if (hf == 0 && my_q[rb] < Nq)
-          LSE[(size_t)bh * Nq + my_q[rb]] = (mc_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(orow + 32 * b + 8 * g) = f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv,
+                                                     o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
+        if (hf == 0) Lpart[row] = l_tot > 0.f ? mc_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
       }
+    } else {
+      // a row without kept keys has l = 0 and O = 0 (rows past Nq: not stored)
+      const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+      uint8_t* stg = smem + wave * kOStageBytes;
+#pragma unroll
+      for (int r = 0; r < DV / 64; ++r) {
+#ifdef FA_SYNC_PHASES
+        __syncthreads();  // check build: a barrier around every staging phase
+#endif
+#pragma unroll
+        for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& ob = o[2 * r + bl];
+            const u32x2 w = {TT::pack(ob[4 * g + 0] * inv, ob[4 * g + 1] * inv),
+                             TT::pack(ob[4 * g + 2] * inv, ob[4 * g + 3] * inv)};
+            *(u32x2*)(stg + lq * kOStageRow + 2 * (32 * bl + 8 * g + 4 * hf)) = w;
+          }
+#ifdef FA_SYNC_PHASES
+        __syncthreads();
+#endif
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * i + (lane >> 3);
+          const u32x4 v = *(const u32x4*)(stg + row * kOStageRow + 16 * (lane & 7));
+          if (q_first + row < Nq)
+            *(u32x4*)(O + ohead + (size_t)(q_first + row) * DV + 64 * r + 8 * (lane & 7)) = v;
+        }
+      }
+      // a row without kept keys: -inf + ln 0 = -inf, the log of the empty sum
+      if (hf == 0 && my_q < Nq) LSE[(size_t)bh * Nq + my_q] = (mc_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
     if (tid == 0) s_item = next;
     __syncthreads();
@@ -1538,24 +1230,23 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   // two), one workgroup per item.  Unequal head dims take the d = 128
   // arrangement.
   constexpr bool WIDE = DK == 128 || DV == 128;
-  constexpr int NS = 2;
+  constexpr int NW = WIDE ? 8 : 4, NS = 2;
   constexpr bool PERSIST = WIDE;
   static std::atomic<unsigned> launches{0};
+  const int nq = (sh.Nq + 32 * NW - 1) / (32 * NW);
   if (plan.n_split > 1) {
-    constexpr int NW = WIDE ? 8 : 4, RB = 1;
-    const int nq = (sh.Nq + 32 * RB * NW - 1) / (32 * RB * NW);
     const int total = nq * sh.BH * plan.n_split;
     const long long rows = (long long)sh.BH * sh.Nq;
     float* opart = (float*)ws;
     float* lpart = opart + (size_t)plan.n_split * rows * DV;
     const dim3 grid(total), block(64 * NW);
     if (causal)
-      hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, false, true, RB>), grid, block, 0, st,
+      hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, false, true>), grid, block, 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o,
                          lse, sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, 0, scale, plan.n_split,
                          opart, lpart);
     else
-      hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, false, true, RB>), grid, block, 0, st,
+      hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, false, true>), grid, block, 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o,
                          lse, sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, 0, scale, plan.n_split,
                          opart, lpart);
@@ -1566,8 +1257,6 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
                        plan.n_split);
     return hipGetLastError();
   }
-  constexpr int RB = DK == 128 && DV == 128 ? 2 : 1, NW = WIDE ? 8 / RB : 4;
-  const int nq = (sh.Nq + 32 * RB * NW - 1) / (32 * RB * NW);
   const int total = nq * sh.BH;
   int grid_wg = total, slot = 0;
   if (PERSIST) {
@@ -1578,11 +1267,11 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
   }
   const dim3 grid(grid_wg), block(64 * NW);
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, PERSIST, false, RB>), grid, block, 0, st,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, true, NW, NS, PERSIST, false>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                        sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, slot, scale, 1, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, PERSIST, false, RB>), grid, block, 0, st,
+    hipLaunchKernelGGL((attn_fwd_sp<TT, DK, DV, false, NW, NS, PERSIST, false>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                        sh.Nq, sh.Nk, sh.H, sh.k_len, sh.q_len, nq, total, slot, scale, 1, nullptr, nullptr);
   return hipGetLastError();
