@@ -25,9 +25,10 @@
 //    column.  Each wave software-pipelines the score product of the next
 //    tile against the softmax of the current one.
 //  * attn_fwd_f32: fp32 inputs, head dim 64..1024, on v_mfma_f32_32x32x2_f32.
-//    Head dims above 128 are split across the waves of a workgroup (128
-//    columns each); the partial scores are summed through LDS in a fixed wave
-//    order, so every wave sees bitwise the same scores and the same softmax.
+//    Head dims above 128 are split across the waves of a workgroup (64
+//    columns each, 128 at d = 1024; at d = 128 on the small grids that take
+//    the key split); the partial scores are summed through LDS in a fixed
+//    wave order, so every wave sees bitwise the same scores and softmax.
 //    Q stays in registers; each wave's slice of the next K tile is loaded
 //    straight into LDS while the current tile's products run.
 //  * attn_combine_sp / attn_combine_f32: grids too small to fill the GPU
@@ -1422,11 +1423,22 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, c
     e = dk == 64 ? launch32<64, 128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws)
                  : launch32<128, 64, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws);
   } else {
+    // Columns per wave: 64 wherever the waves then fit two per SIMD (about
+    // 210 registers, against 340-360 with 128 columns), which at d = 256
+    // and 512 is faster on every grid measured (4-31%).  At d = 128 one
+    // wave of 128 columns needs no exchange of partial scores and is faster
+    // on grids that fill the GPU (8-17%); two waves of 64 are 16-26% faster
+    // on the small grids that take the key split.  d = 1024 keeps 128
+    // columns: sixteen waves' K slices and partial scores would not fit in
+    // the LDS.
     switch (dk) {
       case 64: e = launch32<64, 64, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
-      case 128: e = launch32<128, 128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
-      case 256: e = launch32<128, 128, 2>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
-      case 512: e = launch32<128, 128, 4>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 128:
+        e = plan.n_split > 1 ? launch32<64, 64, 2>(q, k, v, o, lse, sh, scale, c, st, plan, ws)
+                             : launch32<128, 128, 1>(q, k, v, o, lse, sh, scale, c, st, plan, ws);
+        break;
+      case 256: e = launch32<64, 64, 4>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
+      case 512: e = launch32<64, 64, 8>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
       default: e = launch32<128, 128, 8>(q, k, v, o, lse, sh, scale, c, st, plan, ws); break;
     }
   }

@@ -8,7 +8,9 @@ products to every score, and zero columns of V give zero columns of O while
 the other columns see the same weights.  So fa_fwd_gen(d_qk=64, d_v=128) must
 equal fa_fwd(d=128) on Q and K padded to 128 columns bit for bit, and
 fa_fwd_gen(128, 64) must equal the first 64 columns of fa_fwd(d=128) on V
-padded to 128 columns.
+padded to 128 columns -- bit for bit in 16-bit types; in fp32 on small grids
+the d = 128 call sums its scores over two waves of 64 columns where the
+(128, 64) call sums them in one, so there the two agree to fp32 rounding.
 """
 import math
 
@@ -95,8 +97,15 @@ def test_equals_equal_dim_kernel_on_zero_padded_inputs(dt, B, H, Nq, Nk, causal)
     o4, l4 = fa.attention(q, k, pad(v64, 128), causal=causal, scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    assert torch.equal(o3, o4[..., :64]) and torch.equal(l3, l4)
     assert torch.all(o4[..., 64:] == 0)
+    if dt == "fp32":
+        # these fp32 grids are small enough to take the key split, which at
+        # d = 128 adds the scores of two 64-column waves where the d_qk = 128,
+        # d_v = 64 kernel sums all 128 columns in one wave: equal to rounding
+        assert (o3 - o4[..., :64]).abs().max().item() <= 2e-6
+        assert (l3 - l4).abs().max().item() <= 2e-6
+    else:
+        assert torch.equal(o3, o4[..., :64]) and torch.equal(l3, l4)
 
 
 def test_unsupported_pairs_are_rejected():

@@ -52,6 +52,8 @@ CASES = [
     ("fp32", 2, 4, 1500, 1500, 128, 128, True, None, None, False),
     ("fp32", 3, 2, 777, 901, 64, 128, False, [901, 13], None, True),
     ("fp32", 2, 2, 300, 300, 128, 64, True, [300, 299], [300, 31], False),
+    ("fp32", 1, 2, 391, 391, 128, 128, True, None, None, True),     # two waves of 64 columns, key split
+    ("fp32", 2, 2, 500, 700, 256, 256, False, [700, 350], None, True),  # four waves of 64 columns
 ]
 
 
