@@ -82,7 +82,8 @@ typedef enum {
  * Arithmetic: scores and all softmax statistics are fp32; bf16/fp16 products
  * accumulate in fp32 on the matrix cores; probabilities are rounded to the
  * input type before the product with V.  Results are bitwise reproducible run
- * to run (fixed reduction order).
+ * to run (fixed reduction order, which depends only on the shape, the dtype
+ * and the device's compute-unit count).
  *
  * Scheduling: at head dim 128 (bf16/fp16) one workgroup per compute unit
  * claims work items through atomic counters kept in the library's code
@@ -273,7 +274,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
  * written.  Arithmetic: products of 16-bit operands accumulate in fp32; P and
  * dS are rounded to the element type before their products.  fp32 operands
  * take fp32 products throughout (no reduced-precision inputs).  No atomics: the
- * result is bitwise reproducible run to run.
+ * result is bitwise reproducible run to run (the order of every sum depends
+ * only on the shape, the dtype and the device's compute-unit count).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
