@@ -61,7 +61,7 @@ def test_fp32_wide_heads():
 
 
 # ------------------------------------------------------------------ key split (fp32, small grids)
-@pytest.mark.parametrize("d", [64, 128, 256, 1024])
+@pytest.mark.parametrize("d", [64, 128, 256, 512, 1024])
 @pytest.mark.parametrize("causal", [False, True])
 def test_key_split_matches_oracle_and_unsplit_path(d, causal):
     """fp32 grids smaller than the GPU split each query block's keys into
