@@ -351,13 +351,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       }
       // P = exp(scale s - lse); dS = P (dP - delta); a tile across the
       // diagonal or the end of the valid keys keeps key <= query + diag and
-      // key < nk only
+      // key < nk only: its other scores become -inf before the exponentials
+      // (P = 0 exactly), in a branch that only such tiles take
       const bool mask = (CAUSAL && q0 + diag < kw + 31) || kw + 31 >= nk;
-      const int lim = my_k >= nk ? 0x7fffffff : CAUSAL ? my_k - diag : -0x7fffffff;
+      if (mask) {
+        const int lim = my_k >= nk ? 0x7fffffff : CAUSAL ? my_k - diag : -0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (q0 + 8 * (r >> 2) + 4 * h + (r & 3) < lim) s[r] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(s[r] * c2);
-        if (mask && q0 + 8 * (r >> 2) + 4 * h + (r & 3) < lim) p = 0.f;
+        const float p = fast_exp2(s[r] * c2);
         s[r] = p;
         dp[r] = p * dp[r];
       }
@@ -512,7 +517,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       // keys past the row (causal) or past the valid keys get no weight: such
       // a key has zero K and V rows, but its weight exp(-lse) need not be finite
       const bool masked = (CAUSAL && k0 + BC - 1 > q_first + diag) || (k0 + BC > nk);
-      const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1);
 #pragma unroll
       for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
         f32x16 st = f32x16{}, dpt = f32x16{};
@@ -532,12 +536,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
 #pragma unroll
           for (int c = 0; c < DV / 16; ++c) dpt = TT::mma(vop(c), of[c], dpt);
         }
+        // masked scores become -inf before the exponentials (P = 0 exactly), in
+        // a branch that only the tiles across the diagonal or the end take
+        if (masked) {
+          const int lim = min(CAUSAL ? my_q + diag : nk - 1, nk - 1) - (k0 + 32 * kb2 + 4 * h);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(st[r], c2, nl2));
-          if (masked && k0 + 32 * kb2 + 8 * (r >> 2) + 4 * h + (r & 3) > lim) p = 0.f;
-          st[r] = p * (dpt[r] + nd);
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) > lim) st[r] = -INFINITY;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], c2, nl2)) * (dpt[r] + nd);
         u32x4 df[2];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
