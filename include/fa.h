@@ -231,8 +231,8 @@ int fa_fwd_gen_supported(int d_qk, int d_v, int dtype, int causal);
  * current device holds at once (fp32: 32-row blocks against its compute
  * units; 16-bit: 128-key blocks and 256-row query blocks, 128 at d = 64,
  * against the eight waves a compute unit holds, twelve at d = 64), also the
- * fp32 partial sums of the split that spreads
- * each block's work over several workgroups.  Depends on the current device.
+ * fp32 partial sums of the split that spreads each block's work over several
+ * workgroups.  Depends on the current device.
  * 0 for invalid or unsupported arguments.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
