@@ -1009,16 +1009,17 @@ struct BwdSplit {
   size_t bytes = 0;  // partial sums
 };
 
-// dk, dv: head dims of Q/K and of V/dO
 // Waves per workgroup of the 16-bit dQ kernel (32 query rows each): eight
 // above d = 64, where one workgroup fills a CU's two waves per SIMD and each
 // K/V tile in LDS serves 256 rows; four at d = 64, whose three waves per SIMD
 // (12 per CU) take three four-wave workgroups.  Measured on d = 128 gradients
 // against four waves: 1.5-4.5% faster, bitwise equal (the dK/dV kernel with
 // eight waves was 1.8% slower on causal shapes: more of its waves idle at the
-// diagonal).
+// diagonal; eight-wave dQ at d = 64, two waves per SIMD instead of three, was
+// 2.5-9.5% slower).
 constexpr int bwd_dq_waves(int dk, int dv) { return dk + dv == 128 ? 4 : 8; }
 
+// dk, dv: head dims of Q/K and of V/dO
 BwdSplit plan_bwd_split(long long BH, int Nq, int Nk, int dk, int dv, int dtype) {
   BwdSplit p;
   int cus = 0;
