@@ -84,6 +84,11 @@ using namespace fa_dev;
 // all computed whether or not any of its workgroups got the slot (an item
 // computed twice is written twice with the same bits).  A workgroup that
 // arrives after its launch has already finished every item exits.
+// At d = 64 the steady step takes its exponentials against the row's
+// reference without the tile's row max; a lane whose weights of the tile sum
+// past this bound (or not to a finite value) sends the tile to the exact path.
+// Below it every weight is at most 2^15: finite in fp32, bf16 and fp16.
+constexpr float kSumLimit = 32768.0f;
 constexpr int kWorkSlots = 64;
 struct WorkSlot {
   unsigned long long state;     // tag << 16 | workgroups using the slot; 0 when free
@@ -210,6 +215,11 @@ __device__ __forceinline__ void leave_launch(int slot, unsigned long long tag) {
 //           of tile j's probabilities P_j (VALU);
 //   step B: O += P_j V_j (MFMA)           with  mask, max and reference update
 //           of tile j+1 (VALU); a rare rescale of O follows the product.
+// At d = 64, whose step is bound by the vector unit, step B takes no row max:
+// tile j's exponentials are taken against the row's current reference, and a
+// lane whose weights of the tile sum past kSumLimit (or not to a finite
+// value) sends tile j to the exact path before its product (scores computed
+// again from K in global memory, max, reference move, rescale).
 // LDS stage j holds (K_{j+1}, V_j) in buffer j % 2 (block layout above),
 // loaded by all waves during iteration j-1; one barrier per iteration.
 // Tiles that need a mask (diagonal, sequence tail) and each wave's last tile
@@ -437,6 +447,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       const int k0 = (tile0 + t) * BC;
       return (CAUSAL && k0 + BC - 1 > q_first + diag) || (k0 + BC > nk);
     };
+    // d = 64: tile t's scores computed again from K in global memory (the
+    // same operands and products as from the LDS copy, so the same bits)
+    // and the exact path run on them: mask, row max, reference move, O and l
+    // rescaled, exponentials again
+    constexpr bool NOMAX = DK + DV == 128;
+    auto redo = [&](f32x16 (&sv)[BC / 32], int t) {
+      const int k0 = (tile0 + t) * BC;
+#pragma unroll
+      for (int b = 0; b < BC / 32; ++b) {
+        sv[b] = f32x16{};
+        const int key = k0 + 32 * b + lq;
+        const uint16_t* krow = kbase + (size_t)key * DK + 8 * hf;
+#pragma unroll
+        for (int c = 0; c < DK / 16; ++c) {
+          const u32x4 a = key < nk ? *(const u32x4*)(krow + 16 * c) : u32x4{0, 0, 0, 0};
+          sv[b] = TT::mma(a, qf[c], sv[b]);
+        }
+      }
+      bool resc;
+      const float alpha = part1(sv, t, tile_masked(t), resc);
+      if (resc) {
+#pragma unroll
+        for (int bb = 0; bb < DV / 32; ++bb) o[bb] *= alpha;
+      }
+      part2(sv);
+    };
 
     // One steady-state step (tile j's softmax and product, tile j+1's scores
     // and statistics), written in issue order and fenced so that every MFMA is
@@ -477,7 +513,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += ls0 + ls1;
+      if constexpr (NOMAX) {
+        const float ts = ls0 + ls1;
+        if (__builtin_amdgcn_ballot_w64(!(ts <= kSumLimit)) != 0) redo(cur, t_next - 1);
+        else l_run += ts;
+      } else {
+        l_run += ls0 + ls1;
+      }
       // ---- step B: O += P_j V_j (MFMA) with tile j+1's row max (VALU)
       auto vaddr = [&](int i) {
         const int cc = i / (DV / 32), bb = i % (DV / 32);
@@ -518,7 +560,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         if (i + VP < NPV) vop[(i + VP) % (VP + 1)] = vload(i + VP);
         const int cc = i / (DV / 32), bb = i % (DV / 32);
         o[bb] = TT::mma(vop[i % (VP + 1)], pf[cc], o[bb]);
-        if (i >= 2) {
+        if (!NOMAX && i >= 2) {
 #pragma unroll
           for (int k = 0; k < MPM; ++k) {
             if (e < ELEM / 2) {  // two scores of tile j+1 per max3
@@ -532,6 +574,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
+      if constexpr (NOMAX) return;
       // tile j+1's statistics; a row whose keys in this tile are all masked
       // keeps its max (the kept keys are a prefix, so tile 0 gave every row
       // with a kept key a finite one; a row without any stays at -inf)
@@ -645,6 +688,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         if (!idle) steady(sB, sA, kt, kt + TBK, j + 2, tile_masked(j + 2));
       }
       end_iter(j + 1);
+    }
+    // At d = 64 the last steady step hands tile j's scores on without their
+    // row max: take it here (mask, max, reference move, rescale) before the
+    // general path takes the exponentials
+    if constexpr (NOMAX) {
+      if (j > 0 && j < T && !idle) {
+        bool resc;
+        const float alpha = part1(sA, j, tile_masked(j), resc);
+        if (resc) {
+#pragma unroll
+          for (int b = 0; b < DV / 32; ++b) o[b] *= alpha;
+        }
+      }
     }
     // remaining tiles: general path (a wave skips tiles past its last row)
     for (; j < T; ++j) {

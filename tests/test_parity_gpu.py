@@ -221,6 +221,39 @@ def test_large_scores_stay_finite():
             parity.check(st, DT[dt], extra_o=2 * e * vmax, extra_lse=e)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H", [(2, 3), (16, 16)])
+def test_scores_that_jump_past_the_reference(dt, d, B, H):
+    """Keys 0..255 score about N(0,1); keys 256..447 are scaled by 10 and keys
+    from 448 on by 60, so the max of every row that sees them jumps far past
+    the exponent reference its first tiles set: by about 2^38 at the first
+    jump and past 2^128 at the second, which overflows any exponential taken
+    against the old reference.  The kernels must move the reference on those
+    tiles (at d = 64, whose steady step takes no per-tile max, by computing
+    the tile again) and agree with the oracle within the large-score bounds.
+    B2 H3 takes the key split (each share sets its own reference); B16 H16
+    does not."""
+    N = 640
+    q, k, v = make_qkv(B, H, N, d, "fp32", 97 + d)
+    gain = torch.ones(N)
+    gain[256:448] = 10.0
+    gain[448:] = 60.0
+    k = k * gain.view(1, 1, N, 1)
+    scale = 1 / math.sqrt(d)
+    qq, kk, vv = (x.to(DT[dt]) for x in (q, k, v))
+    e = parity.score_rounding_bound(qq, kk, scale)
+    vmax = vv.double().abs().max().item()
+    rows = None if B * H <= 8 else parity.sample_rows(B, H, N, seed=7, per_head_random=16,
+                                                      heads=[(0, 0), (B - 1, H - 1)])
+    for causal in (False, True):
+        o, lse = run(qq, kk, vv, causal)
+        st = parity.compare(o, lse, qq, kk, vv, scale, causal, rows)
+        print(f"{dt} d={d} B{B} H{H} causal={causal}: max|dO| {st['max_o']:.3e} "
+              f"mean|dO| {st['mean_o']:.3e} max|dlse| {st['max_lse']:.3e} (rows {st['rows']})")
+        parity.check(st, DT[dt], extra_o=2 * e * vmax, extra_lse=e)
+
+
 # ------------------------------------------------------------------ behaviour of the entry point
 def test_bitwise_reproducible():
     q, k, v = make_qkv(2, 4, 1000, 128, "bf16", 80)
