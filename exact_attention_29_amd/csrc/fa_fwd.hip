@@ -366,6 +366,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     // running state: row max m, its scaled reference mc (exponents are taken
     // against mc) and the fp32 sum l of the weights
     float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
+    // the exponentials' offset: mc, or 0 while a row has no reference yet
+    // (its scores are then all -inf), kept beside mc as it changes
+    float off_run = 0.f;
     const float c2 = scale * kLog2e;
     u32x4 pf[BC / 16];  // P_j packed, B operand of the P V product
 
@@ -419,12 +422,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       // 0 for a row's first finite tile; a still fully masked row keeps alpha 1
       const float alpha = (!resc || mc_cand == -INFINITY) ? 1.f : fast_exp2(mc_run - mc_cand);
       mc_run = resc ? mc_cand : mc_run;
+      off_run = (mc_run == -INFINITY) ? 0.f : mc_run;
       l_run *= alpha;
       return alpha;
     };
     // Exponentials against the current reference, their sum, and P packed.
     auto part2 = [&](f32x16 (&sv)[BC / 32]) {
-      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
+      const float off = off_run;
       float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < BC / 32; ++b)
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
                       const uint8_t* vt, int t_next, bool mask_next) {
       constexpr int NQK = BC / 32 * DK / 16, NPV = BC / 16 * DV / 32;
       constexpr int ELEM = BC / 2;  // scores of a tile held by one lane
-      const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
+      const float off = off_run;
       float ls0 = 0.f, ls1 = 0.f;
       // ---- step A: S_{j+1} (MFMA) with exp / sums / packing of tile j (VALU)
       auto kaddr = [&](int i) {
@@ -585,6 +589,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       if (resc) {
         const float alpha = mc_cand == -INFINITY ? 1.f : fast_exp2(mc_run - mc_cand);
         mc_run = mc_cand;
+        off_run = (mc_run == -INFINITY) ? 0.f : mc_run;
         l_run *= alpha;
 #pragma unroll
         for (int bb = 0; bb < DV / 32; ++bb) o[bb] *= alpha;
