@@ -481,6 +481,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
   // never stored (the block's last rows may lie past the row padding)
   const float nl2 = my_q < nq ? NL[(size_t)bh * n_pad + my_q] * c2 : -INFINITY;
   const float nd = my_q < nq ? ND[(size_t)bh * n_pad + my_q] : 0.f;
+  // -delta of the lane's row in every register: the initial accumulator of
+  // each dP^T block, so dP - delta comes out of the matrix core
+  f32x16 ndb;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndb[r] = nd;
   f32x16 dq[DK / 32];
 #pragma unroll
   for (int b = 0; b < DK / 32; ++b) dq[b] = f32x16{};
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
       const bool masked = (CAUSAL && k0 + BC - 1 > q_first + diag) || (k0 + BC > nk);
 #pragma unroll
       for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
-        f32x16 st = f32x16{}, dpt = f32x16{};
+        f32x16 st = f32x16{}, dpt = ndb;
         auto vop = [&](int c) {
           return *(const u32x4*)(vt + v_lane + (2 * kb2 * CGV + (c >> 1)) * 1024 + (c & 1) * 512);
         };
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
             if (8 * (r >> 2) + (r & 3) > lim) st[r] = -INFINITY;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], c2, nl2)) * (dpt[r] + nd);
+        for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], c2, nl2)) * dpt[r];
         u32x4 df[2];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
