@@ -84,11 +84,6 @@ using namespace fa_dev;
 // all computed whether or not any of its workgroups got the slot (an item
 // computed twice is written twice with the same bits).  A workgroup that
 // arrives after its launch has already finished every item exits.
-// At d = 64 the steady step takes its exponentials against the row's
-// reference without the tile's row max; a lane whose weights of the tile sum
-// past this bound (or not to a finite value) sends the tile to the exact path.
-// Below it every weight is at most 2^15: finite in fp32, bf16 and fp16.
-constexpr float kSumLimit = 32768.0f;
 constexpr int kWorkSlots = 64;
 struct WorkSlot {
   unsigned long long state;     // tag << 16 | workgroups using the slot; 0 when free
@@ -203,6 +198,12 @@ __device__ __forceinline__ void leave_launch(int slot, unsigned long long tag) {
   __hip_atomic_compare_exchange_strong(&w.state, &mine, 0ull, __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE,
                                        __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// At d = 64 the steady step takes its exponentials against the row's
+// reference without the tile's row max; a lane whose weights of the tile sum
+// past this bound (or not to a finite value) sends the tile to the exact path.
+// Below it every weight is at most 2^15: finite in fp32, bf16 and fp16.
+constexpr float kSumLimit = 32768.0f;
 
 // ---------------------------------------------------------------------------
 // bf16 / fp16 kernel, software-pipelined
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
     };
 
     // One steady-state step (tile j's softmax and product, tile j+1's scores
-    // and statistics), written in issue order and fenced so that every MFMA is
+    // and, above d = 64, statistics), written in issue order and fenced so that every MFMA is
     // followed by the independent vector work that hides it.
     auto steady = [&](f32x16 (&cur)[BC / 32], f32x16 (&nxt)[BC / 32], const uint8_t* kt,
                       const uint8_t* vt, int t_next, bool mask_next) {
