@@ -895,8 +895,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc((void*)u, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
 }
 
+// With 64 V columns a wave fits two waves per SIMD; the hint keeps the
+// compiler there (without it the 128/64 split takes 267 registers).
 template <int DSL, int DSLV, int DS, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
+__global__ __launch_bounds__(DS * 64) __attribute__((amdgpu_waves_per_eu(DSLV == 64 ? 2 : 1))) void attn_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int H,
     const int* __restrict__ k_len, const int* __restrict__ q_len, int n_qtiles, int total_wg,
@@ -1089,10 +1091,20 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
     mt = half_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float mc_new = (m_new == -INFINITY) ? -INFINITY : m_new * c2;
-    const float off = (m_new == -INFINITY) ? 0.f : mc_new;
-    const float alpha = fast_exp2(mc_run - off);
+    m_run = fmaxf(m_run, mt);
+    // the reference moves (and O and l are rescaled) only when some row's max
+    // has grown past it by more than kLazyRescale powers of two, as in the
+    // 16-bit kernel; a row's first finite tile always moves it
+    const float mc_cand = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
+    if (__builtin_amdgcn_ballot_w64(mc_cand > mc_run + kLazyRescale) != 0) {
+      // 0 for a row's first finite tile; a still fully masked row keeps alpha 1
+      const float alpha = mc_cand == -INFINITY ? 1.f : fast_exp2(mc_run - mc_cand);
+      mc_run = mc_cand;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b] *= alpha;
+    }
+    const float off = (mc_run == -INFINITY) ? 0.f : mc_run;
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1100,11 +1112,7 @@ __global__ __launch_bounds__(DS * 64) void attn_fwd_f32(
       s[r] = p;
       lsum += p;
     }
-    l_run = fmaf(l_run, alpha, lsum);
-    m_run = m_new;
-    mc_run = mc_new;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) o[b] *= alpha;
+    l_run += lsum;
     // O^T += V^T P^T; the next tile's V rows of step r go into that step's
     // registers four steps later, so the loads spread over the products and
     // never wait for a product that still has to read the registers
