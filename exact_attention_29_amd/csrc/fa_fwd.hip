@@ -821,9 +821,11 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
   // row blocks on XCDs as the split kernel's blocks were (see attn_combine_f32)
   const long long row = (long long)xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
-  // shares read kCombineBatch at a time, as in attn_combine_f32
+  // shares read kCombineBatch at a time, as in attn_combine_f32 (one batch:
+  // the max from its own loads)
+  const bool one = n_split <= kCombineBatch;
   float bmax = -INFINITY;
-  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+  for (int s0 = 0; !one && s0 < n_split; s0 += kCombineBatch) {
     float l[kCombineBatch];
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i)
@@ -832,11 +834,6 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
     for (int i = 0; i < kCombineBatch; ++i) bmax = fmaxf(bmax, l[i]);
   }
   uint16_t* orow = O + (size_t)row * DV + 8 * t;
-  if (bmax == -INFINITY) {  // no share kept a key of this row: the empty sum
-    *(u32x4*)orow = u32x4{0, 0, 0, 0};
-    if (t == 0) LSE[row] = -INFINITY;
-    return;
-  }
   float wsum = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
@@ -849,6 +846,15 @@ __global__ __launch_bounds__(256) void attn_combine_sp(const float* __restrict__
       l[i] = in ? Lpart[(size_t)(s0 + i) * rows + row] : -INFINITY;
       op0[i] = in ? op[0] : f32x4{0.f, 0.f, 0.f, 0.f};
       op1[i] = in ? op[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (one) {
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) bmax = fmaxf(bmax, l[i]);
+    }
+    if (bmax == -INFINITY) {  // no share kept a key of this row: the empty sum
+      *(u32x4*)orow = u32x4{0, 0, 0, 0};
+      if (t == 0) LSE[row] = -INFINITY;
+      return;
     }
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) {
@@ -1197,20 +1203,18 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
   const long long row = (long long)xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;
   if (threadIdx.x / TPR >= RPB || row >= rows) return;
   // The splits are read kCombineBatch at a time, all loads of a batch issued
-  // before any is used; the sums still run over the splits in order.
+  // before any is used; the sums still run over the splits in order.  Up to
+  // kCombineBatch splits take one batch, and the max comes from its loads
+  // (one round trip to memory); more take a first pass for the max.
+  const bool one = n_split <= kCombineBatch;
   float m = -INFINITY;
-  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+  for (int s0 = 0; !one && s0 < n_split; s0 += kCombineBatch) {
     float l[kCombineBatch];
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i)
       l[i] = s0 + i < n_split ? LSEpart[(size_t)(s0 + i) * rows + row] : -INFINITY;
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) m = fmaxf(m, l[i]);
-  }
-  if (m == -INFINITY) {  // no split kept a key of this row: the empty sum
-    *(f32x4*)(O + (size_t)row * D + 4 * t) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t == 0) LSE[row] = -INFINITY;
-    return;
   }
   float sum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1222,6 +1226,15 @@ __global__ __launch_bounds__(256) void attn_combine_f32(const float* __restrict_
       const bool in = s0 + i < n_split;
       l[i] = in ? LSEpart[(size_t)(s0 + i) * rows + row] : -INFINITY;
       op[i] = in ? *(const f32x4*)(Opart + ((size_t)(s0 + i) * rows + row) * D + 4 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (one) {
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) m = fmaxf(m, l[i]);
+    }
+    if (m == -INFINITY) {  // no split kept a key of this row: the empty sum
+      *(f32x4*)(O + (size_t)row * D + 4 * t) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t == 0) LSE[row] = -INFINITY;
+      return;
     }
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) {
