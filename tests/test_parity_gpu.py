@@ -221,7 +221,7 @@ def test_large_scores_stay_finite():
             parity.check(st, DT[dt], extra_o=2 * e * vmax, extra_lse=e)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H", [(2, 3), (16, 16)])
 def test_scores_that_jump_past_the_reference(dt, d, B, H):
@@ -230,10 +230,20 @@ def test_scores_that_jump_past_the_reference(dt, d, B, H):
     the exponent reference its first tiles set: by about 2^38 at the first
     jump and past 2^128 at the second, which overflows any exponential taken
     against the old reference.  The kernels must move the reference on those
-    tiles (at d = 64, whose steady step takes no per-tile max, by computing
-    the tile again) and agree with the oracle within the large-score bounds.
-    B2 H3 takes the key split (each share sets its own reference); B16 H16
-    does not."""
+    tiles (at d = 64, whose 16-bit steady step takes no per-tile max, by
+    computing the tile again) and agree with the oracle within the
+    large-score bounds.  B2 H3 takes the key split (each share sets its own
+    reference); B16 H16 does not."""
+    jump_case(dt, d, B, H)
+
+
+@pytest.mark.parametrize("d", [256, 1024])
+def test_scores_that_jump_past_the_reference_fp32_wide(d):
+    """The same jumps through the fp32 kernel's head-dim split across waves."""
+    jump_case("fp32", d, 2, 3)
+
+
+def jump_case(dt, d, B, H):
     N = 640
     q, k, v = make_qkv(B, H, N, d, "fp32", 97 + d)
     gain = torch.ones(N)
