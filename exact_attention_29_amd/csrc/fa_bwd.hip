@@ -375,6 +375,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         df[kc] = u32x4{TT::pack(dp[r0 + 0], dp[r0 + 1]), TT::pack(dp[r0 + 2], dp[r0 + 3]),
                        TT::pack(dp[r0 + 4], dp[r0 + 5]), TT::pack(dp[r0 + 6], dp[r0 + 7])};
       }
+      // d = 64 (three waves per SIMD): the wave issuing its dV/dK products
+      // is served before the others' vector work (measured 0.5-6% faster on
+      // d = 64 shapes; 1% slower at d = 128, which keeps the default)
+      if constexpr (DK + DV == 128) __builtin_amdgcn_s_setprio(1);
       // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries
       if constexpr (DK == DV) {
 #pragma unroll
@@ -397,6 +401,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
         }
       }
     }
+    if constexpr (DK + DV == 128) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
@@ -558,6 +563,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
           df[kc] = u32x4{TT::pack(st[r0 + 0], st[r0 + 1]), TT::pack(st[r0 + 2], st[r0 + 3]),
                          TT::pack(st[r0 + 4], st[r0 + 5]), TT::pack(st[r0 + 6], st[r0 + 7])};
         }
+        if constexpr (DK + DV == 128) __builtin_amdgcn_s_setprio(1);  // as in the dK/dV kernel
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -565,6 +571,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DK + DV
             dq[b] = TT::mma(tr_read(kt + ((2 * kb2 + kc) * CGK + b) * 1024, trl), df[kc], dq[b]);
       }
     }
+    if constexpr (DK + DV == 128) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
